@@ -1,0 +1,24 @@
+"""MapFlow cross-model attention-map reuse on MI355X: block-sparse compression of a sender
+layer's causal softmax attention and the fused retrieval into a receiver layer.
+
+The compute lives in ``lib/libmapflow.so`` (HIP kernels for gfx950, C ABI in
+``include/mapflow.h``); ``mapflow`` is its Python binding.
+"""
+from .mapflow import (  # noqa: F401
+    BlockStore,
+    Context,
+    PreparedV,
+    check_layer_map,
+    compress,
+    compress_into,
+    copy_probe,
+    dense_attention,
+    map_layers,
+    probs_canonical_to_store,
+    probs_store_to_canonical,
+    retrieve,
+    retrieve_prepared,
+    v_prepare,
+    version,
+)
+from ._lib import MapflowError  # noqa: F401

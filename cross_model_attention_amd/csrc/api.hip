@@ -1,0 +1,792 @@
+// C ABI of libmapflow: argument validation, geometry of packed batches, context scratch memory,
+// block-store allocation, and dispatch to the kernels.  See include/mapflow.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mapflow.h"
+#include "kernels.h"
+
+#define MF_EXPORT __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_err;
+
+mf_status fail(mf_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+mf_status hip_fail(hipError_t e, const char* what) {
+  return fail(MF_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MF_HIP(call, what)                      \
+  do {                                          \
+    hipError_t _e = (call);                     \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// ---- geometry of a packed batch cut into B-token block rows ------------------------------------
+struct Geometry {
+  int B = 0, n_seq = 0, n_brow = 0, nb_max = 0;
+  int64_t T = 0, n_causal = 0;
+  std::vector<int32_t> info;      // [n_brow][4]
+  std::vector<int32_t> order;     // block rows by descending in-sequence index
+  std::vector<int32_t> brow_seq;  // [n_brow]
+  std::vector<int32_t> cu;        // copy of cu_seqlens
+};
+
+mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& g) {
+  if (cu == nullptr) return fail(MF_ERR_INVALID, "cu_seqlens_host is NULL");
+  if (n_seq < 1) return fail(MF_ERR_INVALID, "n_seq must be >= 1 (got %d)", n_seq);
+  if (B != 16 && B != 32 && B != 64 && B != 128)
+    return fail(MF_ERR_INVALID, "block size B must be 16, 32, 64 or 128 (got %d)", B);
+  if (cu[0] != 0) return fail(MF_ERR_INVALID, "cu_seqlens[0] must be 0 (got %d)", cu[0]);
+  g = Geometry();
+  g.B = B;
+  g.n_seq = n_seq;
+  g.cu.assign(cu, cu + n_seq + 1);
+  for (int s = 0; s < n_seq; ++s) {
+    if (cu[s + 1] < cu[s])
+      return fail(MF_ERR_INVALID, "cu_seqlens must be non-decreasing (entry %d)", s + 1);
+    const int n = cu[s + 1] - cu[s];
+    const int nb = (n + B - 1) / B;
+    g.nb_max = std::max(g.nb_max, nb);
+    g.n_causal += (int64_t)nb * (nb + 1) / 2;
+    for (int I = 0; I < nb; ++I) {
+      g.info.insert(g.info.end(), {cu[s] + I * B, cu[s], n, I});
+      g.brow_seq.push_back(s);
+    }
+  }
+  g.T = cu[n_seq];
+  g.n_brow = (int)g.brow_seq.size();
+  g.order.resize(g.n_brow);
+  for (int b = 0; b < g.n_brow; ++b) g.order[b] = b;
+  std::stable_sort(g.order.begin(), g.order.end(), [&](int x, int y) {
+    return g.info[4 * x + 3] > g.info[4 * y + 3];
+  });
+  if (g.n_causal >= (int64_t)INT32_MAX)
+    return fail(MF_ERR_UNSUPPORTED, "more than 2^31 causal blocks (%lld)", (long long)g.n_causal);
+  return MF_OK;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// One device buffer that only grows.
+struct Scratch {
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+mf_status ensure(Scratch& s, size_t bytes, const char* what) {
+  if (bytes <= s.bytes) return MF_OK;
+  if (s.p) {
+    MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize before scratch growth");
+    MF_HIP(hipFree(s.p), "hipFree(scratch)");
+    s.p = nullptr;
+    s.bytes = 0;
+  }
+  const size_t want = align_up(bytes, 1 << 20);
+  if (hipMalloc(&s.p, want) != hipSuccess) {
+    (void)hipGetLastError();
+    s.p = nullptr;
+    return fail(MF_ERR_OOM, "out of device memory growing %s scratch to %zu bytes", what, want);
+  }
+  s.bytes = want;
+  return MF_OK;
+}
+
+// Bookkeeping behind mf_bsr::_owner.
+struct BsrOwner {
+  void* meta = nullptr;
+  void* data = nullptr;
+  Geometry geom;
+};
+
+// Bookkeeping behind mf_vfrag::_owner.
+struct VfragOwner {
+  void* tables = nullptr;   // info, brow_seq, exps, vmax scratch
+  void* frag = nullptr;     // only when the library allocated it
+  int32_t* info = nullptr;
+  int32_t* brow_seq = nullptr;
+  uint32_t* vmax = nullptr;
+  Geometry geom;
+};
+
+}  // namespace
+
+struct mf_ctx {
+  int device = 0;
+  Scratch lse2, Mh, M, flags, counts, part;
+  mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
+  mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
+  // cached device copies of the dense-attention geometry
+  Scratch dense_tables;
+  std::vector<int32_t> dense_cu;
+  int dense_nbrow = 0;
+};
+
+namespace {
+
+mf_status set_device(mf_ctx* ctx) {
+  if (!ctx) return fail(MF_ERR_INVALID, "context is NULL");
+  MF_HIP(hipSetDevice(ctx->device), "hipSetDevice");
+  return MF_OK;
+}
+
+int dtype_code(mf_dtype dt) { return dt == MF_BF16 ? mf::DT_BF16 : mf::DT_F32; }
+
+mf_status check_dtype(mf_dtype dt) {
+  if (dt != MF_F32 && dt != MF_BF16) return fail(MF_ERR_INVALID, "dtype must be MF_F32 or MF_BF16");
+  return MF_OK;
+}
+
+mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own) {
+  const size_t n_info = (size_t)g.n_brow * 4 * 4;
+  const size_t o_info = 0;
+  const size_t o_order = align_up(o_info + n_info, 256);
+  const size_t o_ptr = align_up(o_order + (size_t)g.n_brow * 4, 256);
+  const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
+  const size_t o_cnt = align_up(o_rkm + (size_t)H_s * g.T * 4, 256);
+  const size_t total = o_cnt + 256;
+  if (hipMalloc(&own->meta, total) != hipSuccess) {
+    (void)hipGetLastError();
+    own->meta = nullptr;
+    return fail(MF_ERR_OOM, "out of device memory for block-store metadata (%zu bytes)", total);
+  }
+  char* base = static_cast<char*>(own->meta);
+  out->brow_info = reinterpret_cast<int32_t*>(base + o_info);
+  out->brow_order = reinterpret_cast<int32_t*>(base + o_order);
+  out->block_ptr = reinterpret_cast<int32_t*>(base + o_ptr);
+  out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
+  out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
+  hipError_t e = hipSuccess;
+  if (g.n_brow > 0) {
+    e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+  }
+  if (e == hipSuccess) e = hipMemset(out->block_ptr, 0, (size_t)(g.n_brow + 1) * 4);
+  if (e == hipSuccess) e = hipMemset(out->counters, 0, 256);
+  if (e == hipSuccess && g.T > 0) e = hipMemset(out->row_kept_mass, 0, (size_t)H_s * g.T * 4);
+  if (e != hipSuccess) {
+    (void)hipFree(own->meta);
+    own->meta = nullptr;
+    return hip_fail(e, "initialising block-store metadata");
+  }
+  return MF_OK;
+}
+
+size_t probs_block_bytes(int H_s, int B) { return (size_t)((H_s + 7) / 8) * B * B * 8 * 2; }
+
+mf_status alloc_bsr_data(int64_t capacity, int H_s, int B, mf_bsr* out, BsrOwner* own) {
+  const size_t o_idx = 0;
+  const size_t o_row = align_up((size_t)capacity * 4, 256);
+  const size_t o_probs = align_up(o_row + (size_t)capacity * 4, 256);
+  const size_t total = o_probs + (size_t)capacity * probs_block_bytes(H_s, B) + 256;
+  if (hipMalloc(&own->data, total) != hipSuccess) {
+    (void)hipGetLastError();
+    own->data = nullptr;
+    return fail(MF_ERR_OOM, "out of device memory for %lld kept blocks (%zu bytes)",
+                (long long)capacity, total);
+  }
+  char* base = static_cast<char*>(own->data);
+  out->block_idx = reinterpret_cast<int32_t*>(base + o_idx);
+  out->block_row = reinterpret_cast<int32_t*>(base + o_row);
+  out->probs = reinterpret_cast<uint16_t*>(base + o_probs);
+  out->capacity = capacity;
+  return MF_OK;
+}
+
+mf_status validate_compress(const void* Q, const void* K, mf_dtype dtype, int32_t d, float tau,
+                            const mf_bsr* bsr) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL or not created by mf_bsr_create");
+  if (!Q || !K) return fail(MF_ERR_INVALID, "Q or K is NULL");
+  mf_status st = check_dtype(dtype);
+  if (st != MF_OK) return st;
+  if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+  if (!(tau > 0.f && tau <= 1.f)) return fail(MF_ERR_INVALID, "tau must be in (0, 1] (got %g)", (double)tau);
+  if (!mf::compress_supported(dtype_code(dtype), bsr->B, d))
+    return fail(MF_ERR_UNSUPPORTED, "no compress kernel for B=%d d=%d", bsr->B, d);
+  if (mf::stats_lds_bytes(bsr->B, bsr->nb_max) > 64 * 1024)
+    return fail(MF_ERR_UNSUPPORTED, "sequence too long for the statistics kernel (%d blocks)", bsr->nb_max);
+  return MF_OK;
+}
+
+mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
+                                int32_t d, float tau, mf_bsr* bsr, int64_t capacity,
+                                mf::CompressArgs& a) {
+  const size_t nbn = (size_t)bsr->n_brow * bsr->nb_max;
+  mf_status st;
+  if ((st = ensure(ctx->lse2, (size_t)bsr->H_s * bsr->T * 4 + 256, "lse")) != MF_OK) return st;
+  if ((st = ensure(ctx->Mh, (size_t)bsr->H_s * nbn * 4 + 256, "block mass")) != MF_OK) return st;
+  if ((st = ensure(ctx->M, nbn * 8 + 256, "head-summed mass")) != MF_OK) return st;
+  if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
+  if ((st = ensure(ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts")) != MF_OK) return st;
+  if ((st = ensure(ctx->part, (size_t)capacity * bsr->H_s * bsr->B * 4 + 256, "row sums")) != MF_OK) return st;
+  a = mf::CompressArgs{};
+  a.Q = Q;
+  a.K = K;
+  a.dtype = dtype_code(dtype);
+  a.H_s = bsr->H_s;
+  a.d = d;
+  a.B = bsr->B;
+  a.T = bsr->T;
+  a.n_brow = bsr->n_brow;
+  a.nb_max = bsr->nb_max;
+  a.info = bsr->brow_info;
+  a.order = bsr->brow_order;
+  a.tau = (double)tau;
+  a.scale2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+  a.lse2 = static_cast<float*>(ctx->lse2.p);
+  a.Mh = static_cast<float*>(ctx->Mh.p);
+  a.M = static_cast<double*>(ctx->M.p);
+  a.flags = static_cast<uint8_t*>(ctx->flags.p);
+  a.counts = static_cast<int32_t*>(ctx->counts.p);
+  a.part = static_cast<float*>(ctx->part.p);
+  a.block_ptr = bsr->block_ptr;
+  a.block_idx = bsr->block_idx;
+  a.block_row = bsr->block_row;
+  a.probs = bsr->probs;
+  a.rkm = bsr->row_kept_mass;
+  a.counters = bsr->counters;
+  a.capacity = capacity;
+  return MF_OK;
+}
+
+mf_status build_headmap(const int32_t* kvmap, int H, int H_kv, mf::HeadMap& hm) {
+  if (!kvmap) return fail(MF_ERR_INVALID, "kv_head_map_host is NULL");
+  if (H < 1 || H > 64) return fail(MF_ERR_UNSUPPORTED, "head count %d outside [1, 64]", H);
+  std::memset(&hm, 0, sizeof(hm));
+  std::vector<int> perm(H);
+  for (int g = 0; g < H; ++g) {
+    if (kvmap[g] < 0 || kvmap[g] >= H_kv)
+      return fail(MF_ERR_INVALID, "kv_head_map[%d] = %d outside [0, %d)", g, kvmap[g], H_kv);
+    hm.kv[g] = (int8_t)kvmap[g];
+    perm[g] = g;
+  }
+  std::stable_sort(perm.begin(), perm.end(), [&](int x, int y) { return kvmap[x] < kvmap[y]; });
+  for (int g = 0; g < H; ++g) hm.perm[g] = (int8_t)perm[g];
+  return MF_OK;
+}
+
+mf_status vfrag_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B, const void* V,
+                        mf_dtype dtype, int32_t H_kv, int32_t d, const int32_t* page_table,
+                        int32_t page_size, int32_t pages_per_seq, mf_vfrag* out, bool reuse,
+                        hipStream_t stream) {
+  if (!out) return fail(MF_ERR_INVALID, "output vfrag is NULL");
+  if (!V) return fail(MF_ERR_INVALID, "V is NULL");
+  mf_status st = check_dtype(dtype);
+  if (st != MF_OK) return st;
+  if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+  if (H_kv < 1 || H_kv > 64) return fail(MF_ERR_INVALID, "H_kv must be in [1, 64] (got %d)", H_kv);
+  if (B != 32 && B != 64) return fail(MF_ERR_UNSUPPORTED, "V preparation supports B = 32 or 64 (got %d)", B);
+  if (page_table && (page_size < 1 || pages_per_seq < 1))
+    return fail(MF_ERR_INVALID, "paged V needs page_size >= 1 and pages_per_seq >= 1");
+  Geometry g;
+  if ((st = build_geometry(cu, n_seq, B, g)) != MF_OK) return st;
+  if (page_table)
+    for (int s = 0; s < n_seq; ++s)
+      if ((int64_t)(cu[s + 1] - cu[s]) > (int64_t)page_size * pages_per_seq)
+        return fail(MF_ERR_INVALID, "sequence %d needs more than pages_per_seq pages", s);
+
+  VfragOwner* own = static_cast<VfragOwner*>(out->_owner);
+  const bool same_geom = own && own->geom.cu == g.cu && own->geom.B == B && out->H_kv == H_kv && out->d == d;
+  if (!(reuse && same_geom)) {
+    if (own) {
+      if (reuse) {
+        MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize before V scratch growth");
+      }
+      if (own->tables) (void)hipFree(own->tables);
+      if (own->frag) (void)hipFree(own->frag);
+      delete own;
+      out->_owner = nullptr;
+      if (reuse) out->frag = nullptr;
+    }
+    own = new (std::nothrow) VfragOwner();
+    if (!own) return fail(MF_ERR_OOM, "host allocation failed");
+    const size_t o_info = 0;
+    const size_t o_seq = align_up((size_t)g.n_brow * 16, 256);
+    const size_t o_exp = align_up(o_seq + (size_t)g.n_brow * 4, 256);
+    const size_t o_max = align_up(o_exp + (size_t)H_kv * 4, 256);
+    const size_t tb = o_max + 256;
+    if (hipMalloc(&own->tables, tb) != hipSuccess) {
+      (void)hipGetLastError();
+      delete own;
+      return fail(MF_ERR_OOM, "out of device memory for V tables");
+    }
+    char* base = static_cast<char*>(own->tables);
+    own->info = reinterpret_cast<int32_t*>(base + o_info);
+    own->brow_seq = reinterpret_cast<int32_t*>(base + o_seq);
+    out->exps = reinterpret_cast<int32_t*>(base + o_exp);
+    own->vmax = reinterpret_cast<uint32_t*>(base + o_max);
+    hipError_t e = hipSuccess;
+    if (g.n_brow > 0) {
+      e = hipMemcpy(own->info, g.info.data(), (size_t)g.n_brow * 16, hipMemcpyHostToDevice);
+      if (e == hipSuccess)
+        e = hipMemcpy(own->brow_seq, g.brow_seq.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    }
+    if (e != hipSuccess) {
+      (void)hipFree(own->tables);
+      delete own;
+      return hip_fail(e, "uploading V tables");
+    }
+    if (out->frag == nullptr) {
+      const size_t fb = (size_t)H_kv * g.n_brow * B * d * 2 + 256;
+      if (hipMalloc(&own->frag, fb) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipFree(own->tables);
+        delete own;
+        return fail(MF_ERR_OOM, "out of device memory for prepared V (%zu bytes)", fb);
+      }
+      out->frag = static_cast<uint16_t*>(own->frag);
+    }
+    own->geom = g;
+    out->_owner = own;
+  }
+  out->B = B;
+  out->d = d;
+  out->H_kv = H_kv;
+  out->n_brow = g.n_brow;
+  out->T = g.T;
+  if (g.n_brow == 0) return MF_OK;
+  mf::VprepArgs va{};
+  va.V = V;
+  va.dtype = dtype_code(dtype);
+  va.H_kv = H_kv;
+  va.d = d;
+  va.B = B;
+  va.T = g.T;
+  va.n_brow = g.n_brow;
+  va.info = own->info;
+  va.page_table = page_table;
+  va.page_size = page_size;
+  va.pages_per_seq = pages_per_seq;
+  va.brow_seq = own->brow_seq;
+  va.vmax_bits = own->vmax;
+  va.frag = out->frag;
+  va.exps = out->exps;
+  MF_HIP(mf::v_prepare(va, stream), "V preparation launch");
+  return MF_OK;
+}
+
+void vfrag_release(mf_vfrag* vf) {
+  if (!vf) return;
+  VfragOwner* own = static_cast<VfragOwner*>(vf->_owner);
+  if (own) {
+    if (own->tables) (void)hipFree(own->tables);
+    if (own->frag) (void)hipFree(own->frag);
+    delete own;
+  }
+  std::memset(vf, 0, sizeof(*vf));
+}
+
+}  // namespace
+
+extern "C" {
+
+MF_EXPORT const char* mf_version(void) { return "libmapflow 0.1.0 (gfx950)"; }
+
+MF_EXPORT const char* mf_last_error(void) { return g_err.c_str(); }
+
+MF_EXPORT mf_status mf_create(int device, mf_ctx** out) {
+  if (!out) return fail(MF_ERR_INVALID, "out is NULL");
+  *out = nullptr;
+  int n = 0;
+  MF_HIP(hipGetDeviceCount(&n), "hipGetDeviceCount");
+  if (device < 0 || device >= n) return fail(MF_ERR_INVALID, "device %d out of range [0, %d)", device, n);
+  MF_HIP(hipSetDevice(device), "hipSetDevice");
+  mf_ctx* ctx = new (std::nothrow) mf_ctx();
+  if (!ctx) return fail(MF_ERR_OOM, "host allocation failed");
+  ctx->device = device;
+  *out = ctx;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
+  if (!ctx) return MF_OK;
+  (void)hipSetDevice(ctx->device);
+  (void)hipDeviceSynchronize();
+  for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->dense_tables})
+    if (s->p) (void)hipFree(s->p);
+  vfrag_release(&ctx->vf_retrieve);
+  vfrag_release(&ctx->vf_dense);
+  delete ctx;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_map_layers(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out) {
+  if (!pi_out) return fail(MF_ERR_INVALID, "pi_out_host is NULL");
+  if (n_recv < 1 || n_send < 1) return fail(MF_ERR_INVALID, "layer counts must be >= 1");
+  if (R < 0 || R > n_recv) return fail(MF_ERR_INVALID, "R must be in [0, n_recv]");
+  for (int l = 0; l < n_recv; ++l) {
+    if (l < R) {
+      pi_out[l] = -1;
+    } else if (n_recv == 1) {
+      pi_out[l] = 0;
+    } else {
+      // round(l (S-1) / (Rv-1)), halves up: floor((2 l (S-1) + (Rv-1)) / (2 (Rv-1)))
+      const int64_t num = 2LL * l * (n_send - 1) + (n_recv - 1);
+      pi_out[l] = (int32_t)(num / (2LL * (n_recv - 1)));
+    }
+  }
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_check_layer_map(const int32_t* pi, int32_t n_recv, int32_t n_send, int32_t R) {
+  if (!pi) return fail(MF_ERR_INVALID, "pi_host is NULL");
+  if (n_recv < 1 || n_send < 1 || R < 0 || R > n_recv) return fail(MF_ERR_INVALID, "bad layer counts");
+  for (int l = 0; l < n_recv; ++l) {
+    if (l < R && pi[l] != -1) return fail(MF_ERR_INVALID, "layer %d < R must map to -1", l);
+    if (l >= R && (pi[l] < 0 || pi[l] >= n_send))
+      return fail(MF_ERR_INVALID, "layer %d maps to %d outside [0, %d)", l, pi[l], n_send);
+  }
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu,
+                                  int32_t n_seq, int64_t capacity, mf_bsr* out) {
+  if (!out) return fail(MF_ERR_INVALID, "out is NULL");
+  if (H_s < 1 || H_s > 64) return fail(MF_ERR_INVALID, "H_s must be in [1, 64] (got %d)", H_s);
+  Geometry g;
+  mf_status st = build_geometry(cu, n_seq, B, g);
+  if (st != MF_OK) return st;
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  BsrOwner* own = new (std::nothrow) BsrOwner();
+  if (!own) return fail(MF_ERR_OOM, "host allocation failed");
+  mf_bsr b{};
+  b.B = B;
+  b.H_s = H_s;
+  b.n_seq = n_seq;
+  b.n_brow = g.n_brow;
+  b.nb_max = g.nb_max;
+  b.T = g.T;
+  b.n_causal = g.n_causal;
+  if (capacity < 0) capacity = g.n_causal;
+  if ((st = alloc_bsr_meta(g, H_s, &b, own)) != MF_OK) {
+    delete own;
+    return st;
+  }
+  if ((st = alloc_bsr_data(capacity, H_s, B, &b, own)) != MF_OK) {
+    (void)hipFree(own->meta);
+    delete own;
+    return st;
+  }
+  own->geom = std::move(g);
+  b._owner = own;
+  *out = b;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr) {
+  if (!bsr) return MF_OK;
+  BsrOwner* own = static_cast<BsrOwner*>(bsr->_owner);
+  if (own) {
+    if (ctx) (void)hipSetDevice(ctx->device);
+    if (own->meta) (void)hipFree(own->meta);
+    if (own->data) (void)hipFree(own->data);
+    delete own;
+  }
+  std::memset(bsr, 0, sizeof(*bsr));
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_bsr_download(mf_ctx* ctx, mf_bsr* bsr, int32_t* block_ptr_host,
+                                    int32_t* block_idx_host, uint16_t* probs_host,
+                                    float* rkm_host) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  int32_t cnt[2] = {0, 0};
+  MF_HIP(hipMemcpy(cnt, bsr->counters, sizeof(cnt), hipMemcpyDeviceToHost), "reading kept-block count");
+  bsr->nnzb = std::min<int64_t>(cnt[0], bsr->capacity);
+  const size_t nn = (size_t)bsr->nnzb;
+  if (block_ptr_host)
+    MF_HIP(hipMemcpy(block_ptr_host, bsr->block_ptr, (size_t)(bsr->n_brow + 1) * 4, hipMemcpyDeviceToHost), "copy block_ptr");
+  if (block_idx_host && nn)
+    MF_HIP(hipMemcpy(block_idx_host, bsr->block_idx, nn * 4, hipMemcpyDeviceToHost), "copy block_idx");
+  if (probs_host && nn)
+    MF_HIP(hipMemcpy(probs_host, bsr->probs, nn * probs_block_bytes(bsr->H_s, bsr->B), hipMemcpyDeviceToHost), "copy probs");
+  if (rkm_host && bsr->T)
+    MF_HIP(hipMemcpy(rkm_host, bsr->row_kept_mass, (size_t)bsr->H_s * bsr->T * 4, hipMemcpyDeviceToHost), "copy row_kept_mass");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_bsr_upload(mf_ctx* ctx, mf_bsr* bsr, const int32_t* block_ptr_host,
+                                  const int32_t* block_idx_host, const uint16_t* probs_host,
+                                  const float* rkm_host) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  if (!block_ptr_host || !rkm_host) return fail(MF_ERR_INVALID, "block_ptr_host and row_kept_mass_host are required");
+  const BsrOwner* own = static_cast<const BsrOwner*>(bsr->_owner);
+  const Geometry& g = own->geom;
+  if (block_ptr_host[0] != 0) return fail(MF_ERR_INVALID, "block_ptr[0] must be 0");
+  for (int b = 0; b < g.n_brow; ++b)
+    if (block_ptr_host[b + 1] < block_ptr_host[b]) return fail(MF_ERR_INVALID, "block_ptr decreases at row %d", b);
+  const int64_t nnzb = block_ptr_host[g.n_brow];
+  if (nnzb > bsr->capacity)
+    return fail(MF_ERR_CAPACITY, "%lld blocks exceed the store capacity %lld", (long long)nnzb, (long long)bsr->capacity);
+  if (nnzb > 0 && (!block_idx_host || !probs_host)) return fail(MF_ERR_INVALID, "block_idx_host / probs_host missing");
+  std::vector<int32_t> rows((size_t)nnzb);
+  for (int b = 0; b < g.n_brow; ++b) {
+    const int I = g.info[4 * b + 3];
+    for (int t = block_ptr_host[b]; t < block_ptr_host[b + 1]; ++t) {
+      const int J = block_idx_host[t];
+      if (J < 0 || J > I) return fail(MF_ERR_INVALID, "block column %d outside [0, %d] in row %d", J, I, b);
+      if (t > block_ptr_host[b] && J <= block_idx_host[t - 1])
+        return fail(MF_ERR_INVALID, "block columns of row %d are not ascending", b);
+      rows[(size_t)t] = b;
+    }
+  }
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  MF_HIP(hipMemcpy(bsr->block_ptr, block_ptr_host, (size_t)(g.n_brow + 1) * 4, hipMemcpyHostToDevice), "copy block_ptr");
+  if (nnzb > 0) {
+    MF_HIP(hipMemcpy(bsr->block_idx, block_idx_host, (size_t)nnzb * 4, hipMemcpyHostToDevice), "copy block_idx");
+    MF_HIP(hipMemcpy(bsr->block_row, rows.data(), (size_t)nnzb * 4, hipMemcpyHostToDevice), "copy block_row");
+    MF_HIP(hipMemcpy(bsr->probs, probs_host, (size_t)nnzb * probs_block_bytes(bsr->H_s, bsr->B), hipMemcpyHostToDevice), "copy probs");
+  }
+  if (g.T) MF_HIP(hipMemcpy(bsr->row_kept_mass, rkm_host, (size_t)bsr->H_s * g.T * 4, hipMemcpyHostToDevice), "copy row_kept_mass");
+  const int32_t cnt[2] = {(int32_t)nnzb, 0};
+  MF_HIP(hipMemcpy(bsr->counters, cnt, sizeof(cnt), hipMemcpyHostToDevice), "copy counters");
+  bsr->nnzb = nnzb;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
+                                     int32_t d, float tau, mf_bsr* bsr, void* stream) {
+  mf_status st = validate_compress(Q, K, dtype, d, tau, bsr);
+  if (st != MF_OK) return st;
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  if (bsr->n_brow == 0) return MF_OK;
+  mf::CompressArgs a;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
+  MF_HIP(mf::compress_fill(a, s), "compress gather launch");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_bsr_sync(mf_ctx* ctx, mf_bsr* bsr, void* stream) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+  int32_t cnt[2] = {0, 0};
+  MF_HIP(hipMemcpy(cnt, bsr->counters, sizeof(cnt), hipMemcpyDeviceToHost), "reading kept-block count");
+  bsr->nnzb = std::min<int64_t>(cnt[0], bsr->capacity);
+  if (cnt[1]) return fail(MF_ERR_CAPACITY, "%d kept blocks exceed the store capacity %lld", cnt[0],
+                          (long long)bsr->capacity);
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
+                                int32_t H_s, int32_t d, const int32_t* cu, int32_t n_seq, float tau,
+                                int32_t B, void* stream, mf_bsr* out) {
+  if (!out) return fail(MF_ERR_INVALID, "out is NULL");
+  mf_bsr b{};
+  mf_status st = mf_bsr_create(ctx, H_s, B, cu, n_seq, 0, &b);
+  if (st != MF_OK) return st;
+  if ((st = validate_compress(Q, K, dtype, d, tau, &b)) != MF_OK) {
+    mf_bsr_free(ctx, &b);
+    return st;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BsrOwner* own = static_cast<BsrOwner*>(b._owner);
+  if (b.n_brow > 0) {
+    mf::CompressArgs a;
+    // selection first with room for every causal block, then exact allocation
+    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, 0, a)) != MF_OK) {
+      mf_bsr_free(ctx, &b);
+      return st;
+    }
+    a.capacity = b.n_causal;
+    hipError_t e = mf::compress_plan(a, s);
+    if (e != hipSuccess) {
+      mf_bsr_free(ctx, &b);
+      return hip_fail(e, "compress statistics / selection launch");
+    }
+    int32_t cnt[2] = {0, 0};
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipMemcpy(cnt, b.counters, sizeof(cnt), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) {
+      mf_bsr_free(ctx, &b);
+      return hip_fail(e, "reading kept-block count");
+    }
+    (void)hipFree(own->data);
+    own->data = nullptr;
+    if ((st = alloc_bsr_data(cnt[0], H_s, B, &b, own)) != MF_OK) {
+      mf_bsr_free(ctx, &b);
+      return st;
+    }
+    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, b.capacity, a)) != MF_OK) {
+      mf_bsr_free(ctx, &b);
+      return st;
+    }
+    e = mf::compress_fill(a, s);
+    if (e != hipSuccess) {
+      mf_bsr_free(ctx, &b);
+      return hip_fail(e, "compress gather launch");
+    }
+    b.nnzb = cnt[0];
+  }
+  *out = b;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_v_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B,
+                                 const void* V, mf_dtype dtype, int32_t H_kv, int32_t d,
+                                 const int32_t* page_table, int32_t page_size,
+                                 int32_t pages_per_seq, mf_vfrag* out, void* stream) {
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  if (out && out->_owner) return fail(MF_ERR_INVALID, "vfrag already prepared; free it first");
+  return vfrag_prepare(ctx, cu, n_seq, B, V, dtype, H_kv, d, page_table, page_size, pages_per_seq,
+                       out, false, static_cast<hipStream_t>(stream));
+}
+
+MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {
+  if (ctx) (void)hipSetDevice(ctx->device);
+  vfrag_release(vf);
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W,
+                                         int32_t H_r, const mf_vfrag* vf,
+                                         const int32_t* kvmap, float* O, void* stream) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  if (!vf || !vf->_owner) return fail(MF_ERR_INVALID, "prepared V is NULL");
+  if (!W || !O) return fail(MF_ERR_INVALID, "W or O is NULL");
+  if (H_r < 1) return fail(MF_ERR_INVALID, "H_r must be >= 1");
+  if (vf->B != bsr->B || vf->n_brow != bsr->n_brow || vf->T != bsr->T)
+    return fail(MF_ERR_INVALID, "prepared V geometry (B=%d, %d block rows, T=%lld) differs from the store's "
+                "(B=%d, %d, T=%lld)", vf->B, vf->n_brow, (long long)vf->T, bsr->B, bsr->n_brow,
+                (long long)bsr->T);
+  const VfragOwner* vo = static_cast<const VfragOwner*>(vf->_owner);
+  const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
+  if (vo->geom.cu != bo->geom.cu) return fail(MF_ERR_INVALID, "prepared V has different cu_seqlens");
+  if (!mf::retrieve_supported(bsr->B, vf->d, H_r, bsr->H_s))
+    return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", bsr->B, vf->d, H_r, bsr->H_s);
+  mf::HeadMap hm;
+  mf_status st = build_headmap(kvmap, H_r, vf->H_kv, hm);
+  if (st != MF_OK) return st;
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  if (bsr->n_brow == 0) return MF_OK;
+  mf::RetrieveArgs a{};
+  a.probs = bsr->probs;
+  a.block_ptr = bsr->block_ptr;
+  a.block_idx = bsr->block_idx;
+  a.info = bsr->brow_info;
+  a.order = bsr->brow_order;
+  a.capacity = bsr->capacity;
+  a.n_brow = bsr->n_brow;
+  a.H_s = bsr->H_s;
+  a.B = bsr->B;
+  a.d = vf->d;
+  a.T = bsr->T;
+  a.rkm = bsr->row_kept_mass;
+  a.W = W;
+  a.H_r = H_r;
+  a.H_kv = vf->H_kv;
+  a.vfrag = vf->frag;
+  a.vexps = vf->exps;
+  a.hm = hm;
+  a.O = O;
+  MF_HIP(mf::retrieve(a, static_cast<hipStream_t>(stream)), "retrieve launch");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,
+                                const void* V, mf_dtype vdtype, int32_t H_kv, int32_t d,
+                                const int32_t* page_table, int32_t page_size, int32_t pages_per_seq,
+                                const int32_t* kvmap, float* O, void* stream) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
+  if (!mf::retrieve_supported(bsr->B, d, H_r, bsr->H_s))
+    return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", bsr->B, d, H_r, bsr->H_s);
+  mf::HeadMap hm;
+  if ((st = build_headmap(kvmap, H_r, H_kv, hm)) != MF_OK) return st;
+  if (!W || !O) return fail(MF_ERR_INVALID, "W or O is NULL");
+  st = vfrag_prepare(ctx, bo->geom.cu.data(), bsr->n_seq, bsr->B, V, vdtype, H_kv, d, page_table,
+                     page_size, pages_per_seq, &ctx->vf_retrieve, true, static_cast<hipStream_t>(stream));
+  if (st != MF_OK) return st;
+  return mf_retrieve_prepared(ctx, bsr, W, H_r, &ctx->vf_retrieve, kvmap, O, stream);
+}
+
+MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K, const void* V,
+                                       mf_dtype dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                                       const int32_t* cu, int32_t n_seq, const int32_t* kvmap,
+                                       float* O, void* stream) {
+  if (!Q || !K || !V || !O) return fail(MF_ERR_INVALID, "Q, K, V or O is NULL");
+  mf_status st = check_dtype(dtype);
+  if (st != MF_OK) return st;
+  if (!mf::dense_supported(dtype_code(dtype), d))
+    return fail(MF_ERR_UNSUPPORTED, "dense attention supports d = 64 or 128 (got %d)", d);
+  if (H_kv < 1 || H_kv > 64) return fail(MF_ERR_INVALID, "H_kv must be in [1, 64]");
+  mf::HeadMap hm;
+  if ((st = build_headmap(kvmap, H_q, H_kv, hm)) != MF_OK) return st;
+  Geometry g;
+  if ((st = build_geometry(cu, n_seq, 64, g)) != MF_OK) return st;
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g.n_brow == 0) return MF_OK;
+  // geometry tables (info, order) cached on the device while cu_seqlens stays the same
+  if (ctx->dense_cu != g.cu) {
+    if ((st = ensure(ctx->dense_tables, (size_t)g.n_brow * 20 + 512, "dense geometry")) != MF_OK) return st;
+    char* base = static_cast<char*>(ctx->dense_tables.p);
+    MF_HIP(hipMemcpy(base, g.info.data(), (size_t)g.n_brow * 16, hipMemcpyHostToDevice), "uploading geometry");
+    MF_HIP(hipMemcpy(base + align_up((size_t)g.n_brow * 16, 256), g.order.data(), (size_t)g.n_brow * 4,
+                     hipMemcpyHostToDevice), "uploading geometry");
+    ctx->dense_cu = g.cu;
+    ctx->dense_nbrow = g.n_brow;
+  }
+  st = vfrag_prepare(ctx, cu, n_seq, 64, V, dtype, H_kv, d, nullptr, 0, 0, &ctx->vf_dense, true, s);
+  if (st != MF_OK) return st;
+  char* base = static_cast<char*>(ctx->dense_tables.p);
+  mf::DenseArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.dtype = dtype_code(dtype);
+  a.H_q = H_q;
+  a.H_kv = H_kv;
+  a.d = d;
+  a.T = g.T;
+  a.n_brow = g.n_brow;
+  a.info = reinterpret_cast<const int32_t*>(base);
+  a.order = reinterpret_cast<const int32_t*>(base + align_up((size_t)g.n_brow * 16, 256));
+  a.vfrag = ctx->vf_dense.frag;
+  a.vexps = ctx->vf_dense.exps;
+  a.hm = hm;
+  a.O = O;
+  MF_HIP(mf::dense_attention(a, s), "dense attention launch");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return fail(MF_ERR_INVALID, "dst or src is NULL");
+  if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return fail(MF_ERR_INVALID, "copy probe needs 16-byte aligned pointers and a multiple of 16 bytes");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(mf::copy_probe(dst, src, bytes, static_cast<hipStream_t>(stream)), "copy probe launch");
+  return MF_OK;
+}
+
+}  // extern "C"

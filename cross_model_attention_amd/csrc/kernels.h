@@ -1,0 +1,103 @@
+// Internal launcher interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mf {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+struct CompressArgs {
+  const void* Q;
+  const void* K;
+  int dtype, H_s, d, B;
+  int64_t T;
+  int n_brow, nb_max;
+  const int32_t* info;   // [n_brow][4]
+  const int32_t* order;  // [n_brow]
+  double tau;
+  float scale2;          // log2(e) / sqrt(d)
+  // context scratch
+  float* lse2;           // [H_s][T]   log2-domain row logsumexp
+  float* Mh;             // [H_s][n_brow][nb_max] per-head block masses
+  double* M;             // [n_brow][nb_max] head-summed block masses
+  uint8_t* flags;        // [n_brow][nb_max] kept flags
+  int32_t* counts;       // [n_brow]
+  float* part;           // [capacity][H_s][B] per-block row sums of stored probs
+  // the store
+  int32_t* block_ptr;
+  int32_t* block_idx;
+  int32_t* block_row;
+  uint16_t* probs;
+  float* rkm;
+  int32_t* counters;
+  int64_t capacity;
+};
+
+// statistics, head reduction, selection and scan (writes block_ptr and counters)
+hipError_t compress_plan(const CompressArgs& a, hipStream_t s);
+// emit block indices, gather kept probabilities, kept row mass
+hipError_t compress_fill(const CompressArgs& a, hipStream_t s);
+bool compress_supported(int dtype, int B, int d);
+size_t stats_lds_bytes(int B, int nb_max);
+
+struct VprepArgs {
+  const void* V;
+  int dtype, H_kv, d, B;
+  int64_t T;
+  int n_brow;
+  const int32_t* info;
+  const int32_t* page_table;  // NULL = contiguous
+  int page_size, pages_per_seq;
+  const int32_t* brow_seq;    // [n_brow] sequence of each block row (paged path)
+  uint32_t* vmax_bits;        // [H_kv] scratch
+  uint16_t* frag;
+  int32_t* exps;
+};
+hipError_t v_prepare(const VprepArgs& a, hipStream_t s);
+
+struct HeadMap {
+  int8_t perm[64];  // receiver heads ordered by KV head
+  int8_t kv[64];    // KV head of each receiver head
+};
+
+struct RetrieveArgs {
+  const uint16_t* probs;
+  const int32_t* block_ptr;
+  const int32_t* block_idx;
+  const int32_t* info;
+  const int32_t* order;
+  int64_t capacity;      // blocks allocated in the store (clamps block_ptr after an overflow)
+  int n_brow, H_s, B, d;
+  int64_t T;
+  const float* rkm;
+  const float* W;
+  int H_r, H_kv;
+  const uint16_t* vfrag;
+  const int32_t* vexps;
+  HeadMap hm;
+  float* O;
+};
+hipError_t retrieve(const RetrieveArgs& a, hipStream_t s);
+bool retrieve_supported(int B, int d, int H_r, int H_s);
+
+struct DenseArgs {
+  const void* Q;
+  const void* K;
+  int dtype, H_q, H_kv, d;
+  int64_t T;
+  int n_brow;            // 64-token block rows
+  const int32_t* info;
+  const int32_t* order;
+  const uint16_t* vfrag; // prepared V with B = 64
+  const int32_t* vexps;
+  HeadMap hm;
+  float* O;
+};
+hipError_t dense_attention(const DenseArgs& a, hipStream_t s);
+bool dense_supported(int dtype, int d);
+
+hipError_t copy_probe(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+}  // namespace mf

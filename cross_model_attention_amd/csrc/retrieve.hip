@@ -1,0 +1,485 @@
+// Fused retrieve: kept sender blocks -> receiver attention output, plus the V preparation it
+// reads.
+//
+// [MapFlow开源, section 算得省的:融合内核执行] (aitest123.com) and [Reuses Attention, third
+// component] (roboind.com): the kernel reads the sparse blocks, performs the linear combination
+// of sender heads into receiver heads in on-chip memory, multiplies by the receiver's own V and
+// accumulates, writing only the output.  Neither the dense map nor the mixed map touches HBM.
+//
+// k_retrieve, one workgroup (8 waves) per (block row, 16-row tile), all receiver heads:
+//   for each kept block J of the row, in column order:
+//     stage 1  head mix on MFMA (bf16): Ahat[g, i, j] = sum_h Ws[g, h] P[h, i, j] for the 16 rows
+//              x B keys, where Ws = W * 2^s_g is split into bf16 hi + lo parts so the product
+//              with the exactly-bf16 P keeps ~16 bits of W; the fp32 sums are rounded to fp16
+//              and staged in LDS (double buffered)
+//     stage 2  P.V on MFMA (fp16): O[g] += Ahat[g] V[kv(g)] with V from the prepared fp16
+//              operand tiles (L2-resident: each V block is shared by every row that keeps it)
+//   epilogue   O = acc * 2^-t_kv / den, den[g, i] = sum_h Ws[g, h] row_kept_mass[h, i] (den and
+//              acc both carry 2^s_g)
+// The kept-block probabilities are streamed once with non-temporal loads; the next block's tile
+// is fetched into registers while the current block's P.V runs.
+#include "common.h"
+#include "kernels.h"
+
+namespace mf {
+
+// ------------------------------------------------------------------------------------------
+// V preparation
+// ------------------------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ float load_v(const T* V, int64_t idx);
+template <>
+__device__ __forceinline__ float load_v<uint16_t>(const uint16_t* V, int64_t idx) {
+  return bf16_to_f32(V[idx]);
+}
+template <>
+__device__ __forceinline__ float load_v<float>(const float* V, int64_t idx) {
+  return V[idx];
+}
+
+// element offset of (token-in-sequence kloc, kv head, column d) for contiguous or paged V
+__device__ __forceinline__ int64_t v_offset(const BrowInfo& bi, int seq, int kloc, int kv, int d,
+                                            int H_kv, int D, const int32_t* page_table,
+                                            int page_size, int pages_per_seq) {
+  if (page_table == nullptr) return ((int64_t)(bi.seq0 + kloc) * H_kv + kv) * D + d;
+  const int page = page_table[(int64_t)seq * pages_per_seq + kloc / page_size];
+  return (((int64_t)page * page_size + kloc % page_size) * H_kv + kv) * D + d;
+}
+
+__global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_vmax(const T* __restrict__ V, int H_kv, int D, int B,
+                                              const int32_t* __restrict__ info,
+                                              const int32_t* __restrict__ brow_seq,
+                                              const int32_t* __restrict__ page_table,
+                                              int page_size, int pages_per_seq,
+                                              uint32_t* __restrict__ vmax_bits) {
+  __shared__ float red[4];
+  const int brow = blockIdx.x, kv = blockIdx.y;
+  const BrowInfo bi = load_info(info, brow);
+  const int seq = brow_seq[brow];
+  float m = 0.f;
+  for (int e = threadIdx.x; e < B * D; e += blockDim.x) {
+    const int kloc = bi.I * B + e / D;
+    if (kloc < bi.n)
+      m = fmaxf(m, fabsf(load_v<T>(V, v_offset(bi, seq, kloc, kv, e % D, H_kv, D, page_table,
+                                                   page_size, pages_per_seq))));
+  }
+  // NaN must win the maximum so that the scale falls back to 1
+  if (m != m) m = __uint_as_float(0x7FC00000u);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = red[0];
+    for (int r = 1; r < (int)(blockDim.x >> 6); ++r) t = fmaxf(t, red[r]);
+    atomicMax(&vmax_bits[kv], __float_as_uint(t));
+  }
+}
+
+__global__ void k_vexps(const uint32_t* __restrict__ vmax_bits, int H_kv, int32_t* __restrict__ exps) {
+  const int kv = threadIdx.x;
+  if (kv >= H_kv) return;
+  const float m = __uint_as_float(vmax_bits[kv]);
+  int e = 0;
+  if (m > 0.f && m < __builtin_inff()) {
+    int ex;
+    frexpf(m, &ex);          // m <= 2^ex
+    e = 15 - ex;
+    e = max(-100, min(100, e));
+  }
+  exps[kv] = e;
+}
+
+// One thread per 16-byte operand record: lane (a, dd) of tile (kv, block row, 32-key chunk,
+// 16-column slice) holds V[key(e)][kv][16 dt + dd] for e = 0..7, where within the chunk
+// key(e) = 4a + e for e < 4 and 16 + 4a + (e - 4) otherwise.  That key order matches the
+// accumulator layout of two stacked 16x16 score tiles, so attention probabilities computed in
+// registers can be used as the other MFMA operand without a transpose.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_vconvert(const T* __restrict__ V, int H_kv, int B,
+                                                  int n_brow, const int32_t* __restrict__ info,
+                                                  const int32_t* __restrict__ brow_seq,
+                                                  const int32_t* __restrict__ page_table,
+                                                  int page_size, int pages_per_seq,
+                                                  const int32_t* __restrict__ exps,
+                                                  uint16_t* __restrict__ frag) {
+  constexpr int NDT = D / 16;
+  const int NCH = B / 32;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)H_kv * n_brow * NCH * NDT * 64;
+  if (gid >= total) return;
+  const int lane = (int)(gid & 63);
+  int64_t rec = gid >> 6;
+  const int dt = (int)(rec % NDT);
+  rec /= NDT;
+  const int ch = (int)(rec % NCH);
+  rec /= NCH;
+  const int brow = (int)(rec % n_brow);
+  const int kv = (int)(rec / n_brow);
+  const BrowInfo bi = load_info(info, brow);
+  const int seq = brow_seq[brow];
+  const int a = lane >> 4, dd = lane & 15;
+  const float scale = ldexpf(1.f, exps[kv]);
+  uint32_t packed[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    uint32_t two = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int e = 2 * p + q;
+      const int koff = 32 * ch + (e < 4 ? 4 * a + e : 16 + 4 * a + (e - 4));
+      const int kloc = bi.I * B + koff;
+      float v = 0.f;
+      if (kloc < bi.n)
+        v = load_v<T>(V, v_offset(bi, seq, kloc, kv, 16 * dt + dd, H_kv, D, page_table, page_size,
+                                   pages_per_seq));
+      two |= (uint32_t)f32_to_f16_bits(v * scale) << (16 * q);
+    }
+    packed[p] = two;
+  }
+  st16(frag + gid * 8, v4u{packed[0], packed[1], packed[2], packed[3]});
+}
+
+template <typename T, int D>
+static hipError_t vconvert_t(const VprepArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.H_kv * a.n_brow * (a.B / 32) * (D / 16) * 64;
+  const unsigned grid = (unsigned)((total + 255) / 256);
+  hipLaunchKernelGGL((k_vconvert<T, D>), dim3(grid), dim3(256), 0, s, (const T*)a.V, a.H_kv, a.B,
+                     a.n_brow, a.info, a.brow_seq, a.page_table, a.page_size, a.pages_per_seq,
+                     a.exps, a.frag);
+  return hipGetLastError();
+}
+
+hipError_t v_prepare(const VprepArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, a.vmax_bits, a.H_kv, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.dtype == DT_BF16)
+    hipLaunchKernelGGL((k_vmax<uint16_t>), dim3(a.n_brow, a.H_kv), dim3(256), 0, s,
+                       (const uint16_t*)a.V, a.H_kv, a.d, a.B, a.info, a.brow_seq, a.page_table,
+                       a.page_size, a.pages_per_seq, a.vmax_bits);
+  else
+    hipLaunchKernelGGL((k_vmax<float>), dim3(a.n_brow, a.H_kv), dim3(256), 0, s,
+                       (const float*)a.V, a.H_kv, a.d, a.B, a.info, a.brow_seq, a.page_table,
+                       a.page_size, a.pages_per_seq, a.vmax_bits);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_vexps, dim3(1), dim3(64), 0, s, a.vmax_bits, a.H_kv, a.exps);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.dtype == DT_BF16) return a.d == 128 ? vconvert_t<uint16_t, 128>(a, s) : vconvert_t<uint16_t, 64>(a, s);
+  return a.d == 128 ? vconvert_t<float, 128>(a, s) : vconvert_t<float, 64>(a, s);
+}
+
+// ------------------------------------------------------------------------------------------
+// k_retrieve
+// ------------------------------------------------------------------------------------------
+constexpr int RT_ROWS = 16;     // rows per work item
+constexpr int RT_WAVES = 8;     // waves per workgroup
+constexpr int ROWS_PER_WAVE = RT_ROWS / RT_WAVES;
+
+template <int B>
+struct AhatLayout {
+  static constexpr int kRowBytes = B * 2 + 16;            // 16 B pad: conflict-free reads
+  static constexpr int kHeadBytes = RT_ROWS * kRowBytes + 16;  // 16 B pad: conflict-free writes
+};
+
+// Mixing tiles: receiver heads come in chunks of 16; a full chunk uses two N-tiles (bf16 "hi"
+// and "lo" parts of the scaled weights), a last chunk of <= 8 heads packs hi in columns 0..7 and
+// lo in columns 8..15 of one tile.  HP = ceil(H_r / 8) tiles in total; HP odd <=> last chunk
+// packed.  The same HP is the number of receiver heads each wave owns in stage 2.
+template <int HP>
+struct MixTiles {
+  static constexpr bool kPackedLast = (HP & 1) != 0;
+  __device__ static void head_of(int nt, int c, int& g, bool& lo) {
+    if (kPackedLast && nt == HP - 1) {
+      g = 16 * (nt / 2) + (c & 7);
+      lo = c >= 8;
+    } else {
+      g = 16 * (nt / 2) + c;
+      lo = (nt & 1) != 0;
+    }
+  }
+};
+
+template <int B, int D, int HP, int KC>
+__global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
+    const uint16_t* __restrict__ probs, const int32_t* __restrict__ block_ptr,
+    const int32_t* __restrict__ block_idx, const int32_t* __restrict__ info,
+    const int32_t* __restrict__ order, int64_t capacity, int n_brow, int H_s, int64_t T_tot,
+    const float* __restrict__ rkm, const float* __restrict__ W, int H_r,
+    const uint16_t* __restrict__ vfrag, const int32_t* __restrict__ vexps, HeadMap hm,
+    float* __restrict__ O) {
+  constexpr int NRT = B / RT_ROWS;         // row tiles per block row
+  constexpr int MT = B / 16;               // 16-key M-tiles per row
+  constexpr int NCH = B / 32;              // 32-key chunks per block
+  constexpr int NDT = D / 16;              // 16-column output tiles
+  constexpr int RB = AhatLayout<B>::kRowBytes;
+  constexpr int GB = AhatLayout<B>::kHeadBytes;
+  constexpr int HR_MAX = 8 * HP;
+
+  __shared__ __attribute__((aligned(16))) unsigned char s_ahat[2][HR_MAX * GB];
+  __shared__ float s_w[HR_MAX][64];        // scaled weights (hi + lo), fp32
+  __shared__ float s_den[HR_MAX][RT_ROWS];
+  __shared__ int s_sexp[HR_MAX];
+
+  // ---- work item: XCD-aware (the row tiles of one block row share an XCD) --------------------
+  const int b = blockIdx.x;
+  const int xcd = b & 7;
+  const int q = b >> 3;
+  const int rt = q % NRT;
+  const int gidx = (q / NRT) * 8 + xcd;
+  if (gidx >= n_brow) return;
+  const int brow = order[gidx];
+  const BrowInfo bi = load_info(info, brow);
+  const int rows_blk = min(B, bi.n - bi.I * B);
+  const int rows = min(RT_ROWS, rows_blk - RT_ROWS * rt);
+  if (rows <= 0) return;
+  const int row0 = RT_ROWS * rt;              // first row of the tile within the block row
+  const int HGp = (H_s + 7) >> 3;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
+
+  // ---- setup: per-head scale, scaled weights, denominators ---------------------------------
+  if (threadIdx.x < HR_MAX) {
+    const int g = threadIdx.x;
+    int e = 0;
+    if (g < H_r) {
+      float sa = 0.f;
+      for (int h = 0; h < H_s; ++h) sa += fabsf(W[g * H_s + h]);
+      if (sa > 0.f && sa < __builtin_inff()) {
+        int ex;
+        frexpf(sa, &ex);      // sum |W| <= 2^ex
+        e = max(-100, min(100, 15 - ex));
+      }
+    }
+    s_sexp[g] = e;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < HR_MAX * 64; t += blockDim.x) {
+    const int g = t >> 6, h = t & 63;
+    float v = 0.f;
+    if (g < H_r && h < H_s) {
+      const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
+      const float hi = bf16_to_f32(f32_to_bf16(x));
+      const float lo = bf16_to_f32(f32_to_bf16(x - hi));
+      v = hi + lo;
+    }
+    s_w[g][h] = v;
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < HR_MAX * RT_ROWS; t += blockDim.x) {
+    const int g = t / RT_ROWS, i = t % RT_ROWS;
+    float den = 0.f;
+    if (g < H_r && i < rows)
+      for (int h = 0; h < H_s; ++h) den += s_w[g][h] * rkm[(size_t)h * T_tot + bi.tok0 + row0 + i];
+    s_den[g][i] = den;
+  }
+
+  // stage-1 B operands: weights of virtual heads (hi / lo) for head dims 32kc + 8a + e
+  v8s wop[HP][KC];
+#pragma unroll
+  for (int nt = 0; nt < HP; ++nt) {
+    int g;
+    bool lo;
+    MixTiles<HP>::head_of(nt, c, g, lo);
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      v8s v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int h = 32 * kc + 8 * a + e;
+        uint16_t bits = 0;
+        if (g < H_r && h < H_s) {
+          const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
+          const uint16_t hb = f32_to_bf16(x);
+          bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
+        }
+        v[e] = (short)bits;
+      }
+      wop[nt][kc] = v;
+    }
+  }
+
+  // stage-2 ownership: slots w*HP .. w*HP+HP-1 of the kv-sorted head list
+  int sg[HP];
+#pragma unroll
+  for (int j = 0; j < HP; ++j) {
+    const int s = w * HP + j;
+    sg[j] = s < H_r ? (int)hm.perm[s] : -1;
+  }
+  v4f acc[HP][NDT];
+#pragma unroll
+  for (int j = 0; j < HP; ++j)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = zero4();
+
+  const int t0 = (int)min((int64_t)block_ptr[brow], capacity);
+  const int t1 = (int)min((int64_t)block_ptr[brow + 1], capacity);
+  const size_t blk_elems = (size_t)HGp * B * B * 8;
+  const int kbrow0 = brow - bi.I;          // block row holding key block 0 of this sequence
+
+  // P operands of this wave: rows ROWS_PER_WAVE*w + rr, all M-tiles, KC head chunks
+  v4u pa[ROWS_PER_WAVE][MT][KC];
+  auto load_p = [&](int t) {
+    const uint16_t* pb = probs + (size_t)t * blk_elems;
+#pragma unroll
+    for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+      const int r = row0 + ROWS_PER_WAVE * w + rr;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int hg = 4 * kc + a;
+          pa[rr][mt][kc] = hg < HGp ? ld16_nt(pb + (((size_t)hg * B + r) * B + 16 * mt + c) * 8)
+                                    : zero_u4();
+        }
+    }
+  };
+  if (t0 < t1) load_p(t0);
+  __syncthreads();
+
+  for (int t = t0; t < t1; ++t) {
+    unsigned char* buf = s_ahat[(t - t0) & 1];
+    // ---- stage 1: head mix -> fp16 Ahat in LDS ----
+#pragma unroll
+    for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
+      const int ii = ROWS_PER_WAVE * w + rr;
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+        v4f mix[2][HP];
+#pragma unroll
+        for (int half = 0; half < 2; ++half)
+#pragma unroll
+          for (int nt = 0; nt < HP; ++nt) {
+            v4f m4 = zero4();
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) m4 = mfma_bf16(as_v8s(pa[rr][2 * ch + half][kc]), wop[nt][kc], m4);
+            mix[half][nt] = m4;
+          }
+        // combine hi + lo per receiver head and write 8 fp16 values (keys of chunk ch, group a)
+#pragma unroll
+        for (int pr = 0; pr < (HP + 1) / 2; ++pr) {
+          const bool packed = MixTiles<HP>::kPackedLast && (2 * pr == HP - 1);
+          float v[8];
+#pragma unroll
+          for (int half = 0; half < 2; ++half)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (packed) {
+                const float x = mix[half][2 * pr][i];
+                const float y = __int_as_float(__builtin_amdgcn_update_dpp(
+                    0, __float_as_int(x), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
+                v[4 * half + i] = x + y;
+              } else {
+                v[4 * half + i] = mix[half][2 * pr][i] + mix[half][2 * pr + 1][i];
+              }
+            }
+          const int g = 16 * pr + c;
+          const bool wr = packed ? (c < 8 && g < H_r) : (g < H_r);
+          if (wr) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p)
+              pk[p] = (uint32_t)f32_to_f16_bits(v[2 * p]) | ((uint32_t)f32_to_f16_bits(v[2 * p + 1]) << 16);
+            *reinterpret_cast<v4u*>(buf + g * GB + ii * RB + (ch * 4 + a) * 16) = v4u{pk[0], pk[1], pk[2], pk[3]};
+          }
+        }
+      }
+    }
+    if (t + 1 < t1) load_p(t + 1);
+    __syncthreads();
+
+    // ---- stage 2: P.V for this wave's receiver heads ----
+    const int J = block_idx[t];
+    const int kbrow = kbrow0 + J;
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      int cur_kv = -1;
+      v8h vop[NDT];
+#pragma unroll
+      for (int j = 0; j < HP; ++j) {
+        const int g = sg[j];
+        if (g < 0) continue;
+        const int kv = hm.kv[g];
+        if (kv != cur_kv) {
+          const uint16_t* vb = vfrag + ((((size_t)kv * n_brow + kbrow) * NCH + ch) * NDT) * 512 + lane * 8;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
+          cur_kv = kv;
+        }
+        const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + g * GB + c * RB + (ch * 4 + a) * 16));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < HP; ++j) {
+    const int g = sg[j];
+    if (g < 0) continue;
+    // den carries the same 2^s_g as the mixed map, so only V's scale is undone here
+    const float unscale = ldexpf(1.f, -vexps[hm.kv[g]]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ii = 4 * a + i;
+      if (ii >= rows) continue;
+      const float inv = unscale / s_den[g][ii];
+      float* orow = O + ((size_t)(bi.tok0 + row0 + ii) * H_r + g) * D;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
+    }
+  }
+}
+
+bool retrieve_supported(int B, int d, int H_r, int H_s) {
+  return (B == 32 || B == 64) && (d == 64 || d == 128) && H_r >= 1 && H_r <= 32 && H_s >= 1 &&
+         H_s <= 64;
+}
+
+template <int B, int D, int HP, int KC>
+static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
+  constexpr int NRT = B / RT_ROWS;
+  const unsigned groups = (unsigned)((a.n_brow + 7) / 8);
+  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC>), dim3(groups * 8 * NRT), dim3(RT_WAVES * 64), 0, s,
+                     a.probs, a.block_ptr, a.block_idx, a.info, a.order, a.capacity, a.n_brow, a.H_s, a.T,
+                     a.rkm, a.W, a.H_r, a.vfrag, a.vexps, a.hm, a.O);
+  return hipGetLastError();
+}
+
+template <int B, int D>
+static hipError_t retrieve_bd(const RetrieveArgs& a, hipStream_t s) {
+  const int HP = (a.H_r + 7) / 8;
+  const int KC = ((a.H_s + 7) / 8 + 3) / 4;
+  if (KC == 1) {
+    switch (HP) {
+      case 1: return retrieve_t<B, D, 1, 1>(a, s);
+      case 2: return retrieve_t<B, D, 2, 1>(a, s);
+      case 3: return retrieve_t<B, D, 3, 1>(a, s);
+      case 4: return retrieve_t<B, D, 4, 1>(a, s);
+    }
+  } else {
+    switch (HP) {
+      case 1: return retrieve_t<B, D, 1, 2>(a, s);
+      case 2: return retrieve_t<B, D, 2, 2>(a, s);
+      case 3: return retrieve_t<B, D, 3, 2>(a, s);
+      case 4: return retrieve_t<B, D, 4, 2>(a, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t retrieve(const RetrieveArgs& a, hipStream_t s) {
+  if (a.B == 64 && a.d == 128) return retrieve_bd<64, 128>(a, s);
+  if (a.B == 64 && a.d == 64) return retrieve_bd<64, 64>(a, s);
+  if (a.B == 32 && a.d == 128) return retrieve_bd<32, 128>(a, s);
+  if (a.B == 32 && a.d == 64) return retrieve_bd<32, 64>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mf

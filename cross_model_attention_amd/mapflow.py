@@ -1,0 +1,312 @@
+"""Python binding of libmapflow with the C ABI's names.
+
+Argument marshalling only: every step of compress / retrieve / dense attention runs in the HIP
+kernels of libmapflow.so.  PyTorch provides device memory and streams; tensors are passed to the
+library as raw device pointers.  Nothing here falls back to a CPU or PyTorch implementation: if
+the library is missing, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import MfBsr, MfVfrag, check, i32_array
+
+_L = _lib.load()
+
+
+def version() -> str:
+    return _L.mf_version().decode()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return _lib.MF_BF16
+    if t.dtype == torch.float32:
+        return _lib.MF_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _cu(cu_seqlens, T: int):
+    if cu_seqlens is None:
+        cu = [0, T]
+    else:
+        cu = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    return i32_array(cu), len(cu) - 1, cu
+
+
+class Context:
+    """A libmapflow context on one device (owns scratch memory)."""
+
+    _defaults: dict = {}
+
+    def __init__(self, device: int = 0):
+        h = ctypes.c_void_p()
+        check(_L.mf_create(int(device), ctypes.byref(h)))
+        self.handle = h
+        self.device = device
+
+    @classmethod
+    def default(cls, device: int | None = None) -> "Context":
+        if device is None:
+            device = torch.cuda.current_device()
+        if device not in cls._defaults:
+            cls._defaults[device] = Context(device)
+        return cls._defaults[device]
+
+    def close(self):
+        if self.handle:
+            _L.mf_destroy(self.handle)
+            self.handle = None
+
+
+def _ctx(ctx):
+    return ctx if ctx is not None else Context.default()
+
+
+# ----------------------------------------------------------------------------------------------
+# block store layout helpers (host-side data movement)
+# ----------------------------------------------------------------------------------------------
+def probs_store_to_canonical(bits: np.ndarray, H_s: int) -> np.ndarray:
+    """[nnzb, HG, B, B, 8] bf16 bits -> float64 [nnzb, H_s, B, B]."""
+    f = (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    n, HG, B, _, _ = f.shape
+    return f.transpose(0, 1, 4, 2, 3).reshape(n, HG * 8, B, B)[:, :H_s].astype(np.float64)
+
+
+def probs_canonical_to_store(probs: np.ndarray, H_s: int) -> np.ndarray:
+    """float [nnzb, H_s, B, B] holding bf16 values -> uint16 bits [nnzb, HG, B, B, 8]."""
+    n, H, B, _ = probs.shape
+    HG = (H_s + 7) // 8
+    full = np.zeros((n, HG * 8, B, B), dtype=np.float32)
+    full[:, :H] = probs
+    bits = (full.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    if not np.array_equal((bits.astype(np.uint32) << np.uint32(16)).view(np.float32), full):
+        raise ValueError("probs must hold bf16-representable values")
+    return np.ascontiguousarray(bits.reshape(n, HG, 8, B, B).transpose(0, 1, 3, 4, 2))
+
+
+class BlockStore:
+    """An mf_bsr owned by the library (freed with the object)."""
+
+    def __init__(self, ctx: Context, raw: MfBsr, cu: list[int]):
+        self.ctx = ctx
+        self.raw = raw
+        self.cu_seqlens = cu
+
+    @classmethod
+    def create(cls, H_s: int, B: int, cu_seqlens, capacity: int = -1, ctx=None) -> "BlockStore":
+        ctx = _ctx(ctx)
+        cu_arr, n_seq, cu = _cu(cu_seqlens, 0)
+        raw = MfBsr()
+        check(_L.mf_bsr_create(ctx.handle, int(H_s), int(B), cu_arr, n_seq, int(capacity), ctypes.byref(raw)))
+        return cls(ctx, raw, cu)
+
+    def __getattr__(self, name):
+        raw = self.__dict__.get("raw")
+        if raw is not None and name in dict(MfBsr._fields_):
+            return getattr(raw, name)
+        raise AttributeError(name)
+
+    def sync(self, stream=None) -> int:
+        check(_L.mf_bsr_sync(self.ctx.handle, ctypes.byref(self.raw), _stream(stream)))
+        return self.raw.nnzb
+
+    def to_host(self) -> dict:
+        r = self.raw
+        ptr = np.zeros(r.n_brow + 1, np.int32)
+        check(_L.mf_bsr_download(self.ctx.handle, ctypes.byref(r), ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 None, None, None))
+        n = int(r.nnzb)
+        HG = (r.H_s + 7) // 8
+        idx = np.zeros(max(n, 1), np.int32)
+        bits = np.zeros((max(n, 1), HG, r.B, r.B, 8), np.uint16)
+        rkm = np.zeros((r.H_s, max(r.T, 1)), np.float32)
+        check(_L.mf_bsr_download(self.ctx.handle, ctypes.byref(r),
+                                 ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                                 rkm.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+        return {"block_ptr": ptr, "block_idx": idx[:n], "probs_bits": bits[:n],
+                "probs": probs_store_to_canonical(bits[:n], r.H_s), "row_kept_mass": rkm[:, : r.T],
+                "nnzb": n}
+
+    def upload(self, block_ptr, block_idx, probs, row_kept_mass) -> None:
+        """Fill from host arrays; ``probs`` canonical [nnzb, H_s, B, B] with bf16 values."""
+        r = self.raw
+        ptr = np.ascontiguousarray(block_ptr, dtype=np.int32)
+        idx = np.ascontiguousarray(block_idx, dtype=np.int32)
+        bits = probs_canonical_to_store(np.asarray(probs, dtype=np.float32), r.H_s)
+        rkm = np.ascontiguousarray(row_kept_mass, dtype=np.float32)
+        check(_L.mf_bsr_upload(self.ctx.handle, ctypes.byref(r),
+                               ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)),
+                               rkm.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+
+    def free(self):
+        if self.__dict__.get("raw") is not None and self.raw._owner:
+            _L.mf_bsr_free(self.ctx.handle, ctypes.byref(self.raw))
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+class PreparedV:
+    """An mf_vfrag (receiver V in MFMA operand layout), owned by the library."""
+
+    def __init__(self, ctx: Context, raw: MfVfrag):
+        self.ctx = ctx
+        self.raw = raw
+
+    def free(self):
+        if self.__dict__.get("raw") is not None and self.raw._owner:
+            _L.mf_vfrag_free(self.ctx.handle, ctypes.byref(self.raw))
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------------------------
+# entry points
+# ----------------------------------------------------------------------------------------------
+def map_layers(n_recv: int, n_send: int, R: int) -> list[int]:
+    out = (ctypes.c_int32 * n_recv)()
+    check(_L.mf_map_layers(int(n_recv), int(n_send), int(R), out))
+    return list(out)
+
+
+def check_layer_map(pi, n_recv: int, n_send: int, R: int) -> None:
+    check(_L.mf_check_layer_map(i32_array(pi), int(n_recv), int(n_send), int(R)))
+
+
+def _check_qk(Q, K):
+    if Q.dim() != 3 or K.shape != Q.shape:
+        raise ValueError(f"Q and K must both be [H_s, T, d] (got {tuple(Q.shape)}, {tuple(K.shape)})")
+    if Q.dtype != K.dtype:
+        raise TypeError("Q and K must have the same dtype")
+
+
+def compress(Q: torch.Tensor, K: torch.Tensor, tau: float, B: int, cu_seqlens=None, ctx=None,
+             stream=None) -> BlockStore:
+    """mf_compress: exactly sized block store of one sender layer (Q, K: [H_s, T, d])."""
+    ctx = _ctx(ctx)
+    _check_qk(Q, K)
+    H_s, T, d = Q.shape
+    cu_arr, n_seq, cu = _cu(cu_seqlens, T)
+    raw = MfBsr()
+    check(_L.mf_compress(ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dtype(Q), int(H_s), int(d),
+                         cu_arr, n_seq, float(tau), int(B), _stream(stream), ctypes.byref(raw)))
+    return BlockStore(ctx, raw, cu)
+
+
+def compress_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, tau: float, stream=None) -> None:
+    """mf_compress_into: asynchronous compress into a preallocated store."""
+    _check_qk(Q, K)
+    if Q.shape[0] != store.raw.H_s or Q.shape[1] != store.raw.T:
+        raise ValueError("Q/K shape does not match the store's geometry")
+    check(_L.mf_compress_into(store.ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dtype(Q), int(Q.shape[2]),
+                              float(tau), ctypes.byref(store.raw), _stream(stream)))
+
+
+def _paged(page_table, page_size):
+    if page_table is None:
+        return None, 0, 0
+    return _dev(page_table, "page_table"), int(page_size), int(page_table.shape[1])
+
+
+def v_prepare(V: torch.Tensor, B: int, cu_seqlens=None, page_table=None, page_size: int = 16,
+              ctx=None, stream=None) -> PreparedV:
+    """mf_v_prepare.  V: [T, H_kv, d] contiguous, or a page pool [n_pages, page_size, H_kv, d]."""
+    ctx = _ctx(ctx)
+    H_kv, d = int(V.shape[-2]), int(V.shape[-1])
+    T = int(V.shape[0]) if page_table is None else None
+    cu_arr, n_seq, _ = _cu(cu_seqlens, T if T is not None else 0)
+    pt, ps, pps = _paged(page_table, page_size)
+    raw = MfVfrag()
+    check(_L.mf_v_prepare(ctx.handle, cu_arr, n_seq, int(B), _dev(V, "V"), _dtype(V), H_kv, d, pt, ps,
+                          pps, ctypes.byref(raw), _stream(stream)))
+    return PreparedV(ctx, raw)
+
+
+def _out(out, T, H, d, like):
+    if out is None:
+        return torch.empty((T, H, d), dtype=torch.float32, device=like.device)
+    if out.shape != (T, H, d) or out.dtype != torch.float32:
+        raise ValueError("out must be float32 [T, H, d]")
+    return out
+
+
+def retrieve_prepared(store: BlockStore, W: torch.Tensor, pv: PreparedV, kv_head_map, out=None,
+                      stream=None) -> torch.Tensor:
+    """mf_retrieve_prepared: O [T, H_r, d] fp32 from the store, W [H_r, H_s] fp32 and prepared V."""
+    H_r = int(W.shape[0])
+    if W.dtype != torch.float32 or W.shape[1] != store.raw.H_s:
+        raise ValueError("W must be float32 [H_r, H_s]")
+    out = _out(out, store.raw.T, H_r, pv.raw.d, W)
+    check(_L.mf_retrieve_prepared(store.ctx.handle, ctypes.byref(store.raw), _dev(W, "W"), H_r,
+                                  ctypes.byref(pv.raw), i32_array(kv_head_map), _dev(out, "out"),
+                                  _stream(stream)))
+    return out
+
+
+def retrieve(store: BlockStore, W: torch.Tensor, V: torch.Tensor, kv_head_map, page_table=None,
+             page_size: int = 16, out=None, stream=None) -> torch.Tensor:
+    """mf_retrieve: V preparation into context scratch + the fused retrieve kernel."""
+    H_r = int(W.shape[0])
+    if W.dtype != torch.float32 or W.shape[1] != store.raw.H_s:
+        raise ValueError("W must be float32 [H_r, H_s]")
+    H_kv, d = int(V.shape[-2]), int(V.shape[-1])
+    out = _out(out, store.raw.T, H_r, d, W)
+    pt, ps, pps = _paged(page_table, page_size)
+    check(_L.mf_retrieve(store.ctx.handle, ctypes.byref(store.raw), _dev(W, "W"), H_r, _dev(V, "V"),
+                         _dtype(V), H_kv, d, pt, ps, pps, i32_array(kv_head_map), _dev(out, "out"),
+                         _stream(stream)))
+    return out
+
+
+def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv_head_map, cu_seqlens=None,
+                    out=None, ctx=None, stream=None) -> torch.Tensor:
+    """mf_dense_attention: causal softmax attention, Q [T, H_q, d], K/V [T, H_kv, d] -> fp32 O."""
+    ctx = _ctx(ctx)
+    T, H_q, d = Q.shape
+    H_kv = int(K.shape[1])
+    if K.shape != V.shape or K.shape[0] != T or K.shape[2] != d:
+        raise ValueError("K and V must be [T, H_kv, d] matching Q")
+    cu_arr, n_seq, _ = _cu(cu_seqlens, T)
+    out = _out(out, T, H_q, d, Q)
+    check(_L.mf_dense_attention(ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype(Q), H_q,
+                                H_kv, d, cu_arr, n_seq, i32_array(kv_head_map), _dev(out, "out"),
+                                _stream(stream)))
+    return out
+
+
+def copy_probe(dst: torch.Tensor, src: torch.Tensor, ctx=None, stream=None) -> None:
+    ctx = _ctx(ctx)
+    nbytes = src.numel() * src.element_size()
+    check(_L.mf_copy_probe(ctx.handle, _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))

@@ -1,0 +1,259 @@
+/*
+ * mapflow.h — C ABI of libmapflow, the MI355X (gfx950) hot path of MapFlow's cross-model
+ * attention-map reuse: block-sparse compression of a sender layer's causal softmax map, and the
+ * fused retrieval that turns the kept blocks into a receiver layer's attention output.
+ *
+ * Page keys cited below:
+ *   [MapFlow开源]  "MapFlow开源:大模型换班,Prefill为何能快20%?" (aitest123.com)
+ *   [Reuses Attention] "Peking University's MapFlow Reuses Attention Across Models without
+ *                   Recomputing the KV Cache" (roboind.com)
+ *   [Abstract]     "Accelerating Cross-Model LLM Inference via Attention Map Reuse", abstract
+ *
+ * Conventions for every call:
+ *   - Pointers named *_host are host memory; every other data pointer is device memory on the
+ *     context's device.  The library never frees caller memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it; calls
+ *     return before the GPU finishes unless stated otherwise.
+ *   - Arguments are validated on the host before anything is launched; a failed check returns
+ *     MF_ERR_INVALID (or MF_ERR_UNSUPPORTED for valid shapes this build has no kernel for) and
+ *     leaves all outputs untouched.  No C++ exception crosses this boundary.
+ *   - After a non-OK status, mf_last_error() returns a message for the calling thread.
+ *   - A context holds scratch memory: calls on one context that use the same scratch (two
+ *     compresses, or two retrieves through mf_retrieve) must be ordered on one stream.
+ */
+#ifndef MAPFLOW_H
+#define MAPFLOW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mf_status {
+  MF_OK = 0,
+  MF_ERR_INVALID = 1,     /* bad argument; nothing launched, outputs untouched */
+  MF_ERR_UNSUPPORTED = 2, /* valid request with no compiled kernel (see each call's limits) */
+  MF_ERR_OOM = 3,         /* a device allocation failed; nothing leaked */
+  MF_ERR_HIP = 4,         /* a HIP runtime call or a kernel launch failed */
+  MF_ERR_CAPACITY = 5     /* a preallocated block store was too small for the kept blocks */
+} mf_status;
+
+typedef enum mf_dtype { MF_F32 = 0, MF_BF16 = 1 } mf_dtype;
+
+typedef struct mf_ctx mf_ctx;
+
+/*
+ * Block-sparse (BSR) store of one sender layer's compressed attention map.
+ * [MapFlow开源, section 只存重要的:块稀疏压缩]: the map is cut into regular B x B blocks and only
+ * the high-mass blocks are stored; the number kept varies per layer and per position.
+ *
+ * Block rows are numbered over the packed batch: sequence s owns block rows
+ * [brow_base(s), brow_base(s) + ceil(n_s / B)); block columns are local to the sequence
+ * (column 0 is the sequence's first B tokens).  All arrays are device memory owned by the
+ * library (free with mf_bsr_free).
+ *
+ *   brow_info   int32 [n_brow][4]   {first token of the block row, first token of its sequence,
+ *                                     sequence length, block row index within the sequence}
+ *   brow_order  int32 [n_brow]       block rows by descending in-sequence index (work order)
+ *   block_ptr   int32 [n_brow + 1]   CSR row pointer over kept blocks
+ *   block_idx   int32 [capacity]     kept block columns, ascending within each block row
+ *   block_row   int32 [capacity]     block row of each kept block
+ *   probs       bf16  [capacity][ceil(H_s/8)][B][B][8]  kept probabilities; element
+ *               [n][h/8][r][c][h%8] is the softmax probability of query row r and key column c
+ *               of block n for sender head h, rounded to bf16 (nearest even).  Zero for r or c
+ *               past the sequence end, above the causal diagonal, and for padding heads >= H_s.
+ *   row_kept_mass fp32 [H_s][T]      per head and token, the sum of that row's stored probs
+ *   counters    int32 [2]            {nnzb, overflow flag} written by the device
+ */
+typedef struct mf_bsr {
+  int32_t B;          /* block size (16, 32, 64 or 128)                        */
+  int32_t H_s;        /* sender heads                                          */
+  int32_t n_seq;      /* sequences in the packed batch                        */
+  int32_t n_brow;     /* block rows over all sequences                        */
+  int32_t nb_max;     /* largest per-sequence block count                     */
+  int32_t _pad;
+  int64_t T;          /* tokens in the packed batch                           */
+  int64_t n_causal;   /* causal (lower-triangular) blocks over all sequences  */
+  int64_t capacity;   /* blocks allocated in block_idx / block_row / probs    */
+  int64_t nnzb;       /* kept blocks; valid after mf_compress or mf_bsr_sync  */
+  int32_t* brow_info;
+  int32_t* brow_order;
+  int32_t* block_ptr;
+  int32_t* block_idx;
+  int32_t* block_row;
+  uint16_t* probs;
+  float* row_kept_mass;
+  int32_t* counters;
+  void* _owner;       /* library bookkeeping; do not touch                    */
+} mf_bsr;
+
+/*
+ * Receiver V prepared for the MFMA kernels: fp16, scaled per KV head by 2^exps[k] so the largest
+ * |V| of each head sits near 2^15, and laid out so that each 32-key x 16-column operand tile is one
+ * contiguous 1 KiB read.  Keys are grouped by B-token block rows exactly as an mf_bsr with the
+ * same cu_seqlens and B; rows past a sequence end are zero.
+ */
+typedef struct mf_vfrag {
+  int32_t B, d, H_kv, n_brow;
+  int64_t T;
+  uint16_t* frag;     /* fp16 [H_kv][n_brow][B/32][d/16][64 lanes][8]            */
+  int32_t* exps;      /* int32 [H_kv] power-of-two scale exponents                */
+  void* _owner;
+} mf_vfrag;
+
+/* Library version string (static storage). */
+const char* mf_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* mf_last_error(void);
+
+/* Create a context on HIP device `device`; the context keeps per-device scratch memory. */
+mf_status mf_create(int device, mf_ctx** out);
+
+/* Destroy a context and free its scratch memory (after synchronising the device). */
+mf_status mf_destroy(mf_ctx* ctx);
+
+/*
+ * Layer map (host only, needs no GPU).  [MapFlow开源, section 不传 KV Cache,改传'注意力关系']:
+ * a sender layer's map is assigned to a suitable receiver layer; [Reuses Attention] and
+ * [Abstract]: the receiver computes its first layers itself (partial recomputation).
+ * Writes pi_out[l] for l in [0, n_recv): -1 for l < R (recomputed densely), otherwise
+ * round(l * (n_send - 1) / (n_recv - 1)) with halves rounded up, computed in integers.
+ * Requires n_recv >= 1, n_send >= 1, 0 <= R <= n_recv.
+ */
+mf_status mf_map_layers(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out_host);
+
+/*
+ * Check a caller-supplied layer map: pi[l] == -1 exactly for l < R and 0 <= pi[l] < n_send
+ * otherwise.  Host only.
+ */
+mf_status mf_check_layer_map(const int32_t* pi_host, int32_t n_recv, int32_t n_send, int32_t R);
+
+/*
+ * Allocate an empty block store for a packed batch: geometry from cu_seqlens_host (int32
+ * [n_seq + 1], non-decreasing, starting at 0) and block size B.  capacity_blocks < 0 allocates
+ * room for every causal block, so any tau fits.  H_s in [1, 64].
+ */
+mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu_seqlens_host,
+                        int32_t n_seq, int64_t capacity_blocks, mf_bsr* out);
+
+/*
+ * Copy a store to host memory (synchronous; waits for the device).  Any destination may be NULL
+ * to skip it.  block_ptr_host: int32 [n_brow + 1]; block_idx_host: int32 [nnzb]; probs_host:
+ * bf16 bits in the store layout, [nnzb][ceil(H_s/8)][B][B][8]; row_kept_mass_host: fp32 [H_s][T].
+ * nnzb is read from the device first (bsr->nnzb is updated).
+ */
+mf_status mf_bsr_download(mf_ctx* ctx, mf_bsr* bsr, int32_t* block_ptr_host,
+                          int32_t* block_idx_host, uint16_t* probs_host,
+                          float* row_kept_mass_host);
+
+/*
+ * Fill a store from host memory (synchronous), e.g. to restore a store saved with
+ * mf_bsr_download from a host-memory tier.  Same layouts as mf_bsr_download.  block_ptr_host
+ * must start at 0, be non-decreasing and end at nnzb <= capacity; each block row's columns must
+ * be ascending and within [0, I] of that row.  Checked on the host; MF_ERR_INVALID otherwise.
+ */
+mf_status mf_bsr_upload(mf_ctx* ctx, mf_bsr* bsr, const int32_t* block_ptr_host,
+                        const int32_t* block_idx_host, const uint16_t* probs_host,
+                        const float* row_kept_mass_host);
+
+/* Free the device arrays of a store created by this library; zeroes *bsr. */
+mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr);
+
+/*
+ * Compress one sender layer into an existing store (no allocation on the store, no host sync).
+ * [MapFlow开源, section 只存重要的:块稀疏压缩] and [Reuses Attention, first component]: block
+ * statistics first, then the kept blocks; the dense L x L map is never formed.
+ *
+ *   Q, K   sender queries and keys, [H_s][T][d] (head-major, post-RoPE), dtype MF_BF16 or MF_F32
+ *   d      64 or 128
+ *   tau    in (0, 1]: per block row, keep the sink block (column 0) and the diagonal block, then
+ *          blocks by descending mass (ties: lower column) until the kept mass reaches
+ *          tau * H_s * rows; tau = 1 keeps every causal block
+ * Scores are q.k / sqrt(d).  If the kept blocks exceed bsr->capacity, the store's overflow flag
+ * is set and the extra blocks are dropped; mf_bsr_sync reports it as MF_ERR_CAPACITY.
+ * Scratch memory of the context may grow (a device allocation) on the first call of a size.
+ */
+mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype, int32_t d,
+                           float tau, mf_bsr* bsr, void* stream);
+
+/* Wait for `stream`, read the kept-block count into bsr->nnzb; MF_ERR_CAPACITY on overflow. */
+mf_status mf_bsr_sync(mf_ctx* ctx, mf_bsr* bsr, void* stream);
+
+/*
+ * Compress with an exactly sized store: the selection runs first, the stream is synchronised
+ * once to read the kept-block count, then block_idx / probs are allocated for exactly nnzb
+ * blocks and filled.  *out must be freed with mf_bsr_free.  Same arguments as mf_compress_into
+ * plus the geometry of mf_bsr_create.
+ */
+mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype, int32_t H_s,
+                      int32_t d, const int32_t* cu_seqlens_host, int32_t n_seq, float tau,
+                      int32_t B, void* stream, mf_bsr* out);
+
+/*
+ * Prepare the receiver's V for retrieval (and for mf_dense_attention).
+ *   V            contiguous [T][H_kv][d] when page_table is NULL; otherwise a page pool
+ *                [n_pages][page_size][H_kv][d] with page_table int32 [n_seq][pages_per_seq]
+ *                (device) mapping each sequence's logical pages to pool pages
+ *   dtype        MF_BF16 or MF_F32
+ * If out->frag is NULL the library allocates frag and exps (free with mf_vfrag_free); otherwise
+ * the caller provides frag with room for H_kv * n_brow * B * d fp16 values and exps for H_kv.
+ * Values scaled past the fp16 range are not possible: each head is scaled by 2^e with
+ * max|V| * 2^e <= 2^15.  Non-finite V propagates as in IEEE arithmetic.
+ */
+mf_status mf_v_prepare(mf_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_seq, int32_t B,
+                       const void* V, mf_dtype dtype, int32_t H_kv, int32_t d,
+                       const int32_t* page_table, int32_t page_size, int32_t pages_per_seq,
+                       mf_vfrag* out, void* stream);
+
+mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf);
+
+/*
+ * Fused retrieve on a prepared V.  [MapFlow开源, section 算得省的:融合内核执行] and
+ * [Reuses Attention, third component]: read the kept blocks, combine sender heads into receiver
+ * heads on chip, multiply by the receiver's own V, accumulate, write the output — no dense map
+ * and no mixed map in device memory.  For receiver head g and token i:
+ *     Ahat[g,i,j] = sum_h W[g,h] P[h,i,j] over kept keys j,
+ *     O[i,g,:]    = sum_j Ahat[g,i,j] V[j, kv(g), :] / sum_j Ahat[g,i,j].
+ *   W                 fp32 [H_r][H_s] device, any real values (not validated; a zero row sum
+ *                     gives IEEE inf/nan like the definition)
+ *   kv_head_map_host  int32 [H_r], each in [0, H_kv)
+ *   O                 fp32 [T][H_r][d] device; must not alias any input
+ * Limits: H_r <= 32, H_s <= 64, d in {64, 128}, B in {32, 64}, vf geometry equal to the store's.
+ * Rows of the mixed map are rounded to fp16 (scaled by a power of two per receiver head) before
+ * the V product; sums are fp32.
+ */
+mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,
+                               const mf_vfrag* vf, const int32_t* kv_head_map_host, float* O,
+                               void* stream);
+
+/* mf_v_prepare into context scratch followed by mf_retrieve_prepared. */
+mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r, const void* V,
+                      mf_dtype vdtype, int32_t H_kv, int32_t d, const int32_t* page_table,
+                      int32_t page_size, int32_t pages_per_seq, const int32_t* kv_head_map_host,
+                      float* O, void* stream);
+
+/*
+ * Dense causal attention for the receiver layers that are recomputed ([Reuses Attention]:
+ * the receiver computes its first layers normally).  O[i,g,:] = softmax_j<=i(q.k / sqrt(d)) V
+ * per sequence, query head g reading KV head kv_head_map_host[g].
+ *   Q [T][H_q][d], K, V [T][H_kv][d] (MF_BF16 or MF_F32), O fp32 [T][H_q][d]; d in {64, 128}.
+ */
+mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K, const void* V,
+                             mf_dtype dtype, int32_t H_q, int32_t H_kv, int32_t d,
+                             const int32_t* cu_seqlens_host, int32_t n_seq,
+                             const int32_t* kv_head_map_host, float* O, void* stream);
+
+/*
+ * HBM probe: copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from src to dst with
+ * a plain streaming kernel.  Used to calibrate bandwidth counters against a known byte count.
+ */
+mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAPFLOW_H */
