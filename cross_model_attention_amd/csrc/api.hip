@@ -655,9 +655,16 @@ MF_EXPORT mf_status mf_v_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, 
                                  int32_t pages_per_seq, mf_vfrag* out, void* stream) {
   mf_status st = set_device(ctx);
   if (st != MF_OK) return st;
-  if (out && out->_owner) return fail(MF_ERR_INVALID, "vfrag already prepared; free it first");
+  if (out && out->_owner) {
+    // re-preparation into the same buffers: the geometry must be unchanged
+    const VfragOwner* own = static_cast<const VfragOwner*>(out->_owner);
+    Geometry g;
+    if ((st = build_geometry(cu, n_seq, B, g)) != MF_OK) return st;
+    if (!(own->geom.cu == g.cu && own->geom.B == B && out->H_kv == H_kv && out->d == d))
+      return fail(MF_ERR_INVALID, "prepared V exists with a different geometry; free it first");
+  }
   return vfrag_prepare(ctx, cu, n_seq, B, V, dtype, H_kv, d, page_table, page_size, pages_per_seq,
-                       out, false, static_cast<hipStream_t>(stream));
+                       out, out && out->_owner, static_cast<hipStream_t>(stream));
 }
 
 MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {

@@ -241,17 +241,21 @@ def _paged(page_table, page_size):
 
 
 def v_prepare(V: torch.Tensor, B: int, cu_seqlens=None, page_table=None, page_size: int = 16,
-              ctx=None, stream=None) -> PreparedV:
-    """mf_v_prepare.  V: [T, H_kv, d] contiguous, or a page pool [n_pages, page_size, H_kv, d]."""
-    ctx = _ctx(ctx)
+              out: PreparedV | None = None, ctx=None, stream=None) -> PreparedV:
+    """mf_v_prepare.  V: [T, H_kv, d] contiguous, or a page pool [n_pages, page_size, H_kv, d].
+    With ``out`` (same geometry) the preparation is redone in place without allocating."""
+    ctx = out.ctx if out is not None else _ctx(ctx)
     H_kv, d = int(V.shape[-2]), int(V.shape[-1])
-    T = int(V.shape[0]) if page_table is None else None
-    cu_arr, n_seq, _ = _cu(cu_seqlens, T if T is not None else 0)
+    if page_table is None and cu_seqlens is None:
+        cu_seqlens = [0, int(V.shape[0])]
+    if cu_seqlens is None:
+        raise ValueError("paged V needs cu_seqlens")
+    cu_arr, n_seq, _ = _cu(cu_seqlens, 0)
     pt, ps, pps = _paged(page_table, page_size)
-    raw = MfVfrag()
+    raw = out.raw if out is not None else MfVfrag()
     check(_L.mf_v_prepare(ctx.handle, cu_arr, n_seq, int(B), _dev(V, "V"), _dtype(V), H_kv, d, pt, ps,
                           pps, ctypes.byref(raw), _stream(stream)))
-    return PreparedV(ctx, raw)
+    return out if out is not None else PreparedV(ctx, raw)
 
 
 def _out(out, T, H, d, like):

@@ -199,7 +199,8 @@ mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
  *                (device) mapping each sequence's logical pages to pool pages
  *   dtype        MF_BF16 or MF_F32
  * If out->frag is NULL the library allocates frag and exps (free with mf_vfrag_free); otherwise
- * the caller provides frag with room for H_kv * n_brow * B * d fp16 values and exps for H_kv.
+ * the caller provides frag with room for H_kv * n_brow * B * d fp16 values.  Calling again with an
+ * already prepared *out of the same geometry re-prepares in place without allocating.
  * Values scaled past the fp16 range are not possible: each head is scaled by 2^e with
  * max|V| * 2^e <= 2^15.  Non-finite V propagates as in IEEE arithmetic.
  */

@@ -12,7 +12,9 @@ from .workloads import (  # noqa: F401
     bf16_bits_to_f32,
     cu_seqlens_of,
     make_dense_inputs,
+    make_dense_inputs_torch,
     make_layer_inputs,
+    make_layer_inputs_torch,
     make_page_table,
     make_lengths,
     page_v,

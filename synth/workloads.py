@@ -221,3 +221,67 @@ def page_v(v: np.ndarray, lengths, table: np.ndarray, page_size: int, n_pages: i
             pool[table[s, p], : t1 - t0] = v[tok + t0: tok + t1]
         tok += n
     return pool
+
+
+# ----------------------------------------------------------------------------------------------
+# Device-side bulk generation (same recipe, torch's generator instead of numpy's).  Used for
+# multi-gigabyte benchmark inputs; the numbers differ from the numpy path, the distributions and
+# structure do not.
+# ----------------------------------------------------------------------------------------------
+def _torch_gen(seed: int, layer: int, tensor: str, device):
+    import torch
+    state = np.random.SeedSequence([int(seed), int(layer), _TENSOR_IDS[tensor]]).generate_state(2)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(state[0]) << 32 | int(state[1]))
+    return g
+
+
+def make_layer_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
+    """Q_s, K_s [H_s, T, d], V_r [T, H_kv, d] (input dtype) and W [H_r, H_s] fp32 on ``device``."""
+    import torch
+    lengths = make_lengths(wl, seed, lengths)
+    cu = cu_seqlens_of(lengths)
+    T, H_s, d = int(cu[-1]), wl.H_s, wl.d
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    a = 0.75 * math.sqrt(d)
+    u = torch.randn((H_s, d), generator=_torch_gen(seed, layer, "u", device), device=device)
+    u = u / u.norm(dim=1, keepdim=True)
+    boost = (a * u)[:, None, :]
+    q = torch.randn((H_s, T, d), generator=_torch_gen(seed, layer, "q_s", device), device=device)
+    q += boost
+    q_out = q.to(dt)
+    del q
+    k = torch.randn((H_s, T, d), generator=_torch_gen(seed, layer, "k_s", device), device=device)
+    g_hot = _torch_gen(seed, layer, "hot", device)
+    hot = []
+    for s, n in enumerate(lengths):
+        n_hot = min(int(round(wl.hot_frac * n)), max(n - 1, 0))
+        pos = torch.randperm(max(n - 1, 0), generator=g_hot, device=device)[:n_hot] + 1
+        hot.append(torch.cat([torch.zeros(1, dtype=pos.dtype, device=device), pos]) + int(cu[s]))
+    hot = torch.cat(hot)
+    k[:, hot, :] += boost
+    k_out = k.to(dt)
+    del k
+    v = torch.randn((T, wl.H_kv, d), generator=_torch_gen(seed, layer, "v_r", device), device=device).to(dt)
+    w = torch.from_numpy(rng_for(seed, layer, "w").dirichlet(np.full(H_s, 0.5), size=wl.H_r)
+                         .astype(np.float32)).to(device)
+    group = max(wl.H_r // wl.H_kv, 1)
+    return {"q_s": q_out, "k_s": k_out, "v_r": v, "w": w, "cu_seqlens": cu, "lengths": lengths,
+            "kv_head_map": [min(g // group, wl.H_kv - 1) for g in range(wl.H_r)], "T": T}
+
+
+def make_dense_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
+    """Plain N(0,1) Q [T, H_r, d], K and V [T, H_kv, d] for a recomputed receiver layer."""
+    import torch
+    lengths = make_lengths(wl, seed, lengths)
+    cu = cu_seqlens_of(lengths)
+    T = int(cu[-1])
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    out = {}
+    for name, H in [("q", wl.H_r), ("k", wl.H_kv), ("v", wl.H_kv)]:
+        out[name] = torch.randn((T, H, wl.d), generator=_torch_gen(seed, layer, name + "_dense", device),
+                                device=device).to(dt)
+    group = max(wl.H_r // wl.H_kv, 1)
+    out.update(cu_seqlens=cu, lengths=lengths, T=T,
+               kv_head_map=[min(g // group, wl.H_kv - 1) for g in range(wl.H_r)])
+    return out
