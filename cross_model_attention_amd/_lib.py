@@ -20,7 +20,8 @@ class MfBsr(ctypes.Structure):
         ("B", c_int32), ("H_s", c_int32), ("n_seq", c_int32), ("n_brow", c_int32),
         ("nb_max", c_int32), ("_pad", c_int32), ("T", c_int64), ("n_causal", c_int64),
         ("capacity", c_int64), ("nnzb", c_int64),
-        ("brow_info", c_void_p), ("brow_order", c_void_p), ("block_ptr", c_void_p),
+        ("brow_info", c_void_p), ("brow_order", c_void_p), ("brow_coff", c_void_p),
+        ("block_ptr", c_void_p),
         ("block_idx", c_void_p), ("block_row", c_void_p), ("probs", c_void_p),
         ("row_kept_mass", c_void_p), ("counters", c_void_p), ("_owner", c_void_p),
     ]

@@ -47,6 +47,7 @@ struct Geometry {
   std::vector<int32_t> info;      // [n_brow][4]
   std::vector<int32_t> order;     // block rows by descending in-sequence index
   std::vector<int32_t> brow_seq;  // [n_brow]
+  std::vector<int32_t> coff;      // [n_brow] causal blocks of all earlier block rows
   std::vector<int32_t> cu;        // copy of cu_seqlens
 };
 
@@ -70,6 +71,8 @@ mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& 
     for (int I = 0; I < nb; ++I) {
       g.info.insert(g.info.end(), {cu[s] + I * B, cu[s], n, I});
       g.brow_seq.push_back(s);
+      g.coff.push_back((int32_t)std::min<int64_t>(g.n_causal - (int64_t)nb * (nb + 1) / 2 + (int64_t)I * (I + 1) / 2,
+                                                  INT32_MAX));
     }
   }
   g.T = cu[n_seq];
@@ -131,7 +134,7 @@ struct VfragOwner {
 
 struct mf_ctx {
   int device = 0;
-  Scratch lse2, Mh, M, flags, counts, part;
+  Scratch lse2, Mh, M, flags, counts, part, zbuf;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
   // cached device copies of the dense-attention geometry
@@ -159,7 +162,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   const size_t n_info = (size_t)g.n_brow * 4 * 4;
   const size_t o_info = 0;
   const size_t o_order = align_up(o_info + n_info, 256);
-  const size_t o_ptr = align_up(o_order + (size_t)g.n_brow * 4, 256);
+  const size_t o_coff = align_up(o_order + (size_t)g.n_brow * 4, 256);
+  const size_t o_ptr = align_up(o_coff + (size_t)g.n_brow * 4, 256);
   const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
   const size_t o_cnt = align_up(o_rkm + (size_t)H_s * g.T * 4, 256);
   const size_t total = o_cnt + 256;
@@ -171,6 +175,7 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   char* base = static_cast<char*>(own->meta);
   out->brow_info = reinterpret_cast<int32_t*>(base + o_info);
   out->brow_order = reinterpret_cast<int32_t*>(base + o_order);
+  out->brow_coff = reinterpret_cast<int32_t*>(base + o_coff);
   out->block_ptr = reinterpret_cast<int32_t*>(base + o_ptr);
   out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
   out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
@@ -179,6 +184,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
     if (e == hipSuccess)
       e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipMemset(out->block_ptr, 0, (size_t)(g.n_brow + 1) * 4);
   if (e == hipSuccess) e = hipMemset(out->counters, 0, 256);
@@ -222,8 +229,8 @@ mf_status validate_compress(const void* Q, const void* K, mf_dtype dtype, int32_
   if (!(tau > 0.f && tau <= 1.f)) return fail(MF_ERR_INVALID, "tau must be in (0, 1] (got %g)", (double)tau);
   if (!mf::compress_supported(dtype_code(dtype), bsr->B, d))
     return fail(MF_ERR_UNSUPPORTED, "no compress kernel for B=%d d=%d", bsr->B, d);
-  if (mf::stats_lds_bytes(bsr->B, bsr->nb_max) > 64 * 1024)
-    return fail(MF_ERR_UNSUPPORTED, "sequence too long for the statistics kernel (%d blocks)", bsr->nb_max);
+  if (bsr->nb_max > 4096)
+    return fail(MF_ERR_UNSUPPORTED, "sequence too long for the selection kernel (%d blocks > 4096)", bsr->nb_max);
   return MF_OK;
 }
 
@@ -233,6 +240,7 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   const size_t nbn = (size_t)bsr->n_brow * bsr->nb_max;
   mf_status st;
   if ((st = ensure(ctx->lse2, (size_t)bsr->H_s * bsr->T * 4 + 256, "lse")) != MF_OK) return st;
+  if ((st = ensure(ctx->zbuf, (size_t)bsr->H_s * bsr->n_causal * bsr->B * 8 + 256, "block statistics")) != MF_OK) return st;
   if ((st = ensure(ctx->Mh, (size_t)bsr->H_s * nbn * 4 + 256, "block mass")) != MF_OK) return st;
   if ((st = ensure(ctx->M, nbn * 8 + 256, "head-summed mass")) != MF_OK) return st;
   if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
@@ -250,9 +258,12 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.nb_max = bsr->nb_max;
   a.info = bsr->brow_info;
   a.order = bsr->brow_order;
+  a.coff = bsr->brow_coff;
+  a.n_causal = bsr->n_causal;
   a.tau = (double)tau;
   a.scale2 = (float)(1.4426950408889634 / std::sqrt((double)d));
   a.lse2 = static_cast<float*>(ctx->lse2.p);
+  a.zbuf = static_cast<float2*>(ctx->zbuf.p);
   a.Mh = static_cast<float*>(ctx->Mh.p);
   a.M = static_cast<double*>(ctx->M.p);
   a.flags = static_cast<uint8_t*>(ctx->flags.p);
@@ -421,7 +432,8 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
   if (!ctx) return MF_OK;
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
-  for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->dense_tables})
+  for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf,
+                     &ctx->dense_tables})
     if (s->p) (void)hipFree(s->p);
   vfrag_release(&ctx->vf_retrieve);
   vfrag_release(&ctx->vf_dense);

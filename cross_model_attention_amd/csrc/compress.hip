@@ -63,120 +63,149 @@ __device__ __forceinline__ v4f dot_tile(const Frag<float, D>& A, const Frag<floa
 
 constexpr float kNegInf = -__builtin_inff();
 
+template <int D>
+__device__ __forceinline__ void load_lds_frag(Frag<uint16_t, D>& f, const unsigned char* row, int a) {
+#pragma unroll
+  for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
+    f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(row + (32 * k + 8 * a) * 2));
+}
+template <int D>
+__device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned char* row, int a) {
+#pragma unroll
+  for (int k = 0; k < Frag<float, D>::N; ++k) f.v[k] = *reinterpret_cast<const float*>(row + (4 * k + a) * 4);
+}
+
+
 // ------------------------------------------------------------------------------------------
-// k_stats: row logsumexp (pass 1) and per-head block masses (pass 2) for one block row.
-// Workgroup = B/16 waves; wave w owns keys 16w..16w+15 of every key block, all B queries.
-// Scores are held transposed (keys x queries) so each lane accumulates statistics for its own
-// query column without cross-lane traffic until the end of a pass.
+// k_stats: one workgroup per (block row, sender head), B/16 waves; wave w owns queries
+// 16w..16w+15 and all B keys of each key block.  One pass over the key blocks: each block's key
+// tile is staged in LDS (double buffered, next tile fetched while the current one is used),
+// scores are formed transposed (keys x queries) on MFMA, and for every (query i, key block J)
+// the block-local maximum r_iJ and z_iJ = sum_{j in J} 2^(s_ij c - r_iJ) are stored (c folds
+// log2(e) / sqrt(d)).  A finalisation then gives, exactly as a softmax over the row would,
+//     lse2_i   = log2 sum_J z_iJ 2^(r_iJ)                       (row logsumexp, base 2)
+//     M_h[I,J] = sum_{i in I} z_iJ 2^(r_iJ - lse2_i)            (block mass of head h)
+// with fp64 accumulation in fixed order: one exponential per score instead of two, and one
+// score pass instead of two.
 // ------------------------------------------------------------------------------------------
 template <typename T, int B, int D>
 __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
                                                  int H_s, int64_t T_tot,
                                                  const int32_t* __restrict__ info,
-                                                 const int32_t* __restrict__ order, int n_brow,
-                                                 int nb_max, float scale2, float* __restrict__ lse2,
+                                                 const int32_t* __restrict__ order,
+                                                 const int32_t* __restrict__ coff, int64_t n_causal,
+                                                 int n_brow, int nb_max, float scale2,
+                                                 float2* __restrict__ zbuf,
+                                                 float* __restrict__ lse2,
                                                  float* __restrict__ Mh) {
   constexpr int NW = B / 16;
-  constexpr int NT = B / 16;
-  extern __shared__ float part[];  // [NW][nb_max]
-  __shared__ float red_m[NW * 4][B];
-  __shared__ float red_l[NW * 4][B];
+  constexpr int MT = B / 16;                               // 16-key tiles per block
+  constexpr int NTHR = B * 4;
+  constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
+  constexpr int CPR = D * (int)sizeof(T) / 16;
+  constexpr int CPT = B * CPR / NTHR;
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
   __shared__ float s_lse[B];
 
-  const int h = blockIdx.x % H_s;
-  const int brow = order[blockIdx.x / H_s];
+  // head-major grid: the key rows of the few heads in flight stay cache resident
+  const int h = blockIdx.x / n_brow;
+  const int brow = order[blockIdx.x % n_brow];
   const BrowInfo bi = load_info(info, brow);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int rows = min(B, bi.n - bi.I * B);
-  const int qbase = bi.I * B;
-  const T* Qh = Q + (size_t)h * T_tot * D;
-  const T* Kh = K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D;
+  const bool partial = rows < B;
+  const int qrow = 16 * w + c;                             // this lane's query (column)
+  const int qloc = bi.I * B + qrow;
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D);
+  float2* zrow = zbuf + ((size_t)h * n_causal + coff[brow]) * B;
 
-  Frag<T, D> qf[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int q = 16 * nt + c;
-    qf[nt].load(Qh + (size_t)(bi.tok0 + q) * D, q < rows, a);
-  }
+  Frag<T, D> qf;
+  qf.load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qrow) * D, qrow < rows, a);
 
-  // ---- pass 1: online max / sum per query column -----------------------------------------
-  float m[NT], l[NT];
+  v4u kst[CPT];
+  auto fetch_k = [&](int J) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) { m[nt] = kNegInf; l[nt] = 0.f; }
-  for (int J = 0; J <= bi.I; ++J) {
-    const int key = J * B + 16 * w + c;
-    Frag<T, D> kf;
-    kf.load(Kh + (size_t)key * D, key < bi.n, a);
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const v4f s = dot_tile<D>(kf, qf[nt], zero4());
-      const int q = qbase + 16 * nt + c;
-      float x[4];
-      float tmax = kNegInf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k2 = J * B + 16 * w + 4 * a + i;
-        x[i] = (k2 <= q && q < bi.n) ? s[i] * scale2 : kNegInf;
-        tmax = fmaxf(tmax, x[i]);
-      }
-      if (tmax > kNegInf) {
-        const float mn = fmaxf(m[nt], tmax);
-        float acc = l[nt] * fast_exp2(m[nt] - mn);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc += fast_exp2(x[i] - mn);
-        m[nt] = mn;
-        l[nt] = acc;
-      }
+    for (int u = 0; u < CPT; ++u) {
+      const int piece = threadIdx.x + u * NTHR;
+      const int row = piece / CPR, col = piece % CPR;
+      const int key = J * B + row;
+      kst[u] = key < bi.n ? ld16(Kh + (size_t)key * D * sizeof(T) + col * 16) : zero_u4();
     }
-  }
+  };
+  auto stage_k = [&](int buf) {
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    red_m[w * 4 + a][16 * nt + c] = m[nt];
-    red_l[w * 4 + a][16 * nt + c] = l[nt];
-  }
+    for (int u = 0; u < CPT; ++u) {
+      const int piece = threadIdx.x + u * NTHR;
+      *reinterpret_cast<v4u*>(&s_k[buf][(piece / CPR) * ROWB + (piece % CPR) * 16]) = kst[u];
+    }
+  };
+
+  fetch_k(0);
+  stage_k(0);
   __syncthreads();
+  for (int J = 0; J <= bi.I; ++J) {
+    if (J < bi.I) fetch_k(J + 1);
+    const unsigned char* kt = s_k[J & 1];
+    v4f s[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      Frag<T, D> kf;
+      load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
+      s[mt] = dot_tile<D>(kf, qf, zero4());
+    }
+    const bool masked = J == bi.I || partial;
+    if (masked) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = J * B + 16 * mt + 4 * a + i;
+          if (!(key <= qloc && qloc < bi.n)) s[mt][i] = kNegInf;
+        }
+    }
+    float bm = kNegInf;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      bm = fmaxf(bm, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+    const float r = bm == kNegInf ? 0.f : bm * scale2;     // nothing visible: z = 0
+    float z = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z += fast_exp2(fmaf(s[mt][i], scale2, -r));
+    z += __shfl_xor(z, 16, 64);
+    z += __shfl_xor(z, 32, 64);
+    if (a == 0) zrow[(size_t)J * B + qrow] = make_float2(z, bm == kNegInf ? kNegInf : r);
+    if (J < bi.I) stage_k((J + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- finalisation: row logsumexp, then block masses -------------------------------------
   if (threadIdx.x < B) {
     const int q = threadIdx.x;
     float M = kNegInf;
-    for (int r = 0; r < NW * 4; ++r) M = fmaxf(M, red_m[r][q]);
-    float L = 0.f;
-    for (int r = 0; r < NW * 4; ++r)
-      if (red_m[r][q] > kNegInf) L += red_l[r][q] * fast_exp2(red_m[r][q] - M);
-    const float v = M + log2f(L);
+    for (int J = 0; J <= bi.I; ++J) M = fmaxf(M, zrow[(size_t)J * B + q].y);
+    double L = 0.0;
+    for (int J = 0; J <= bi.I; ++J) {
+      const float2 e = zrow[(size_t)J * B + q];
+      if (e.y > kNegInf) L += (double)e.x * (double)fast_exp2(e.y - M);
+    }
+    const float v = (float)((double)M + log2(L));
     s_lse[q] = v;
     if (q < rows) lse2[(size_t)h * T_tot + bi.tok0 + q] = v;
   }
   __syncthreads();
-
-  // ---- pass 2: block masses ---------------------------------------------------------------
-  float lq[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) lq[nt] = s_lse[16 * nt + c];
-  for (int J = 0; J <= bi.I; ++J) {
-    const int key = J * B + 16 * w + c;
-    Frag<T, D> kf;
-    kf.load(Kh + (size_t)key * D, key < bi.n, a);
-    float sum = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const v4f s = dot_tile<D>(kf, qf[nt], zero4());
-      const int q = qbase + 16 * nt + c;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k2 = J * B + 16 * w + 4 * a + i;
-        if (k2 <= q && q < bi.n) sum += fast_exp2(s[i] * scale2 - lq[nt]);
-      }
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) part[w * nb_max + J] = sum;
-  }
-  __syncthreads();
   float* out = Mh + ((size_t)h * n_brow + brow) * nb_max;
   for (int J = threadIdx.x; J <= bi.I; J += blockDim.x) {
-    float t = 0.f;
-#pragma unroll
-    for (int r = 0; r < NW; ++r) t += part[r * nb_max + J];
-    out[J] = t;
+    const float2* zr = zrow + (size_t)J * B;
+    double t = 0.0;
+    for (int q = 0; q < rows; ++q) {
+      const float2 e = zr[q];
+      if (e.y > kNegInf) t += (double)e.x * (double)fast_exp2(e.y - s_lse[q]);
+    }
+    out[J] = (float)t;
   }
 }
 
@@ -336,10 +365,15 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 }
 
 // ------------------------------------------------------------------------------------------
-// k_gather: one workgroup per (kept block, group of 8 sender heads).  Wave w owns query rows
-// 16w..16w+15; for each head the score tile is recomputed (queries x keys), exponentiated with
-// the stored row logsumexp, rounded to bf16 and written as 16-byte records of 8 heads per
-// (row, column), so each 16-lane group stores 256 contiguous bytes.
+// k_gather: one workgroup per (kept block, group of 8 sender heads); the grid runs head group by
+// head group, so the Q / K rows in flight (one head group of the layer) stay cache resident.
+// Wave w owns query rows 16w..16w+15.  Heads are processed in turn: the key tile of head h + 1
+// is fetched into registers and staged into the other half of a double-buffered LDS tile while
+// head h's scores (queries x keys) are formed from LDS; the query rows of head h + 1 are
+// prefetched into registers.  Each probability exp(s - lse) is rounded to bf16 right away and
+// packed into the 16-byte record of its (row, column), which holds 8 heads; after the last head
+// every 16-lane group stores 256 contiguous bytes.  Per-block row sums of the stored values are
+// reduced across the 16 lanes of a column group with DPP.
 // ------------------------------------------------------------------------------------------
 template <typename T, int B, int D>
 __global__ __launch_bounds__(B * 4) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
@@ -352,90 +386,117 @@ __global__ __launch_bounds__(B * 4) void k_gather(const T* __restrict__ Q, const
                                                   float scale2, uint16_t* __restrict__ probs,
                                                   float* __restrict__ part) {
   constexpr int NT = B / 16;
+  constexpr int NTHR = B * 4;
+  constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
+  constexpr int CHUNKS = B * D * (int)sizeof(T) / 16;      // 16-byte pieces of one key tile
+  constexpr int CPT = CHUNKS / NTHR;                       // pieces per thread
+  constexpr int CPR = D * (int)sizeof(T) / 16;             // pieces per key row
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
+
   const int HG = (H_s + 7) >> 3;
-  const int64_t nblk = blockIdx.x / HG;
-  const int hg = blockIdx.x - (int)(nblk * HG);
+  const int hg = (int)(blockIdx.x / capacity);
+  const int64_t nblk = blockIdx.x - (int64_t)hg * capacity;
   const int64_t nnzb = min((int64_t)counters[0], capacity);
-  if (nblk >= nnzb) return;
+  if (nblk >= nnzb || hg >= HG) return;
   const int brow = block_row[nblk];
   const int J = block_idx[nblk];
   const BrowInfo bi = load_info(info, brow);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int rows = min(B, bi.n - bi.I * B);
   const int qloc0 = bi.I * B;
+  const int nh = min(8, H_s - 8 * hg);
 
-  v4f acc[8][NT];
+  // key tile of head h -> registers (rows past the sequence end are zero)
+  v4u kst[CPT];
+  auto fetch_k = [&](int h) {
+    const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D);
 #pragma unroll
-  for (int hh = 0; hh < 8; ++hh) {
-    const int h = hg * 8 + hh;
+    for (int u = 0; u < CPT; ++u) {
+      const int piece = threadIdx.x + u * NTHR;
+      const int row = piece / CPR, col = piece % CPR;
+      const int key = J * B + row;
+      kst[u] = key < bi.n ? ld16(Kh + ((size_t)key * D * sizeof(T)) + col * 16) : zero_u4();
+    }
+  };
+  auto stage_k = [&](int buf) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[hh][nt] = zero4();
-    if (h >= H_s) continue;
-    const T* Qh = Q + (size_t)h * T_tot * D;
-    const T* Kh = K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D;
-    Frag<T, D> qf;
-    qf.load(Qh + (size_t)(bi.tok0 + 16 * w + c) * D, 16 * w + c < rows, a);
+    for (int u = 0; u < CPT; ++u) {
+      const int piece = threadIdx.x + u * NTHR;
+      const int row = piece / CPR, col = piece % CPR;
+      *reinterpret_cast<v4u*>(&s_k[buf][row * ROWB + col * 16]) = kst[u];
+    }
+  };
+  const int qrow = 16 * w + c;
+  auto fetch_q = [&](Frag<T, D>& f, float* l2, int h) {
+    f.load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qrow) * D, qrow < rows, a);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * a + i;
+      l2[i] = r < rows ? lse2[(size_t)h * T_tot + bi.tok0 + r] : 0.f;
+    }
+  };
+
+  v4u rec[4][NT];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) rec[i][nt] = zero_u4();
+
+  Frag<T, D> qcur, qnext;
+  float lcur[4], lnext[4];
+  fetch_k(8 * hg);
+  fetch_q(qcur, lcur, 8 * hg);
+  stage_k(0);
+  __syncthreads();
+
+#pragma unroll
+  for (int hh = 0; hh < 8; ++hh) {   // unrolled: the record word of head hh is a constant
+    if (hh >= nh) break;
+    const int h = 8 * hg + hh;
+    const bool more = hh + 1 < nh;
+    if (more) {
+      fetch_k(h + 1);
+      fetch_q(qnext, lnext, h + 1);
+    }
+    const unsigned char* kt = s_k[hh & 1];
+    v4f acc[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      const int key = J * B + 16 * nt + c;
       Frag<T, D> kf;
-      kf.load(Kh + (size_t)key * D, key < bi.n, a);
-      acc[hh][nt] = dot_tile<D>(qf, kf, acc[hh][nt]);
+      load_lds_frag<D>(kf, kt + (16 * nt + c) * ROWB, a);
+      acc[nt] = dot_tile<D>(qcur, kf, zero4());
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * a + i;
+      const bool vq = r < rows;
+      float rsum = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int key = J * B + 16 * nt + c;
+        const float p = (vq && key <= qloc0 + r) ? fast_exp2(acc[nt][i] * scale2 - lcur[i]) : 0.f;
+        const uint16_t pb = f32_to_bf16(p);
+        rsum += bf16_to_f32(pb);
+        rec[i][nt][hh >> 1] |= (uint32_t)pb << (16 * (hh & 1));
+      }
+      rsum = row16_sum(rsum);
+      if (c == 0) part[((size_t)nblk * H_s + h) * B + r] = rsum;
+    }
+    if (more) {
+      stage_k((hh + 1) & 1);
+      qcur = qnext;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lcur[i] = lnext[i];
+    }
+    __syncthreads();
   }
-
-  float rs[8][4];
-#pragma unroll
-  for (int hh = 0; hh < 8; ++hh)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) rs[hh][i] = 0.f;
 
   uint16_t* pblk = probs + ((size_t)nblk * HG + hg) * (size_t)(B * B * 8);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * a + i;
-    const bool vq = r < rows;
-    float l2[8];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      const int h = hg * 8 + hh;
-      l2[hh] = (vq && h < H_s) ? lse2[(size_t)h * T_tot + bi.tok0 + r] : 0.f;
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int key = J * B + 16 * nt + c;
-      const bool ok = vq && key <= qloc0 + r;
-      uint32_t packed[4];
-#pragma unroll
-      for (int hp = 0; hp < 4; ++hp) {
-        uint32_t two = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int hh = 2 * hp + e;
-          const bool okh = ok && (hg * 8 + hh < H_s);
-          const float p = okh ? fast_exp2(acc[hh][nt][i] * scale2 - l2[hh]) : 0.f;
-          const uint16_t pb = f32_to_bf16(p);
-          rs[hh][i] += bf16_to_f32(pb);
-          two |= (uint32_t)pb << (16 * e);
-        }
-        packed[hp] = two;
-      }
-      st16(pblk + ((size_t)r * B + 16 * nt + c) * 8, v4u{packed[0], packed[1], packed[2], packed[3]});
-    }
-  }
-  // row sums over the 16 lanes of each column group
-#pragma unroll
-  for (int hh = 0; hh < 8; ++hh) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = rs[hh][i];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      v += __shfl_xor(v, 8, 64);
-      const int h = hg * 8 + hh;
-      if (c == 0 && h < H_s) part[((size_t)nblk * H_s + h) * B + 16 * w + 4 * a + i] = v;
-    }
+    for (int nt = 0; nt < NT; ++nt) st16(pblk + ((size_t)r * B + 16 * nt + c) * 8, rec[i][nt]);
   }
 }
 
@@ -457,7 +518,6 @@ __global__ void k_rowmass(const float* __restrict__ part, const int32_t* __restr
 // ------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------
-size_t stats_lds_bytes(int B, int nb_max) { return (size_t)(B / 16) * nb_max * sizeof(float); }
 
 bool compress_supported(int dtype, int B, int d) {
   return (dtype == DT_F32 || dtype == DT_BF16) && (B == 32 || B == 64) && (d == 64 || d == 128);
@@ -465,10 +525,9 @@ bool compress_supported(int dtype, int B, int d) {
 
 template <typename T, int B, int D>
 static hipError_t plan_t(const CompressArgs& a, hipStream_t s) {
-  const size_t lds = stats_lds_bytes(B, a.nb_max);
-  hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_brow * a.H_s), dim3(B * 4), lds, s,
-                     (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.nb_max,
-                     a.scale2, a.lse2, a.Mh);
+  hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_brow * a.H_s), dim3(B * 4), 0, s,
+                     (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.order, a.coff, a.n_causal,
+                     a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh);
   return hipGetLastError();
 }
 

@@ -16,9 +16,12 @@ struct CompressArgs {
   int n_brow, nb_max;
   const int32_t* info;   // [n_brow][4]
   const int32_t* order;  // [n_brow]
+  const int32_t* coff;   // [n_brow] causal block offset of each block row
+  int64_t n_causal;
   double tau;
   float scale2;          // log2(e) / sqrt(d)
   // context scratch
+  float2* zbuf;          // [H_s][n_causal][B] per (query, key block): {z, block max}
   float* lse2;           // [H_s][T]   log2-domain row logsumexp
   float* Mh;             // [H_s][n_brow][nb_max] per-head block masses
   double* M;             // [n_brow][nb_max] head-summed block masses
@@ -40,7 +43,6 @@ hipError_t compress_plan(const CompressArgs& a, hipStream_t s);
 // emit block indices, gather kept probabilities, kept row mass
 hipError_t compress_fill(const CompressArgs& a, hipStream_t s);
 bool compress_supported(int dtype, int B, int d);
-size_t stats_lds_bytes(int B, int nb_max);
 
 struct VprepArgs {
   const void* V;

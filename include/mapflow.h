@@ -57,6 +57,8 @@ typedef struct mf_ctx mf_ctx;
  *   brow_info   int32 [n_brow][4]   {first token of the block row, first token of its sequence,
  *                                     sequence length, block row index within the sequence}
  *   brow_order  int32 [n_brow]       block rows by descending in-sequence index (work order)
+ *   brow_coff   int32 [n_brow]       causal blocks of all earlier block rows (exclusive prefix
+ *                                    of I + 1): the row's offset in per-causal-block scratch
  *   block_ptr   int32 [n_brow + 1]   CSR row pointer over kept blocks
  *   block_idx   int32 [capacity]     kept block columns, ascending within each block row
  *   block_row   int32 [capacity]     block row of each kept block
@@ -80,6 +82,7 @@ typedef struct mf_bsr {
   int64_t nnzb;       /* kept blocks; valid after mf_compress or mf_bsr_sync  */
   int32_t* brow_info;
   int32_t* brow_order;
+  int32_t* brow_coff;
   int32_t* block_ptr;
   int32_t* block_idx;
   int32_t* block_row;
