@@ -17,6 +17,9 @@ typedef short v8s __attribute__((__vector_size__(8 * sizeof(short))));
 typedef _Float16 v8h __attribute__((__vector_size__(8 * sizeof(_Float16))));
 typedef float v4f __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t v4u __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));   // converts with v_cvt_pk_bf16_f32 (RNE)
+typedef _Float16 h2 __attribute__((ext_vector_type(2))); // converts with v_cvt_pk_f16_f32 (RNE)
 
 constexpr float kLog2e = 1.4426950408889634f;
 

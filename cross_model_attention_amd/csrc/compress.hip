@@ -365,138 +365,116 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 }
 
 // ------------------------------------------------------------------------------------------
-// k_gather: one workgroup per (kept block, group of 8 sender heads); the grid runs head group by
-// head group, so the Q / K rows in flight (one head group of the layer) stay cache resident.
-// Wave w owns query rows 16w..16w+15.  Heads are processed in turn: the key tile of head h + 1
-// is fetched into registers and staged into the other half of a double-buffered LDS tile while
-// head h's scores (queries x keys) are formed from LDS; the query rows of head h + 1 are
-// prefetched into registers.  Each probability exp(s - lse) is rounded to bf16 right away and
-// packed into the 16-byte record of its (row, column), which holds 8 heads; after the last head
-// every 16-lane group stores 256 contiguous bytes.  Per-block row sums of the stored values are
-// reduced across the 16 lanes of a column group with DPP.
+// k_gather: one workgroup per (block row, group of 8 sender heads), 8 waves; wave w owns sender
+// head 8*hg + w and keeps that head's query rows of the block row in registers for the whole row.
+// It sweeps the row's kept blocks in column order: per block, the key tile is read per 16-key
+// slice (the next slice in flight during the current one), scores are formed on MFMA, turned into
+// bf16 probabilities exp(s - lse) and written into an LDS tile laid out exactly like the stored
+// 16-byte records of 8 heads per (row, column); once all 8 waves have written their head, the
+// tile is streamed to HBM as one contiguous 64 KiB burst (LDS double buffered: one barrier per
+// block).  Per-block row sums of the stored values are reduced over the 16 lanes of a column
+// group with DPP.  Queries are read once per row, not once per block.
 // ------------------------------------------------------------------------------------------
 template <typename T, int B, int D>
-__global__ __launch_bounds__(B * 4) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
-                                                  int H_s, int64_t T_tot,
-                                                  const int32_t* __restrict__ info,
-                                                  const int32_t* __restrict__ block_idx,
-                                                  const int32_t* __restrict__ block_row,
-                                                  const int32_t* __restrict__ counters,
-                                                  int64_t capacity, const float* __restrict__ lse2,
-                                                  float scale2, uint16_t* __restrict__ probs,
-                                                  float* __restrict__ part) {
-  constexpr int NT = B / 16;
-  constexpr int NTHR = B * 4;
-  constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
-  constexpr int CHUNKS = B * D * (int)sizeof(T) / 16;      // 16-byte pieces of one key tile
-  constexpr int CPT = CHUNKS / NTHR;                       // pieces per thread
-  constexpr int CPR = D * (int)sizeof(T) / 16;             // pieces per key row
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
+__global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
+                                                int H_s, int64_t T_tot,
+                                                const int32_t* __restrict__ info,
+                                                const int32_t* __restrict__ order, int n_brow,
+                                                const int32_t* __restrict__ block_ptr,
+                                                const int32_t* __restrict__ block_idx,
+                                                const int32_t* __restrict__ counters,
+                                                int64_t capacity, const float* __restrict__ lse2,
+                                                float scale2, uint16_t* __restrict__ probs,
+                                                float* __restrict__ part) {
+  constexpr int MT = B / 16;                       // 16-row tiles
+  constexpr int NT = B / 16;                       // 16-key tiles
+  constexpr int TILE = B * B * 16;                 // bytes of one block's 8-head records
+  __shared__ __attribute__((aligned(16))) unsigned char s_out[2][TILE];
 
   const int HG = (H_s + 7) >> 3;
-  const int hg = (int)(blockIdx.x / capacity);
-  const int64_t nblk = blockIdx.x - (int64_t)hg * capacity;
-  const int64_t nnzb = min((int64_t)counters[0], capacity);
-  if (nblk >= nnzb || hg >= HG) return;
-  const int brow = block_row[nblk];
-  const int J = block_idx[nblk];
+  const int hg = blockIdx.x / n_brow;
+  const int brow = order[blockIdx.x % n_brow];
   const BrowInfo bi = load_info(info, brow);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int rows = min(B, bi.n - bi.I * B);
   const int qloc0 = bi.I * B;
-  const int nh = min(8, H_s - 8 * hg);
+  const int h = 8 * hg + w;
+  const bool active = h < H_s;                     // padding heads write zeros
+  const int64_t nnzb = min((int64_t)counters[0], capacity);
+  const int t0 = (int)min((int64_t)block_ptr[brow], nnzb);
+  const int t1 = (int)min((int64_t)block_ptr[brow + 1], nnzb);
+  if (t0 >= t1) return;
 
-  // key tile of head h -> registers (rows past the sequence end are zero)
-  v4u kst[CPT];
-  auto fetch_k = [&](int h) {
-    const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D);
+  const int hq = active ? h : 0;
+  Frag<T, D> qf[MT];
+  float l2[MT][4];
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int piece = threadIdx.x + u * NTHR;
-      const int row = piece / CPR, col = piece % CPR;
-      const int key = J * B + row;
-      kst[u] = key < bi.n ? ld16(Kh + ((size_t)key * D * sizeof(T)) + col * 16) : zero_u4();
-    }
-  };
-  auto stage_k = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int piece = threadIdx.x + u * NTHR;
-      const int row = piece / CPR, col = piece % CPR;
-      *reinterpret_cast<v4u*>(&s_k[buf][row * ROWB + col * 16]) = kst[u];
-    }
-  };
-  const int qrow = 16 * w + c;
-  auto fetch_q = [&](Frag<T, D>& f, float* l2, int h) {
-    f.load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qrow) * D, qrow < rows, a);
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = 16 * mt + c;
+    qf[mt].load(Q + (size_t)hq * T_tot * D + (size_t)(bi.tok0 + r) * D, active && r < rows, a);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * a + i;
-      l2[i] = r < rows ? lse2[(size_t)h * T_tot + bi.tok0 + r] : 0.f;
+      const int rr = 16 * mt + 4 * a + i;
+      l2[mt][i] = (active && rr < rows) ? lse2[(size_t)hq * T_tot + bi.tok0 + rr] : 0.f;
     }
+  }
+  const T* Kh = K + (size_t)hq * T_tot * D + (size_t)bi.seq0 * D;
+  auto load_k = [&](Frag<T, D>& f, int J, int nt) {
+    const int key = J * B + 16 * nt + c;
+    f.load(Kh + (size_t)key * D, active && key < bi.n, a);
   };
 
-  v4u rec[4][NT];
+  Frag<T, D> kf, kn;
+  load_k(kf, block_idx[t0], 0);
+  for (int t = t0; t < t1; ++t) {
+    const int J = block_idx[t];
+    const int Jn = t + 1 < t1 ? block_idx[t + 1] : J;
+    const bool masked = J == bi.I || rows < B;
+    unsigned char* tile = s_out[(t - t0) & 1];
+    float rs[MT][4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) rec[i][nt] = zero_u4();
-
-  Frag<T, D> qcur, qnext;
-  float lcur[4], lnext[4];
-  fetch_k(8 * hg);
-  fetch_q(qcur, lcur, 8 * hg);
-  stage_k(0);
-  __syncthreads();
-
-#pragma unroll
-  for (int hh = 0; hh < 8; ++hh) {   // unrolled: the record word of head hh is a constant
-    if (hh >= nh) break;
-    const int h = 8 * hg + hh;
-    const bool more = hh + 1 < nh;
-    if (more) {
-      fetch_k(h + 1);
-      fetch_q(qnext, lnext, h + 1);
-    }
-    const unsigned char* kt = s_k[hh & 1];
-    v4f acc[NT];
+      for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      Frag<T, D> kf;
-      load_lds_frag<D>(kf, kt + (16 * nt + c) * ROWB, a);
-      acc[nt] = dot_tile<D>(qcur, kf, zero4());
-    }
+      // next key slice (of this block, or the first of the next block) in flight
+      if (nt + 1 < NT) load_k(kn, J, nt + 1);
+      else if (t + 1 < t1) load_k(kn, Jn, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * a + i;
-      const bool vq = r < rows;
-      float rsum = 0.f;
+      for (int mt = 0; mt < MT; ++mt) {
+        const v4f sc = dot_tile<D>(qf[mt], kf, zero4());
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int key = J * B + 16 * nt + c;
-        const float p = (vq && key <= qloc0 + r) ? fast_exp2(acc[nt][i] * scale2 - lcur[i]) : 0.f;
-        const uint16_t pb = f32_to_bf16(p);
-        rsum += bf16_to_f32(pb);
-        rec[i][nt][hh >> 1] |= (uint32_t)pb << (16 * (hh & 1));
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * a + i;
+          float p = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
+          if (masked) {
+            const int key = J * B + 16 * nt + c;
+            p = (r < rows && key <= qloc0 + r) ? p : 0.f;
+          }
+          if (!active) p = 0.f;
+          const __bf16 pb = (__bf16)p;
+          rs[mt][i] += (float)pb;
+          *reinterpret_cast<__bf16*>(tile + ((r * B + 16 * nt + c) * 8 + w) * 2) = pb;
+        }
       }
-      rsum = row16_sum(rsum);
-      if (c == 0) part[((size_t)nblk * H_s + h) * B + r] = rsum;
+      kf = kn;
     }
-    if (more) {
-      stage_k((hh + 1) & 1);
-      qcur = qnext;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lcur[i] = lnext[i];
-    }
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float v = row16_sum(rs[mt][i]);
+        if (c == 0 && active) part[((size_t)t * H_s + h) * B + 16 * mt + 4 * a + i] = v;
+      }
     __syncthreads();
-  }
-
-  uint16_t* pblk = probs + ((size_t)nblk * HG + hg) * (size_t)(B * B * 8);
+    // stream the finished tile: contiguous 16-byte pieces
+    unsigned char* dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * w + 4 * a + i;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) st16(pblk + ((size_t)r * B + 16 * nt + c) * 8, rec[i][nt]);
+    for (int u = 0; u < TILE / 16 / 512; ++u) {
+      const int piece = threadIdx.x + u * 512;
+      st16(dst + (size_t)piece * 16, *reinterpret_cast<const v4u*>(tile + piece * 16));
+    }
   }
 }
 
@@ -534,11 +512,10 @@ static hipError_t plan_t(const CompressArgs& a, hipStream_t s) {
 template <typename T, int B, int D>
 static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
   const int HG = (a.H_s + 7) / 8;
-  const uint64_t grid = (uint64_t)a.capacity * HG;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gather<T, B, D>), dim3((unsigned)grid), dim3(B * 4), 0, s, (const T*)a.Q,
-                     (const T*)a.K, a.H_s, a.T, a.info, a.block_idx, a.block_row, a.counters,
-                     a.capacity, a.lse2, a.scale2, a.probs, a.part);
+  if (a.capacity == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gather<T, B, D>), dim3((unsigned)a.n_brow * HG), dim3(512), 0, s, (const T*)a.Q,
+                     (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.block_ptr, a.block_idx,
+                     a.counters, a.capacity, a.lse2, a.scale2, a.probs, a.part);
   return hipGetLastError();
 }
 

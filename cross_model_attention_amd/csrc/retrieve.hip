@@ -181,30 +181,23 @@ constexpr int RT_ROWS = 16;     // rows per work item
 constexpr int RT_WAVES = 8;     // waves per workgroup
 constexpr int ROWS_PER_WAVE = RT_ROWS / RT_WAVES;
 
-template <int B>
+// LDS layout of the mixed map: [head][row][key] fp16.  Row and head strides of 32 mod 128 bytes
+// make the 16-byte stage-2 reads (lane (a, c): row c, key chunk a) and stage-1 writes (lane (a,
+// c): head c, key chunk a) bank-conflict free on gfx950; with 32 receiver heads that padding
+// does not fit twice in LDS, so HP = 4 keeps 16-byte padding (2-way conflicts).
+template <int B, int HP>
 struct AhatLayout {
-  static constexpr int kRowBytes = B * 2 + 16;            // 16 B pad: conflict-free reads
-  static constexpr int kHeadBytes = RT_ROWS * kRowBytes + 16;  // 16 B pad: conflict-free writes
+  static constexpr bool kWide = HP <= 3;
+  static constexpr int kRowBytes = kWide ? 160 : B * 2 + 16;
+  static constexpr int kHeadBytes = RT_ROWS * kRowBytes + (kWide ? 32 : 0);
+  static_assert(!kWide || B * 2 <= 160, "row must fit its stride");
 };
 
-// Mixing tiles: receiver heads come in chunks of 16; a full chunk uses two N-tiles (bf16 "hi"
-// and "lo" parts of the scaled weights), a last chunk of <= 8 heads packs hi in columns 0..7 and
-// lo in columns 8..15 of one tile.  HP = ceil(H_r / 8) tiles in total; HP odd <=> last chunk
-// packed.  The same HP is the number of receiver heads each wave owns in stage 2.
-template <int HP>
-struct MixTiles {
-  static constexpr bool kPackedLast = (HP & 1) != 0;
-  __device__ static void head_of(int nt, int c, int& g, bool& lo) {
-    if (kPackedLast && nt == HP - 1) {
-      g = 16 * (nt / 2) + (c & 7);
-      lo = c >= 8;
-    } else {
-      g = 16 * (nt / 2) + c;
-      lo = (nt & 1) != 0;
-    }
-  }
-};
-
+// Head mix on MFMA: N-tiles are receiver heads in chunks of 16 (NTG = ceil(H_r / 16) tiles), the
+// contraction runs over the sender heads twice, once against the bf16 "hi" part and once against
+// the bf16 "lo" part of the scaled weights, accumulating into the same fp32 tile: Ws = hi + lo
+// keeps ~16 bits of W while the kept probabilities enter the MFMA exactly.  HP = ceil(H_r / 8)
+// is the number of receiver heads each of the 8 waves owns in stage 2.
 template <int B, int D, int HP, int KC>
 __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const uint16_t* __restrict__ probs, const int32_t* __restrict__ block_ptr,
@@ -217,14 +210,15 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   constexpr int MT = B / 16;               // 16-key M-tiles per row
   constexpr int NCH = B / 32;              // 32-key chunks per block
   constexpr int NDT = D / 16;              // 16-column output tiles
-  constexpr int RB = AhatLayout<B>::kRowBytes;
-  constexpr int GB = AhatLayout<B>::kHeadBytes;
+  constexpr int RB = AhatLayout<B, HP>::kRowBytes;
+  constexpr int GB = AhatLayout<B, HP>::kHeadBytes;
   constexpr int HR_MAX = 8 * HP;
+  constexpr int NTG = (HP + 1) / 2;        // 16-head N-tiles of the mix
 
   __shared__ __attribute__((aligned(16))) unsigned char s_ahat[2][HR_MAX * GB];
-  __shared__ float s_w[HR_MAX][64];        // scaled weights (hi + lo), fp32
   __shared__ float s_den[HR_MAX][RT_ROWS];
   __shared__ int s_sexp[HR_MAX];
+  __shared__ v4u s_wop[NTG][KC][2][64];
 
   // ---- work item: XCD-aware (the row tiles of one block row share an XCD) --------------------
   const int b = blockIdx.x;
@@ -243,6 +237,9 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
 
   // ---- setup: per-head scale, scaled weights, denominators ---------------------------------
+  // scaled weights (hi + lo, fp32) live in the second mixed-map buffer until the loop needs it
+  static_assert(HR_MAX * 64 * sizeof(float) <= HR_MAX * GB, "weights fit in one Ahat buffer");
+  float (*s_w)[64] = reinterpret_cast<float (*)[64]>(s_ahat[1]);
   if (threadIdx.x < HR_MAX) {
     const int g = threadIdx.x;
     int e = 0;
@@ -278,28 +275,35 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     s_den[g][i] = den;
   }
 
-  // stage-1 B operands: weights of virtual heads (hi / lo) for head dims 32kc + 8a + e
-  v8s wop[HP][KC];
+  // stage-1 B operands (weights of virtual heads, bf16 hi / lo, head dims 32kc + 8a + e), kept in
+  // LDS per lane and read on use: registers stay free for the operand prefetches
+  if (w == 0) {
 #pragma unroll
-  for (int nt = 0; nt < HP; ++nt) {
-    int g;
-    bool lo;
-    MixTiles<HP>::head_of(nt, c, g, lo);
+    for (int nt = 0; nt < NTG; ++nt) {
+      const int g = 16 * nt + c;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      v8s v;
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int h = 32 * kc + 8 * a + e;
-        uint16_t bits = 0;
-        if (g < H_r && h < H_s) {
-          const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
-          const uint16_t hb = f32_to_bf16(x);
-          bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
+        for (int lo = 0; lo < 2; ++lo) {
+          uint32_t pk[4];
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            uint32_t two = 0;
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+              const int h = 32 * kc + 8 * a + 2 * e2 + q2;
+              uint32_t bits = 0;
+              if (g < H_r && h < H_s) {
+                const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
+                const uint16_t hb = f32_to_bf16(x);
+                bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
+              }
+              two |= bits << (16 * q2);
+            }
+            pk[e2] = two;
+          }
+          s_wop[nt][kc][lo][lane] = v4u{pk[0], pk[1], pk[2], pk[3]};
         }
-        v[e] = (short)bits;
-      }
-      wop[nt][kc] = v;
     }
   }
 
@@ -341,49 +345,56 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   if (t0 < t1) load_p(t0);
   __syncthreads();
 
+  // V operand tiles of the wave's first KV head for key chunk 0 are fetched before the head mix,
+  // so their latency hides under it; later chunks and other KV heads are loaded on use.
+  int kvj[HP];
+#pragma unroll
+  for (int j = 0; j < HP; ++j) kvj[j] = sg[j] >= 0 ? (int)hm.kv[sg[j]] : 0;
+  const int kv0 = kvj[0];
+  auto vtile = [&](int kv, int kbrow, int ch) {
+    return vfrag + ((((size_t)kv * n_brow + kbrow) * NCH + ch) * NDT) * 512 + lane * 8;
+  };
   for (int t = t0; t < t1; ++t) {
     unsigned char* buf = s_ahat[(t - t0) & 1];
+    const int J = block_idx[t];
+    const int kbrow = kbrow0 + J;
+    v8h vpre[NCH][NDT];
+    {
+      const uint16_t* vb = vtile(kv0, kbrow, 0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
+    }
     // ---- stage 1: head mix -> fp16 Ahat in LDS ----
 #pragma unroll
     for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
       const int ii = ROWS_PER_WAVE * w + rr;
 #pragma unroll
       for (int ch = 0; ch < NCH; ++ch) {
-        v4f mix[2][HP];
 #pragma unroll
-        for (int half = 0; half < 2; ++half)
+        for (int nt = 0; nt < NTG; ++nt) {
+          v4f mix[2];
 #pragma unroll
-          for (int nt = 0; nt < HP; ++nt) {
+          for (int half = 0; half < 2; ++half) {
             v4f m4 = zero4();
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) m4 = mfma_bf16(as_v8s(pa[rr][2 * ch + half][kc]), wop[nt][kc], m4);
-            mix[half][nt] = m4;
-          }
-        // combine hi + lo per receiver head and write 8 fp16 values (keys of chunk ch, group a)
-#pragma unroll
-        for (int pr = 0; pr < (HP + 1) / 2; ++pr) {
-          const bool packed = MixTiles<HP>::kPackedLast && (2 * pr == HP - 1);
-          float v[8];
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (packed) {
-                const float x = mix[half][2 * pr][i];
-                const float y = __int_as_float(__builtin_amdgcn_update_dpp(
-                    0, __float_as_int(x), 0x128 /* row_ror:8 */, 0xF, 0xF, false));
-                v[4 * half + i] = x + y;
-              } else {
-                v[4 * half + i] = mix[half][2 * pr][i] + mix[half][2 * pr + 1][i];
-              }
+            for (int kc = 0; kc < KC; ++kc) {
+              const v8s p8 = as_v8s(pa[rr][2 * ch + half][kc]);
+              m4 = mfma_bf16(p8, as_v8s(s_wop[nt][kc][0][lane]), m4);
+              m4 = mfma_bf16(p8, as_v8s(s_wop[nt][kc][1][lane]), m4);
             }
-          const int g = 16 * pr + c;
-          const bool wr = packed ? (c < 8 && g < H_r) : (g < H_r);
-          if (wr) {
+            mix[half] = m4;
+          }
+          // lane (a, c): receiver head 16 nt + c, keys 32 ch + 16 half + 4a + i -> 8 fp16 values
+          const int g = 16 * nt + c;
+          if (g < H_r) {
             uint32_t pk[4];
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
-              pk[p] = (uint32_t)f32_to_f16_bits(v[2 * p]) | ((uint32_t)f32_to_f16_bits(v[2 * p + 1]) << 16);
+            for (int half = 0; half < 2; ++half)
+#pragma unroll
+              for (int p2 = 0; p2 < 2; ++p2) {
+                const f2 v2 = {mix[half][2 * p2], mix[half][2 * p2 + 1]};
+                pk[2 * half + p2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, h2));
+              }
             *reinterpret_cast<v4u*>(buf + g * GB + ii * RB + (ch * 4 + a) * 16) = v4u{pk[0], pk[1], pk[2], pk[3]};
           }
         }
@@ -393,22 +404,26 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     __syncthreads();
 
     // ---- stage 2: P.V for this wave's receiver heads ----
-    const int J = block_idx[t];
-    const int kbrow = kbrow0 + J;
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      int cur_kv = -1;
-      v8h vop[NDT];
+      if (ch > 0) {
+        const uint16_t* vb = vtile(kv0, kbrow, ch);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
+      }
 #pragma unroll
       for (int j = 0; j < HP; ++j) {
         const int g = sg[j];
         if (g < 0) continue;
-        const int kv = hm.kv[g];
-        if (kv != cur_kv) {
-          const uint16_t* vb = vfrag + ((((size_t)kv * n_brow + kbrow) * NCH + ch) * NDT) * 512 + lane * 8;
+        const int kv = kvj[j];
+        v8h vop[NDT];
+        if (kv == kv0) {
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) vop[dt] = vpre[ch][dt];
+        } else {
+          const uint16_t* vb = vtile(kv, kbrow, ch);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
-          cur_kv = kv;
         }
         const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + g * GB + c * RB + (ch * 4 + a) * 16));
 #pragma unroll
