@@ -6,8 +6,9 @@
 // stored; the dense L x L map is never assembled.
 //
 // Kernels, in launch order:
-//   k_stats        two passes per (block row, sender head): pass 1 the row logsumexp (online
-//                  max / sum over key blocks), pass 2 the per-block mass sum of exp(s - lse)
+//   k_stats        one score pass per (block row, sender head): per (query, key block) the block
+//                  maximum and scaled sum, from which the row logsumexp and the per-block mass
+//                  of exp(s - lse) follow exactly
 //   k_head_reduce  head-summed block masses in fp64, fixed head order
 //   k_select       per block row: forced sink + diagonal, then descending mass (ties: lower
 //                  column) until the kept mass reaches tau * H_s * rows
