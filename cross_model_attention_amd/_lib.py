@@ -45,6 +45,7 @@ _SIGNATURES = {
     "mf_bsr_create": (c_int, [c_void_p, c_int32, c_int32, _P_I32, c_int32, c_int64, POINTER(MfBsr)]),
     "mf_bsr_download": (c_int, [c_void_p, POINTER(MfBsr), _P_I32, _P_I32, POINTER(c_uint16),
                                 POINTER(c_float)]),
+    "mf_bsr_download_blocks": (c_int, [c_void_p, POINTER(MfBsr), c_int64, c_int64, _P_I32, POINTER(c_uint16)]),
     "mf_bsr_upload": (c_int, [c_void_p, POINTER(MfBsr), _P_I32, _P_I32, POINTER(c_uint16),
                               POINTER(c_float)]),
     "mf_bsr_free": (c_int, [c_void_p, POINTER(MfBsr)]),
@@ -75,7 +76,7 @@ def load() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libmapflow.so is not built ({LIB_PATH}); run "
-                          "`python -m cross_model_attention_amd.build`")
+                          "`python cross_model_attention_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,7 @@
 """Build libmapflow.so (HIP, gfx950) in-tree: cross_model_attention_amd/lib/libmapflow.so.
 
-Usage: ``python -m cross_model_attention_amd.build`` (or ``__graft_entry__.build()``).  Always
+Usage: ``python cross_model_attention_amd/build.py`` (or ``__graft_entry__.build()``); run by path,
+since importing the package loads the library this script replaces.  Always
 recompiles every source; the objects go to ``cross_model_attention_amd/_build/``.
 """
 from __future__ import annotations

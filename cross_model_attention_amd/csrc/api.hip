@@ -539,6 +539,29 @@ MF_EXPORT mf_status mf_bsr_download(mf_ctx* ctx, mf_bsr* bsr, int32_t* block_ptr
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_bsr_download_blocks(mf_ctx* ctx, mf_bsr* bsr, int64_t first, int64_t count,
+                                           int32_t* block_idx_host, uint16_t* probs_host) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  int32_t cnt[2] = {0, 0};
+  MF_HIP(hipMemcpy(cnt, bsr->counters, sizeof(cnt), hipMemcpyDeviceToHost), "reading kept-block count");
+  bsr->nnzb = std::min<int64_t>(cnt[0], bsr->capacity);
+  if (first < 0 || count < 0 || first + count > bsr->nnzb)
+    return fail(MF_ERR_INVALID, "blocks [%lld, %lld) outside the %lld kept blocks", (long long)first,
+                (long long)(first + count), (long long)bsr->nnzb);
+  if (count == 0) return MF_OK;
+  if (block_idx_host)
+    MF_HIP(hipMemcpy(block_idx_host, bsr->block_idx + first, (size_t)count * 4, hipMemcpyDeviceToHost), "copy block_idx");
+  if (probs_host) {
+    const size_t bb = probs_block_bytes(bsr->H_s, bsr->B);
+    MF_HIP(hipMemcpy(probs_host, reinterpret_cast<const unsigned char*>(bsr->probs) + (size_t)first * bb,
+                     (size_t)count * bb, hipMemcpyDeviceToHost), "copy probs");
+  }
+  return MF_OK;
+}
+
 MF_EXPORT mf_status mf_bsr_upload(mf_ctx* ctx, mf_bsr* bsr, const int32_t* block_ptr_host,
                                   const int32_t* block_idx_host, const uint16_t* probs_host,
                                   const float* rkm_host) {

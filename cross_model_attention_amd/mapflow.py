@@ -150,6 +150,32 @@ class BlockStore:
                 "probs": probs_store_to_canonical(bits[:n], r.H_s), "row_kept_mass": rkm[:, : r.T],
                 "nnzb": n}
 
+    def meta_to_host(self) -> dict:
+        """block_ptr and row_kept_mass only (no probabilities)."""
+        r = self.raw
+        ptr = np.zeros(r.n_brow + 1, np.int32)
+        rkm = np.zeros((r.H_s, max(r.T, 1)), np.float32)
+        check(_L.mf_bsr_download(self.ctx.handle, ctypes.byref(r),
+                                 ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, None,
+                                 rkm.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+        return {"block_ptr": ptr, "row_kept_mass": rkm[:, : r.T], "nnzb": int(r.nnzb)}
+
+    def blocks_to_host(self, first: int, count: int, probs: bool = True) -> dict:
+        """Kept blocks [first, first + count): columns and (optionally) canonical probs
+        [count, H_s, B, B]."""
+        r = self.raw
+        n = max(int(count), 1)
+        idx = np.zeros(n, np.int32)
+        bits = np.zeros((n, (r.H_s + 7) // 8, r.B, r.B, 8), np.uint16) if probs else None
+        check(_L.mf_bsr_download_blocks(
+            self.ctx.handle, ctypes.byref(r), int(first), int(count),
+            idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+            bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16)) if probs else None))
+        out = {"block_idx": idx[:count]}
+        if probs:
+            out["probs"] = probs_store_to_canonical(bits[:count], r.H_s)
+        return out
+
     def upload(self, block_ptr, block_idx, probs, row_kept_mass) -> None:
         """Fill from host arrays; ``probs`` canonical [nnzb, H_s, B, B] with bf16 values."""
         r = self.raw

@@ -153,6 +153,15 @@ mf_status mf_bsr_download(mf_ctx* ctx, mf_bsr* bsr, int32_t* block_ptr_host,
                           float* row_kept_mass_host);
 
 /*
+ * Copy the kept blocks [first, first + count) of a store to host memory (synchronous; waits for
+ * the device): block_idx_host int32 [count] and probs_host bf16 bits [count][ceil(H_s/8)][B][B][8]
+ * (either may be NULL).  The range must lie inside [0, nnzb) of the device's kept-block count;
+ * MF_ERR_INVALID otherwise.  Lets a caller inspect part of a store that does not fit the host.
+ */
+mf_status mf_bsr_download_blocks(mf_ctx* ctx, mf_bsr* bsr, int64_t first, int64_t count,
+                                 int32_t* block_idx_host, uint16_t* probs_host);
+
+/*
  * Fill a store from host memory (synchronous), e.g. to restore a store saved with
  * mf_bsr_download from a host-memory tier.  Same layouts as mf_bsr_download.  block_ptr_host
  * must start at 0, be non-decreasing and end at nnzb <= capacity; each block row's columns must

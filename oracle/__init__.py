@@ -24,6 +24,7 @@ from .mapflow_oracle import (  # noqa: F401
     OracleBSR,
     attention_rows,
     bf16_round,
+    block_masses,
     block_row_compress,
     compress,
     dense_causal_attention,

@@ -63,10 +63,10 @@ def attention_rows(q: np.ndarray, k: np.ndarray, r0: int, r1: int):
     q, k: [n, d] float64 for one head of one sequence.  Returns (A, lse) with A [r1-r0, r1]
     (zero above the diagonal) and lse [r1-r0] the natural-log row logsumexp.
     """
-    q = np.asarray(q, dtype=F64)
-    k = np.asarray(k, dtype=F64)
+    q = np.asarray(q[r0:r1], dtype=F64)
+    k = np.asarray(k[:r1], dtype=F64)
     d = q.shape[1]
-    s = (q[r0:r1] @ k[:r1].T) / math.sqrt(d)                      # [rows, r1]
+    s = (q @ k.T) / math.sqrt(d)                                  # [rows, r1]
     i_idx = np.arange(r0, r1)[:, None]
     j_idx = np.arange(r1)[None, :]
     causal = j_idx <= i_idx
@@ -123,6 +123,30 @@ def select_blocks(M_row: np.ndarray, I: int, T_I: float, tau: float) -> dict:
 # ----------------------------------------------------------------------------------------------
 # O4-O7 for one block row: block masses, selection, bf16 probs, kept row mass
 # ----------------------------------------------------------------------------------------------
+def block_masses(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: int, B: int):
+    """Block-level statistics of block row I of one sequence: the first stage of the staged
+    compression in [MapFlow开源, 只存重要的:块稀疏压缩].
+
+    M[J] = sum_h sum_{i in I} sum_{j in J} A[h, i, j] for J = 0..I (explicit block sums over the
+    causal softmax map of every sender head); also returns lse [H_s, rows].
+    """
+    H_s = Q.shape[0]
+    r0 = I * B
+    r1 = min(seq_len, (I + 1) * B)
+    rows = r1 - r0
+    M = np.zeros(I + 1, dtype=F64)
+    lse = np.zeros((H_s, rows), dtype=F64)
+    for h in range(H_s):
+        q = Q[h, seq_start: seq_start + seq_len]
+        k = K[h, seq_start: seq_start + seq_len]
+        A, lse[h] = attention_rows(q, k, r0, r1)
+        for J in range(I + 1):
+            c0 = J * B
+            c1 = min(seq_len, (J + 1) * B)
+            M[J] += A[:, c0:c1].sum()
+    return M, lse
+
+
 def block_row_compress(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: int,
                        B: int, tau: float, keep_exact: bool = False) -> dict:
     """Compress block row I of one sequence (all sender heads).
@@ -140,17 +164,7 @@ def block_row_compress(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: in
     r0 = I * B
     r1 = min(seq_len, (I + 1) * B)
     rows = r1 - r0
-    nb_cols = I + 1
-    M = np.zeros(nb_cols, dtype=F64)
-    lse = np.zeros((H_s, rows), dtype=F64)
-    for h in range(H_s):
-        q = Q[h, seq_start: seq_start + seq_len]
-        k = K[h, seq_start: seq_start + seq_len]
-        A, lse[h] = attention_rows(q, k, r0, r1)
-        for J in range(nb_cols):
-            c0 = J * B
-            c1 = min(seq_len, (J + 1) * B)
-            M[J] += A[:, c0:c1].sum()
+    M, lse = block_masses(Q, K, seq_start, seq_len, I, B)
     T_I = float(H_s * rows)
     sel = select_blocks(M, I, T_I, tau)
     kept = sel["kept"]

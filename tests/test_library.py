@@ -21,7 +21,7 @@ def _declared_functions():
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(_lib.LIB_PATH):
-        pytest.fail("libmapflow.so is not built; run `python -m cross_model_attention_amd.build`")
+        pytest.fail("libmapflow.so is not built; run `python cross_model_attention_amd/build.py`")
     return _lib.load()
 
 
