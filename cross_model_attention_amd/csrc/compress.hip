@@ -367,15 +367,166 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 
 // ------------------------------------------------------------------------------------------
 // k_gather: one workgroup per (block row, group of 8 sender heads), 8 waves; wave w owns sender
-// head 8*hg + w and keeps that head's query rows of the block row in registers for the whole row.
-// It sweeps the row's kept blocks in column order: per block, the key tile is read per 16-key
-// slice (the next slice in flight during the current one), scores are formed on MFMA, turned into
-// bf16 probabilities exp(s - lse) and written into an LDS tile laid out exactly like the stored
-// 16-byte records of 8 heads per (row, column); once all 8 waves have written their head, the
-// tile is streamed to HBM as one contiguous 64 KiB burst (LDS double buffered: one barrier per
-// block).  Per-block row sums of the stored values are reduced over the 16 lanes of a column
-// group with DPP.  Queries are read once per row, not once per block.
+// head 8*hg + w and keeps that head's query rows of the block row in registers for the whole
+// row.  It sweeps the row's kept blocks in column order; per block and 16-key slice:
+//   * the slice's keys are fetched with fully coalesced 16-byte loads (each load instruction reads
+//     1 KiB of contiguous key rows) two slices ahead, and passed through a per-wave LDS stage into
+//     MFMA operand layout (16-byte chunks XOR-swizzled by row: conflict-free both ways).  Loading
+//     the operand layout straight from memory would touch 16 rows per instruction and make the
+//     vector L1 the bottleneck;
+//   * scores are formed on MFMA and turned into bf16 probabilities exp(s - lse); a lane's values
+//     for two adjacent rows are converted as one packed pair, and each stored value is added to
+//     its row's sum with a bf16 dot2 against a unit vector (no unpacking);
+//   * the pair is written into an LDS tile laid out like the stored 16-byte records of 8 heads
+//     per (row, column), head slots rotated by 2*((row / 4) mod 4) so that one wave's 2-byte
+//     writes hit distinct banks;
+// once all 8 waves have written their head, the tile is streamed to HBM with the rotation undone,
+// with non-temporal stores spread over the next block's slices, each part issued right after
+// that slice's key loads (LDS double buffered where it fits: one barrier per block).
+// The causal / partial-row mask is evaluated only on blocks that need it.
 // ------------------------------------------------------------------------------------------
+template <typename T, int D>
+struct KStage {
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per key row
+  static constexpr int kSliceBytes = 16 * kRowBytes;           // one 16-key slice
+  static constexpr int kLoads = kSliceBytes / 1024;            // 1 KiB coalesced loads per slice
+  static_assert(kSliceBytes % 1024 == 0, "slice must split into 1 KiB loads");
+  // byte offset of (row, chunk) inside the stage
+  __device__ static int at(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & (kChunks - 1))) << 4); }
+};
+
+template <typename T, int D, int NL>
+__device__ __forceinline__ void kstage_fetch(v4u (&raw)[NL], const T* Kh, int key0, int kvalid, int lane) {
+  using S = KStage<T, D>;
+  static_assert(NL == S::kLoads, "load count");
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int piece = i * 64 + lane;
+    const int row = piece / S::kChunks, chunk = piece % S::kChunks;
+    const int key = key0 + row;
+    raw[i] = key < kvalid ? ld16(reinterpret_cast<const unsigned char*>(Kh + (size_t)key * D) + chunk * 16)
+                          : zero_u4();
+  }
+}
+
+template <typename T, int D, int NL>
+__device__ __forceinline__ void kstage_put(unsigned char* st, const v4u (&raw)[NL], int lane) {
+  using S = KStage<T, D>;
+#pragma unroll
+  for (int i = 0; i < NL; ++i) {
+    const int piece = i * 64 + lane;
+    *reinterpret_cast<v4u*>(st + S::at(piece / S::kChunks, piece % S::kChunks)) = raw[i];
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void kstage_get(Frag<uint16_t, D>& f, const unsigned char* st, int a, int c) {
+  using S = KStage<uint16_t, D>;
+#pragma unroll
+  for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
+    f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(st + S::at(c, 4 * k + a)));
+}
+template <int D>
+__device__ __forceinline__ void kstage_get(Frag<float, D>& f, const unsigned char* st, int a, int c) {
+  using S = KStage<float, D>;
+#pragma unroll
+  for (int k = 0; k < Frag<float, D>::N; ++k)
+    f.v[k] = *reinterpret_cast<const float*>(st + S::at(c, k) + 4 * a);
+}
+
+// Stream part q of NQ of a finished 8-head record tile (B x B records of 16 bytes) to HBM with the
+// head-slot rotation undone.  Each thread handles contiguous 16-byte pieces; the rotation of a
+// piece depends only on its row, which is uniform over a wave.
+template <int B>
+__device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned char* dst, int q, int NQ) {
+  constexpr int PIECES = B * B / 512;              // pieces per thread per tile
+  const int per = PIECES / NQ;
+#pragma unroll
+  for (int u0 = 0; u0 < PIECES; ++u0) {
+    if (u0 / per != q) continue;
+    const int piece = threadIdx.x + u0 * 512;
+    const int rot = ((piece / B) >> 2) & 3;
+    const v4u x = *reinterpret_cast<const v4u*>(tile + piece * 16);
+    v4u y;
+    if (rot == 0) y = x;
+    else if (rot == 1) y = v4u{x[1], x[2], x[3], x[0]};
+    else if (rot == 2) y = v4u{x[2], x[3], x[0], x[1]};
+    else y = v4u{x[3], x[0], x[1], x[2]};
+    __builtin_nontemporal_store(y, reinterpret_cast<v4u*>(dst + (size_t)piece * 16));
+  }
+}
+
+template <typename T, int B, int D, bool MASKED, int NL>
+__device__ __forceinline__ void gather_block(const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16][4],
+                                             Frag<T, D>& kf, v4u (&raw)[2][NL],
+                                             unsigned char* kst, const T* Kh, int J, int Jn, bool has_next,
+                                             int kvalid, int rows, int qdiag, float scale2,
+                                             unsigned char* tile, int w, int lane, int a, int c,
+                                             float (&rs)[B / 16][4], const unsigned char* prev,
+                                             unsigned char* prev_dst) {
+  constexpr int MT = B / 16;   // 16-row tiles
+  constexpr int NT = B / 16;   // 16-key slices
+  static_assert(NT % 2 == 0, "key slices alternate between the two fetch buffers");
+  // unit vectors (1, 0) and (0, 1) in bf16, kept in registers: as inline constants the compiler
+  // would encode 1.0, which the dot2 reads as the pair (0, 1)
+  uint32_t u0 = 0x00003F80u, u1 = 0x3F800000u;
+  asm volatile("" : "+v"(u0), "+v"(u1));
+  const b2 e0 = __builtin_bit_cast(b2, u0), e1 = __builtin_bit_cast(b2, u1);
+  const int slot = ((w + 2 * a) & 7) * 2;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    // key slice two ahead (of this block or the next) into the fetch buffer slice nt emptied
+    if (nt + 2 < NT) kstage_fetch<T, D, NL>(raw[nt & 1], Kh, J * B + 16 * (nt + 2), kvalid, lane);
+    else if (has_next) kstage_fetch<T, D, NL>(raw[nt & 1], Kh, Jn * B + 16 * (nt + 2 - NT), kvalid, lane);
+    // a part of the previous block's tile goes out after the key loads, so no wait on a key
+    // slice ever covers these stores (one counter, completed in issue order)
+    if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT);
+    int kq = 0, rl = 0;
+    if (MASKED) {
+      // per-slice mask bases, pinned here so the compares are not hoisted out of the loop
+      kq = J * B + 16 * nt + c - qdiag - 4 * a;       // key - (first row of the lane's rows)
+      rl = rows - 4 * a;
+      asm volatile("" : "+v"(kq), "+v"(rl));
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const v4f sc = dot_tile<D>(qf[mt], kf, zero4());
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
+        if (MASKED) p[i] = (16 * mt + i < rl && kq <= 16 * mt + i) ? p[i] : 0.f;
+      }
+      // rows 4a+i and 4a+i+1 of key 16nt+c: one packed conversion, each row's stored value
+      // added to its sum with a bf16 dot2 against a unit vector
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        const f2 v2 = {p[i], p[i + 1]};
+        const b2 pk = __builtin_convertvector(v2, b2);
+        rs[mt][i] = __builtin_amdgcn_fdot2_f32_bf16(pk, e0, rs[mt][i], false);
+        rs[mt][i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, e1, rs[mt][i + 1], false);
+        const int r = 16 * mt + 4 * a + i;
+        unsigned char* rec = tile + (r * B + 16 * nt + c) * 16 + slot;
+        *reinterpret_cast<__bf16*>(rec) = pk[0];
+        *reinterpret_cast<__bf16*>(rec + B * 16) = pk[1];
+      }
+    }
+    // next slice (fetched two slices ago) into MFMA operand layout
+    if (nt + 1 < NT || has_next) {
+      kstage_put<T, D, NL>(kst, raw[(nt + 1) & 1], lane);
+      kstage_get<D>(kf, kst, a, c);
+    }
+  }
+}
+
+template <typename T, int B, int D>
+struct GatherLds {
+  static constexpr int kTile = B * B * 16;                               // 8-head records of a block
+  static constexpr int kStage = 8 * KStage<T, D>::kSliceBytes;           // per-wave key stages
+  static constexpr int kBufs = 2 * kTile + kStage <= 160 * 1024 ? 2 : 1;
+};
+
 template <typename T, int B, int D>
 __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
                                                 int H_s, int64_t T_tot,
@@ -387,10 +538,16 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
                                                 int64_t capacity, const float* __restrict__ lse2,
                                                 float scale2, uint16_t* __restrict__ probs,
                                                 float* __restrict__ part) {
-  constexpr int MT = B / 16;                       // 16-row tiles
-  constexpr int NT = B / 16;                       // 16-key tiles
-  constexpr int TILE = B * B * 16;                 // bytes of one block's 8-head records
-  __shared__ __attribute__((aligned(16))) unsigned char s_out[2][TILE];
+  constexpr int MT = B / 16;
+  using L = GatherLds<T, B, D>;
+  constexpr int TILE = L::kTile;
+  constexpr int NBUF = L::kBufs;
+  constexpr int SB = KStage<T, D>::kSliceBytes;
+  constexpr int NL = KStage<T, D>::kLoads;
+  constexpr int PIECES = TILE / 16 / 512;
+  static_assert(PIECES >= 1 && (TILE / 16) % 512 == 0, "tile must split evenly over 512 threads");
+  __shared__ __attribute__((aligned(16))) unsigned char s_out[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) unsigned char s_k[8][SB];
 
   const int HG = (H_s + 7) >> 3;
   const int hg = blockIdx.x / n_brow;
@@ -398,7 +555,7 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
   const BrowInfo bi = load_info(info, brow);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int rows = min(B, bi.n - bi.I * B);
-  const int qloc0 = bi.I * B;
+  const int qdiag = bi.I * B;
   const int h = 8 * hg + w;
   const bool active = h < H_s;                     // padding heads write zeros
   const int64_t nnzb = min((int64_t)counters[0], capacity);
@@ -420,47 +577,42 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     }
   }
   const T* Kh = K + (size_t)hq * T_tot * D + (size_t)bi.seq0 * D;
-  auto load_k = [&](Frag<T, D>& f, int J, int nt) {
-    const int key = J * B + 16 * nt + c;
-    f.load(Kh + (size_t)key * D, active && key < bi.n, a);
-  };
+  const int kvalid = active ? bi.n : 0;            // keys at or beyond it load as zeros
+  unsigned char* kst = s_k[w];
 
-  Frag<T, D> kf, kn;
-  load_k(kf, block_idx[t0], 0);
+  // software pipeline over the row's key slices: frag(s) in kf, slices s+1 and s+2 in flight
+  Frag<T, D> kf;
+  v4u raw[2][NL];
+  {
+    constexpr int NT = B / 16;
+    const int J0 = block_idx[t0];
+    kstage_fetch<T, D, NL>(raw[0], Kh, J0 * B, kvalid, lane);
+    if (NT > 1) kstage_fetch<T, D, NL>(raw[1], Kh, J0 * B + 16, kvalid, lane);
+    kstage_put<T, D, NL>(kst, raw[0], lane);
+    kstage_get<D>(kf, kst, a, c);
+  }
   for (int t = t0; t < t1; ++t) {
     const int J = block_idx[t];
-    const int Jn = t + 1 < t1 ? block_idx[t + 1] : J;
-    const bool masked = J == bi.I || rows < B;
-    unsigned char* tile = s_out[(t - t0) & 1];
+    const bool has_next = t + 1 < t1;
+    const int Jn = has_next ? block_idx[t + 1] : J;
+    unsigned char* tile = s_out[(t - t0) % NBUF];
     float rs[MT][4];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      // next key slice (of this block, or the first of the next block) in flight
-      if (nt + 1 < NT) load_k(kn, J, nt + 1);
-      else if (t + 1 < t1) load_k(kn, Jn, 0);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const v4f sc = dot_tile<D>(qf[mt], kf, zero4());
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * a + i;
-          float p = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
-          if (masked) {
-            const int key = J * B + 16 * nt + c;
-            p = (r < rows && key <= qloc0 + r) ? p : 0.f;
-          }
-          if (!active) p = 0.f;
-          const __bf16 pb = (__bf16)p;
-          rs[mt][i] += (float)pb;
-          *reinterpret_cast<__bf16*>(tile + ((r * B + 16 * nt + c) * 8 + w) * 2) = pb;
-        }
-      }
-      kf = kn;
-    }
+    // with two tile buffers the previous block's tile is streamed during this block
+    const bool overlap = NBUF == 2 && t > t0;
+    const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
+    unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
+    if (!active || J == bi.I || rows < B)
+      gather_block<T, B, D, true, KStage<T, D>::kLoads>(qf, l2, kf, raw, kst, Kh, J, Jn, has_next, kvalid,
+                                                         active ? rows : 0, qdiag, scale2, tile, w, lane, a,
+                                                         c, rs, prev, prev_dst);
+    else
+      gather_block<T, B, D, false, KStage<T, D>::kLoads>(qf, l2, kf, raw, kst, Kh, J, Jn, has_next, kvalid,
+                                                          rows, qdiag, scale2, tile, w, lane, a, c, rs, prev,
+                                                          prev_dst);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -469,14 +621,14 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
         if (c == 0 && active) part[((size_t)t * H_s + h) * B + 16 * mt + 4 * a + i] = v;
       }
     __syncthreads();
-    // stream the finished tile: contiguous 16-byte pieces
-    unsigned char* dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE;
-#pragma unroll
-    for (int u = 0; u < TILE / 16 / 512; ++u) {
-      const int piece = threadIdx.x + u * 512;
-      st16(dst + (size_t)piece * 16, *reinterpret_cast<const v4u*>(tile + piece * 16));
+    if (NBUF == 1) {                               // single buffer: stream now, then reuse
+      stream_tile<B>(tile, reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE, 0, 1);
+      __syncthreads();
     }
   }
+  if (NBUF == 2)                                   // the last block's tile
+    stream_tile<B>(s_out[(t1 - 1 - t0) % NBUF],
+                   reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1);
 }
 
 // ------------------------------------------------------------------------------------------
