@@ -25,6 +25,8 @@ FLAGS = [
     "-Wno-unused-result", "-Wno-unknown-pragmas",
     # packed fp32 VALU forms stay disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no copies through the accumulation registers)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

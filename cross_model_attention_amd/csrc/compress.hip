@@ -83,12 +83,57 @@ __device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned 
 // tile is staged in LDS (double buffered, next tile fetched while the current one is used),
 // scores are formed transposed (keys x queries) on MFMA, and for every (query i, key block J)
 // the block-local maximum r_iJ and z_iJ = sum_{j in J} 2^(s_ij c - r_iJ) are stored (c folds
-// log2(e) / sqrt(d)).  A finalisation then gives, exactly as a softmax over the row would,
+// log2(e) / sqrt(d)), and keeps the running row logsumexp (fp64) of its query.  Exactly as a
+// softmax over the row would:
 //     lse2_i   = log2 sum_J z_iJ 2^(r_iJ)                       (row logsumexp, base 2)
 //     M_h[I,J] = sum_{i in I} z_iJ 2^(r_iJ - lse2_i)            (block mass of head h)
-// with fp64 accumulation in fixed order: one exponential per score instead of two, and one
-// score pass instead of two.
+// the second sum in fp64, one coalesced read of the stored pairs per block and wave: one
+// exponential per score instead of two, and one score pass instead of two.
 // ------------------------------------------------------------------------------------------
+// max / sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), result in every
+// lane: the gfx950 row-swap permutes exchange halves and row pairs without going through LDS
+__device__ __forceinline__ float xrow_max(float v) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
+// Statistics of one (query, key block) pair from the transposed score tiles s[mt] (lane (a, c):
+// keys 16 mt + 4 a + i of the block, query c): block maximum r (scaled, base 2) and
+// z = sum_j 2^(s_j c - r).  MASKED: keys with (key - query) > 0 are invisible, as is every key of
+// a query beyond the sequence; kq = first key of the lane minus the query.
+template <int MT, bool MASKED>
+__device__ __forceinline__ float2 block_stats(v4f (&s)[MT], int kq, bool qvalid, float scale2) {
+  if (MASKED) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!(qvalid && kq + 16 * mt + i <= 0)) s[mt][i] = kNegInf;
+  }
+  float bm = kNegInf;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    bm = __builtin_fmaxf(bm, __builtin_fmaxf(__builtin_fmaxf(s[mt][0], s[mt][1]), __builtin_fmaxf(s[mt][2], s[mt][3])));
+  bm = xrow_max(bm);
+  const bool none = MASKED && bm == kNegInf;            // nothing visible: z = 0
+  const float r = none ? 0.f : bm * scale2;
+  float z = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z += fast_exp2(fmaf(s[mt][i], scale2, -r));
+  z = xrow_sum(z);
+  return make_float2(z, none ? kNegInf : r);
+}
+
 template <typename T, int B, int D>
 __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
                                                  int H_s, int64_t T_tot,
@@ -123,8 +168,8 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
   Frag<T, D> qf;
   qf.load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qrow) * D, qrow < rows, a);
 
-  v4u kst[CPT];
-  auto fetch_k = [&](int J) {
+  // key tiles: registers -> LDS, fetched two blocks ahead (LDS double buffered)
+  auto fetch_k = [&](v4u (&kst)[CPT], int J) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int piece = threadIdx.x + u * NTHR;
@@ -133,7 +178,7 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
       kst[u] = key < bi.n ? ld16(Kh + (size_t)key * D * sizeof(T) + col * 16) : zero_u4();
     }
   };
-  auto stage_k = [&](int buf) {
+  auto stage_k = [&](const v4u (&kst)[CPT], int buf) {
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int piece = threadIdx.x + u * NTHR;
@@ -141,11 +186,11 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
     }
   };
 
-  fetch_k(0);
-  stage_k(0);
-  __syncthreads();
-  for (int J = 0; J <= bi.I; ++J) {
-    if (J < bi.I) fetch_k(J + 1);
+  // running base-2 logsumexp of this lane's query (every row a of the wave holds the same one)
+  float m_run = kNegInf;
+  double l_run = 0.0;
+  auto block = [&](int J, v4u (&fill)[CPT], const v4u (&next)[CPT]) {
+    if (J + 2 <= bi.I) fetch_k(fill, J + 2);
     const unsigned char* kt = s_k[J & 1];
     v4f s[MT];
 #pragma unroll
@@ -154,59 +199,42 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
       load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
       s[mt] = dot_tile<D>(kf, qf, zero4());
     }
-    const bool masked = J == bi.I || partial;
-    if (masked) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = J * B + 16 * mt + 4 * a + i;
-          if (!(key <= qloc && qloc < bi.n)) s[mt][i] = kNegInf;
-        }
+    // only the diagonal block and blocks of a partial row need the causal / length mask
+    const float2 zr = (J == bi.I || partial) ? block_stats<MT, true>(s, J * B + 4 * a - qloc, qloc < bi.n, scale2)
+                                             : block_stats<MT, false>(s, 0, true, scale2);
+    if (a == 0) zrow[(size_t)J * B + qrow] = zr;
+    if (zr.x > 0.f) {
+      const float mn = __builtin_fmaxf(m_run, zr.y);
+      l_run = l_run * (double)fast_exp2(m_run - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
+      m_run = mn;
     }
-    float bm = kNegInf;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      bm = fmaxf(bm, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, 64));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
-    const float r = bm == kNegInf ? 0.f : bm * scale2;     // nothing visible: z = 0
-    float z = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z += fast_exp2(fmaf(s[mt][i], scale2, -r));
-    z += __shfl_xor(z, 16, 64);
-    z += __shfl_xor(z, 32, 64);
-    if (a == 0) zrow[(size_t)J * B + qrow] = make_float2(z, bm == kNegInf ? kNegInf : r);
-    if (J < bi.I) stage_k((J + 1) & 1);
+    if (J + 1 <= bi.I) stage_k(next, (J + 1) & 1);
     __syncthreads();
+  };
+  v4u k0[CPT], k1[CPT];
+  fetch_k(k0, 0);
+  if (bi.I >= 1) fetch_k(k1, 1);
+  stage_k(k0, 0);
+  __syncthreads();
+  for (int J = 0; J <= bi.I; J += 2) {
+    block(J, k0, k1);
+    if (J + 1 <= bi.I) block(J + 1, k1, k0);
   }
 
-  // ---- finalisation: row logsumexp, then block masses -------------------------------------
-  if (threadIdx.x < B) {
-    const int q = threadIdx.x;
-    float M = kNegInf;
-    for (int J = 0; J <= bi.I; ++J) M = fmaxf(M, zrow[(size_t)J * B + q].y);
-    double L = 0.0;
-    for (int J = 0; J <= bi.I; ++J) {
-      const float2 e = zrow[(size_t)J * B + q];
-      if (e.y > kNegInf) L += (double)e.x * (double)fast_exp2(e.y - M);
-    }
-    const float v = (float)((double)M + log2(L));
-    s_lse[q] = v;
-    if (q < rows) lse2[(size_t)h * T_tot + bi.tok0 + q] = v;
+  // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
+  if (a == 0) {
+    const float v = (float)((double)m_run + log2(l_run));
+    s_lse[qrow] = v;
+    if (qrow < rows) lse2[(size_t)h * T_tot + bi.tok0 + qrow] = v;
   }
   __syncthreads();
   float* out = Mh + ((size_t)h * n_brow + brow) * nb_max;
-  for (int J = threadIdx.x; J <= bi.I; J += blockDim.x) {
-    const float2* zr = zrow + (size_t)J * B;
-    double t = 0.0;
-    for (int q = 0; q < rows; ++q) {
-      const float2 e = zr[q];
-      if (e.y > kNegInf) t += (double)e.x * (double)fast_exp2(e.y - s_lse[q]);
-    }
-    out[J] = (float)t;
+  const float lq = lane < rows ? s_lse[lane] : 0.f;
+  for (int J = w; J <= bi.I; J += NW) {
+    const float2 e = lane < B ? zrow[(size_t)J * B + lane] : make_float2(0.f, kNegInf);
+    const double v = (lane < rows && e.y > kNegInf) ? (double)e.x * (double)fast_exp2(e.y - lq) : 0.0;
+    const double t = wave_sum_f64(v);
+    if (lane == 0) out[J] = (float)t;
   }
 }
 
