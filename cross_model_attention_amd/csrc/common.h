@@ -92,6 +92,21 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// max / sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), result in every
+// lane: the gfx950 row-swap permutes exchange halves and row pairs without going through LDS
+__device__ __forceinline__ float xrow_max(float v) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float xrow_sum(float v) {
+  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // fp64 sum over the wave: rows by DPP on both 32-bit halves, then rows 0..3 added in order;
 // uniform result.
 template <int CTRL>

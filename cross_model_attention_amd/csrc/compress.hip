@@ -90,21 +90,6 @@ __device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned 
 // the second sum in fp64, one coalesced read of the stored pairs per block and wave: one
 // exponential per score instead of two, and one score pass instead of two.
 // ------------------------------------------------------------------------------------------
-// max / sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), result in every
-// lane: the gfx950 row-swap permutes exchange halves and row pairs without going through LDS
-__device__ __forceinline__ float xrow_max(float v) {
-  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
-  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-__device__ __forceinline__ float xrow_sum(float v) {
-  auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
-}
-
 // Statistics of one (query, key block) pair from the transposed score tiles s[mt] (lane (a, c):
 // keys 16 mt + 4 a + i of the block, query c): block maximum r (scaled, base 2) and
 // z = sum_j 2^(s_j c - r).  MASKED: keys with (key - query) > 0 are invisible, as is every key of
