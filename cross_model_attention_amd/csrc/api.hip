@@ -48,7 +48,9 @@ struct Geometry {
   std::vector<int32_t> order;     // block rows by descending in-sequence index
   std::vector<int32_t> brow_seq;  // [n_brow]
   std::vector<int32_t> coff;      // [n_brow] causal blocks of all earlier block rows
+  std::vector<int32_t> pairs;     // [n_pair][2] block rows (I, I+1) of one sequence (-1: none)
   std::vector<int32_t> cu;        // copy of cu_seqlens
+  int n_pair = 0;
 };
 
 mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& g) {
@@ -82,6 +84,17 @@ mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& 
   std::stable_sort(g.order.begin(), g.order.end(), [&](int x, int y) {
     return g.info[4 * x + 3] > g.info[4 * y + 3];
   });
+  // pairs of consecutive block rows of one sequence, the one with the larger row first
+  std::vector<std::pair<int, int>> pr;
+  for (int b = 0; b < g.n_brow; ++b) {
+    if (g.info[4 * b + 3] % 2 != 0) continue;
+    const bool has_next = b + 1 < g.n_brow && g.brow_seq[b + 1] == g.brow_seq[b];
+    pr.emplace_back(b, has_next ? b + 1 : -1);
+  }
+  auto top = [&](const std::pair<int, int>& x) { return g.info[4 * (x.second >= 0 ? x.second : x.first) + 3]; };
+  std::stable_sort(pr.begin(), pr.end(), [&](const auto& x, const auto& y) { return top(x) > top(y); });
+  g.n_pair = (int)pr.size();
+  for (const auto& x : pr) g.pairs.insert(g.pairs.end(), {x.first, x.second});
   if (g.n_causal >= (int64_t)INT32_MAX)
     return fail(MF_ERR_UNSUPPORTED, "more than 2^31 causal blocks (%lld)", (long long)g.n_causal);
   return MF_OK;
@@ -117,6 +130,7 @@ mf_status ensure(Scratch& s, size_t bytes, const char* what) {
 struct BsrOwner {
   void* meta = nullptr;
   void* data = nullptr;
+  int32_t* pairs = nullptr;       // device copy of geom.pairs (inside meta)
   Geometry geom;
 };
 
@@ -166,7 +180,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   const size_t o_ptr = align_up(o_coff + (size_t)g.n_brow * 4, 256);
   const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
   const size_t o_cnt = align_up(o_rkm + (size_t)H_s * g.T * 4, 256);
-  const size_t total = o_cnt + 256;
+  const size_t o_pairs = o_cnt + 256;
+  const size_t total = align_up(o_pairs + (size_t)g.n_pair * 8, 256) + 256;
   if (hipMalloc(&own->meta, total) != hipSuccess) {
     (void)hipGetLastError();
     own->meta = nullptr;
@@ -179,6 +194,7 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   out->block_ptr = reinterpret_cast<int32_t*>(base + o_ptr);
   out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
   out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
+  own->pairs = reinterpret_cast<int32_t*>(base + o_pairs);
   hipError_t e = hipSuccess;
   if (g.n_brow > 0) {
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
@@ -186,6 +202,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
       e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
       e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess && g.n_pair > 0)
+      e = hipMemcpy(own->pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipMemset(out->block_ptr, 0, (size_t)(g.n_brow + 1) * 4);
   if (e == hipSuccess) e = hipMemset(out->counters, 0, 256);
@@ -259,6 +277,8 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.info = bsr->brow_info;
   a.order = bsr->brow_order;
   a.coff = bsr->brow_coff;
+  a.pairs = static_cast<const BsrOwner*>(bsr->_owner)->pairs;
+  a.n_pair = static_cast<const BsrOwner*>(bsr->_owner)->geom.n_pair;
   a.n_causal = bsr->n_causal;
   a.tau = (double)tau;
   a.scale2 = (float)(1.4426950408889634 / std::sqrt((double)d));

@@ -78,13 +78,14 @@ __device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned 
 
 
 // ------------------------------------------------------------------------------------------
-// k_stats: one workgroup per (block row, sender head), B/16 waves; wave w owns queries
-// 16w..16w+15 and all B keys of each key block.  One pass over the key blocks: each block's key
-// tile is staged in LDS (double buffered, next tile fetched while the current one is used),
-// scores are formed transposed (keys x queries) on MFMA, and for every (query i, key block J)
-// the block-local maximum r_iJ and z_iJ = sum_{j in J} 2^(s_ij c - r_iJ) are stored (c folds
-// log2(e) / sqrt(d)), and keeps the running row logsumexp (fp64) of its query.  Exactly as a
-// softmax over the row would:
+// k_stats: one workgroup per (pair of consecutive block rows I, I+1 of one sequence, sender
+// head), 2 B/32 waves; the waves of each row own 32 of its queries (two 16-query tiles), so each
+// key fragment read from LDS serves 32 queries, and each key tile staged in LDS serves both rows.
+// One pass over the key blocks 0..I+1: each block's key tile is staged in LDS (fetched two
+// blocks ahead, double buffered), scores are formed transposed (keys x queries) on MFMA, and for
+// every (query i, key block J) the block-local maximum r_iJ and z_iJ = sum_{j in J} 2^(s_ij c -
+// r_iJ) are stored (c folds log2(e) / sqrt(d)), while each lane keeps the running row logsumexp
+// (fp64) of its queries.  Exactly as a softmax over the row would:
 //     lse2_i   = log2 sum_J z_iJ 2^(r_iJ)                       (row logsumexp, base 2)
 //     M_h[I,J] = sum_{i in I} z_iJ 2^(r_iJ - lse2_i)            (block mass of head h)
 // the second sum in fp64, one coalesced read of the stored pairs per block and wave: one
@@ -123,35 +124,44 @@ template <typename T, int B, int D>
 __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
                                                  int H_s, int64_t T_tot,
                                                  const int32_t* __restrict__ info,
-                                                 const int32_t* __restrict__ order,
+                                                 const int32_t* __restrict__ pairs, int n_pair,
                                                  const int32_t* __restrict__ coff, int64_t n_causal,
                                                  int n_brow, int nb_max, float scale2,
                                                  float2* __restrict__ zbuf,
                                                  float* __restrict__ lse2,
                                                  float* __restrict__ Mh) {
-  constexpr int NW = B / 16;
+  constexpr int WR = B / 32;                               // waves per block row
   constexpr int MT = B / 16;                               // 16-key tiles per block
+  constexpr int QT = 2;                                    // 16-query tiles per wave
   constexpr int NTHR = B * 4;
   constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
   constexpr int CPR = D * (int)sizeof(T) / 16;
   constexpr int CPT = B * CPR / NTHR;
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
-  __shared__ float s_lse[B];
+  __shared__ float s_lse[2][B];
 
   // head-major grid: the key rows of the few heads in flight stay cache resident
-  const int h = blockIdx.x / n_brow;
-  const int brow = order[blockIdx.x % n_brow];
-  const BrowInfo bi = load_info(info, brow);
+  const int h = blockIdx.x / n_pair;
+  const int pr = blockIdx.x % n_pair;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
-  const int rows = min(B, bi.n - bi.I * B);
+  const int side = w / WR;                                 // 0: row I, 1: row I+1
+  const int brow = pairs[2 * pr + side];                   // -1: the pair has one row
+  const BrowInfo b0 = load_info(info, pairs[2 * pr]);
+  const int Jend = pairs[2 * pr + 1] >= 0 ? b0.I + 1 : b0.I;  // last key block of the sweep
+  const bool mine = brow >= 0;
+  const BrowInfo bi = mine ? load_info(info, brow) : b0;
+  const int rows = mine ? min(B, bi.n - bi.I * B) : 0;
   const bool partial = rows < B;
-  const int qrow = 16 * w + c;                             // this lane's query (column)
-  const int qloc = bi.I * B + qrow;
-  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)bi.seq0 * D);
-  float2* zrow = zbuf + ((size_t)h * n_causal + coff[brow]) * B;
+  const int q0 = 32 * (w % WR);                            // first query of this wave in its row
+  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)b0.seq0 * D);
+  float2* zrow = zbuf + ((size_t)h * n_causal + (mine ? coff[brow] : 0)) * B;
 
-  Frag<T, D> qf;
-  qf.load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qrow) * D, qrow < rows, a);
+  Frag<T, D> qf[QT];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int qr = q0 + 16 * qt + c;
+    qf[qt].load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qr) * D, qr < rows, a);
+  }
 
   // key tiles: registers -> LDS, fetched two blocks ahead (LDS double buffered)
   auto fetch_k = [&](v4u (&kst)[CPT], int J) {
@@ -160,7 +170,7 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
       const int piece = threadIdx.x + u * NTHR;
       const int row = piece / CPR, col = piece % CPR;
       const int key = J * B + row;
-      kst[u] = key < bi.n ? ld16(Kh + (size_t)key * D * sizeof(T) + col * 16) : zero_u4();
+      kst[u] = key < b0.n ? ld16(Kh + (size_t)key * D * sizeof(T) + col * 16) : zero_u4();
     }
   };
   auto stage_k = [&](const v4u (&kst)[CPT], int buf) {
@@ -171,51 +181,69 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
     }
   };
 
-  // running base-2 logsumexp of this lane's query (every row a of the wave holds the same one)
-  float m_run = kNegInf;
-  double l_run = 0.0;
-  auto block = [&](int J, v4u (&fill)[CPT], const v4u (&next)[CPT]) {
-    if (J + 2 <= bi.I) fetch_k(fill, J + 2);
-    const unsigned char* kt = s_k[J & 1];
-    v4f s[MT];
+  // running base-2 logsumexp of this lane's queries (every row a of the wave holds the same ones)
+  float m_run[QT];
+  double l_run[QT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      Frag<T, D> kf;
-      load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
-      s[mt] = dot_tile<D>(kf, qf, zero4());
+  for (int qt = 0; qt < QT; ++qt) {
+    m_run[qt] = kNegInf;
+    l_run[qt] = 0.0;
+  }
+  auto block = [&](int J, v4u (&fill)[CPT], const v4u (&next)[CPT]) {
+    if (J + 2 <= Jend) fetch_k(fill, J + 2);
+    if (mine && J <= bi.I) {
+      const unsigned char* kt = s_k[J & 1];
+      v4f s[QT][MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        Frag<T, D> kf;
+        load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt][mt] = dot_tile<D>(kf, qf[qt], zero4());
+      }
+      // only the diagonal block and blocks of a partial row need the causal / length mask
+      const bool masked = J == bi.I || partial;
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        const int qr = q0 + 16 * qt + c;
+        const int qloc = bi.I * B + qr;
+        const float2 zr = masked ? block_stats<MT, true>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
+                                 : block_stats<MT, false>(s[qt], 0, true, scale2);
+        if (a == 0) zrow[(size_t)J * B + qr] = zr;
+        if (zr.x > 0.f) {
+          const float mn = __builtin_fmaxf(m_run[qt], zr.y);
+          l_run[qt] = l_run[qt] * (double)fast_exp2(m_run[qt] - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
+          m_run[qt] = mn;
+        }
+      }
     }
-    // only the diagonal block and blocks of a partial row need the causal / length mask
-    const float2 zr = (J == bi.I || partial) ? block_stats<MT, true>(s, J * B + 4 * a - qloc, qloc < bi.n, scale2)
-                                             : block_stats<MT, false>(s, 0, true, scale2);
-    if (a == 0) zrow[(size_t)J * B + qrow] = zr;
-    if (zr.x > 0.f) {
-      const float mn = __builtin_fmaxf(m_run, zr.y);
-      l_run = l_run * (double)fast_exp2(m_run - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
-      m_run = mn;
-    }
-    if (J + 1 <= bi.I) stage_k(next, (J + 1) & 1);
+    if (J + 1 <= Jend) stage_k(next, (J + 1) & 1);
     __syncthreads();
   };
   v4u k0[CPT], k1[CPT];
   fetch_k(k0, 0);
-  if (bi.I >= 1) fetch_k(k1, 1);
+  if (Jend >= 1) fetch_k(k1, 1);
   stage_k(k0, 0);
   __syncthreads();
-  for (int J = 0; J <= bi.I; J += 2) {
+  for (int J = 0; J <= Jend; J += 2) {
     block(J, k0, k1);
-    if (J + 1 <= bi.I) block(J + 1, k1, k0);
+    if (J + 1 <= Jend) block(J + 1, k1, k0);
   }
-
   // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
-  if (a == 0) {
-    const float v = (float)((double)m_run + log2(l_run));
-    s_lse[qrow] = v;
-    if (qrow < rows) lse2[(size_t)h * T_tot + bi.tok0 + qrow] = v;
+  if (mine && a == 0) {
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+      const int qr = q0 + 16 * qt + c;
+      const float v = (float)((double)m_run[qt] + log2(l_run[qt]));
+      s_lse[side][qr] = v;
+      if (qr < rows) lse2[(size_t)h * T_tot + bi.tok0 + qr] = v;
+    }
   }
-  __syncthreads();
+  __syncthreads();                                         // every wave reaches it
+  if (!mine) return;
   float* out = Mh + ((size_t)h * n_brow + brow) * nb_max;
-  const float lq = lane < rows ? s_lse[lane] : 0.f;
-  for (int J = w; J <= bi.I; J += NW) {
+  const float lq = lane < rows ? s_lse[side][lane] : 0.f;
+  for (int J = w % WR; J <= bi.I; J += WR) {
     const float2 e = lane < B ? zrow[(size_t)J * B + lane] : make_float2(0.f, kNegInf);
     const double v = (lane < rows && e.y > kNegInf) ? (double)e.x * (double)fast_exp2(e.y - lq) : 0.0;
     const double t = wave_sum_f64(v);
@@ -470,8 +498,8 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
   }
 }
 
-template <typename T, int B, int D, bool MASKED, int NL>
-__device__ __forceinline__ void gather_block(const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16][4],
+template <typename T, int B, int D, int NL>
+__device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16][4],
                                              Frag<T, D>& kf, v4u (&raw)[2][NL],
                                              unsigned char* kst, const T* Kh, int J, int Jn, bool has_next,
                                              int kvalid, int rows, int qdiag, float scale2,
@@ -495,22 +523,21 @@ __device__ __forceinline__ void gather_block(const Frag<T, D> (&qf)[B / 16], con
     // a part of the previous block's tile goes out after the key loads, so no wait on a key
     // slice ever covers these stores (one counter, completed in issue order)
     if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT);
-    int kq = 0, rl = 0;
-    if (MASKED) {
-      // per-slice mask bases, pinned here so the compares are not hoisted out of the loop
-      kq = J * B + 16 * nt + c - qdiag - 4 * a;       // key - (first row of the lane's rows)
-      rl = rows - 4 * a;
-      asm volatile("" : "+v"(kq), "+v"(rl));
-    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const v4f sc = dot_tile<D>(qf[mt], kf, zero4());
+      v4f sc = dot_tile<D>(qf[mt], kf, zero4());
+      if (masked) {
+        // diagonal / partial blocks only: invisible keys and padding rows get -inf scores
+        int kq = J * B + 16 * nt + c - qdiag - 4 * a;  // key - (first row of the lane's rows)
+        int rl = rows - 4 * a;
+        asm volatile("" : "+v"(kq), "+v"(rl));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(16 * mt + i < rl && kq <= 16 * mt + i)) sc[i] = -__builtin_inff();
+      }
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[i] = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
-        if (MASKED) p[i] = (16 * mt + i < rl && kq <= 16 * mt + i) ? p[i] : 0.f;
-      }
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
       // rows 4a+i and 4a+i+1 of key 16nt+c: one packed conversion, each row's stored value
       // added to its sum with a bf16 dot2 against a unit vector
 #pragma unroll
@@ -618,14 +645,9 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     const bool overlap = NBUF == 2 && t > t0;
     const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
-    if (!active || J == bi.I || rows < B)
-      gather_block<T, B, D, true, KStage<T, D>::kLoads>(qf, l2, kf, raw, kst, Kh, J, Jn, has_next, kvalid,
-                                                         active ? rows : 0, qdiag, scale2, tile, w, lane, a,
-                                                         c, rs, prev, prev_dst);
-    else
-      gather_block<T, B, D, false, KStage<T, D>::kLoads>(qf, l2, kf, raw, kst, Kh, J, Jn, has_next, kvalid,
-                                                          rows, qdiag, scale2, tile, w, lane, a, c, rs, prev,
-                                                          prev_dst);
+    gather_block<T, B, D, NL>(!active || J == bi.I || rows < B, qf, l2, kf, raw, kst, Kh, J, Jn, has_next,
+                              kvalid, active ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev,
+                              prev_dst);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -669,9 +691,9 @@ bool compress_supported(int dtype, int B, int d) {
 
 template <typename T, int B, int D>
 static hipError_t plan_t(const CompressArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_brow * a.H_s), dim3(B * 4), 0, s,
-                     (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.order, a.coff, a.n_causal,
-                     a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh);
+  hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_pair * a.H_s), dim3(B * 4), 0, s,
+                     (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.pairs, a.n_pair, a.coff,
+                     a.n_causal, a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh);
   return hipGetLastError();
 }
 

@@ -17,6 +17,8 @@ struct CompressArgs {
   const int32_t* info;   // [n_brow][4]
   const int32_t* order;  // [n_brow]
   const int32_t* coff;   // [n_brow] causal block offset of each block row
+  const int32_t* pairs;  // [n_pair][2] block rows (I, I+1) of one sequence, second may be -1
+  int n_pair;
   int64_t n_causal;
   double tau;
   float scale2;          // log2(e) / sqrt(d)
