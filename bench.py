@@ -43,7 +43,7 @@ def parse():
     p.add_argument("--slots", type=int, default=3, help="device block stores in the compress ring")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=8, help="block rows in the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=16, help="block rows in the oracle sample")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
                    help="size of the HBM copy probe run after the timed steps (0 = skip)")
     return p.parse_args()
