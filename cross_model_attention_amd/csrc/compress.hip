@@ -121,7 +121,7 @@ __device__ __forceinline__ float2 block_stats(v4f (&s)[MT], int kq, bool qvalid,
 }
 
 template <typename T, int B, int D>
-__global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
                                                  int H_s, int64_t T_tot,
                                                  const int32_t* __restrict__ info,
                                                  const int32_t* __restrict__ pairs, int n_pair,
@@ -189,8 +189,9 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
     m_run[qt] = kNegInf;
     l_run[qt] = 0.0;
   }
-  auto block = [&](int J, v4u (&fill)[CPT], const v4u (&next)[CPT]) {
-    if (J + 2 <= Jend) fetch_k(fill, J + 2);
+  v4u kst[CPT];
+  auto block = [&](int J) {
+    if (J + 1 <= Jend) fetch_k(kst, J + 1);
     if (mine && J <= bi.I) {
       const unsigned char* kt = s_k[J & 1];
       v4f s[QT][MT];
@@ -217,18 +218,13 @@ __global__ __launch_bounds__(B * 4) void k_stats(const T* __restrict__ Q, const 
         }
       }
     }
-    if (J + 1 <= Jend) stage_k(next, (J + 1) & 1);
+    if (J + 1 <= Jend) stage_k(kst, (J + 1) & 1);
     __syncthreads();
   };
-  v4u k0[CPT], k1[CPT];
-  fetch_k(k0, 0);
-  if (Jend >= 1) fetch_k(k1, 1);
-  stage_k(k0, 0);
+  fetch_k(kst, 0);
+  stage_k(kst, 0);
   __syncthreads();
-  for (int J = 0; J <= Jend; J += 2) {
-    block(J, k0, k1);
-    if (J + 1 <= Jend) block(J + 1, k1, k0);
-  }
+  for (int J = 0; J <= Jend; ++J) block(J);
   // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
   if (mine && a == 0) {
 #pragma unroll
