@@ -148,7 +148,7 @@ struct VfragOwner {
 
 struct mf_ctx {
   int device = 0;
-  Scratch lse2, Mh, M, flags, counts, part, zbuf;
+  Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
   // cached device copies of the dense-attention geometry
@@ -264,6 +264,9 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
   if ((st = ensure(ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts")) != MF_OK) return st;
   if ((st = ensure(ctx->part, (size_t)capacity * bsr->H_s * bsr->B * 4 + 256, "row sums")) != MF_OK) return st;
+  const size_t elem = dtype == MF_BF16 ? 2 : 4;
+  if ((st = ensure(ctx->ktile, (size_t)bsr->H_s * bsr->n_brow * bsr->B * d * elem + 256, "key operand tiles")) != MF_OK)
+    return st;
   a = mf::CompressArgs{};
   a.Q = Q;
   a.K = K;
@@ -289,6 +292,7 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.flags = static_cast<uint8_t*>(ctx->flags.p);
   a.counts = static_cast<int32_t*>(ctx->counts.p);
   a.part = static_cast<float*>(ctx->part.p);
+  a.ktile = ctx->ktile.p;
   a.block_ptr = bsr->block_ptr;
   a.block_idx = bsr->block_idx;
   a.block_row = bsr->block_row;
@@ -452,7 +456,7 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
   if (!ctx) return MF_OK;
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
-  for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf,
+  for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf, &ctx->ktile,
                      &ctx->dense_tables})
     if (s->p) (void)hipFree(s->p);
   vfrag_release(&ctx->vf_retrieve);

@@ -403,14 +403,14 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 }
 
 // ------------------------------------------------------------------------------------------
-// k_gather: one workgroup per (block row, group of 8 sender heads), 8 waves; wave w owns sender
-// head 8*hg + w and keeps that head's query rows of the block row in registers for the whole
-// row.  It sweeps the row's kept blocks in column order; per block and 16-key slice:
-//   * the slice's keys are fetched with fully coalesced 16-byte loads (each load instruction reads
-//     1 KiB of contiguous key rows) two slices ahead, and passed through a per-wave LDS stage into
-//     MFMA operand layout (16-byte chunks XOR-swizzled by row: conflict-free both ways).  Loading
-//     the operand layout straight from memory would touch 16 rows per instruction and make the
-//     vector L1 the bottleneck;
+// k_gather: one workgroup per (chunk of 16 kept blocks of a block row, group of 8 sender heads),
+// 8 waves; wave w owns sender head 8*hg + w and keeps that head's query rows of the block row in
+// registers.  Work items are ordered chunk-major, so the workgroups in flight share one range of
+// key blocks in L2.  Per kept block of the chunk, in column order, and 16-key slice:
+//   * the slice's key operands are loaded B/16 - 1 slices ahead from the key tiles written by
+//     k_ktile, already in MFMA fragment layout: each load instruction reads 1 KiB of contiguous
+//     memory (loading the fragments from the plain key rows would touch 16 rows per instruction
+//     and make the vector L1 the bottleneck);
 //   * scores are formed on MFMA and turned into bf16 probabilities exp(s - lse); a lane's values
 //     for two adjacent rows are converted as one packed pair, and each stored value is added to
 //     its row's sum with a bf16 dot2 against a unit vector (no unpacking);
@@ -422,54 +422,52 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 // that slice's key loads (LDS double buffered where it fits: one barrier per block).
 // The causal / partial-row mask is evaluated only on blocks that need it.
 // ------------------------------------------------------------------------------------------
+// Key operands in MFMA fragment layout.  For sender head h, block row kb (used as key block),
+// 16-key slice nt, fragment element k and lane l = (a, c): element k of Frag<T, D> for key
+// 16 nt + c of that block, i.e. K[h][key][32 k + 8 a .. +8] (bf16) or K[h][key][4 k + a] (fp32).
+// Every (slice, element) is one contiguous run over the 64 lanes, so the gather loads its
+// operands with fully coalesced loads straight into registers; keys beyond the sequence are 0.
 template <typename T, int D>
-struct KStage {
-  static constexpr int kRowBytes = D * (int)sizeof(T);
-  static constexpr int kChunks = kRowBytes / 16;               // 16-byte chunks per key row
-  static constexpr int kSliceBytes = 16 * kRowBytes;           // one 16-key slice
-  static constexpr int kLoads = kSliceBytes / 1024;            // 1 KiB coalesced loads per slice
-  static_assert(kSliceBytes % 1024 == 0, "slice must split into 1 KiB loads");
-  // byte offset of (row, chunk) inside the stage
-  __device__ static int at(int row, int chunk) { return row * kRowBytes + ((chunk ^ (row & (kChunks - 1))) << 4); }
+struct KTile {
+  static constexpr int kElems = Frag<T, D>::N;                                  // per lane and slice
+  static constexpr int kElemBytes = (int)sizeof(Frag<T, D>::v[0]);
+  static constexpr int kSliceBytes = kElems * 64 * kElemBytes;                  // = 16 keys x D
 };
 
-template <typename T, int D, int NL>
-__device__ __forceinline__ void kstage_fetch(v4u (&raw)[NL], const T* Kh, int key0, int kvalid, int lane) {
-  using S = KStage<T, D>;
-  static_assert(NL == S::kLoads, "load count");
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int piece = i * 64 + lane;
-    const int row = piece / S::kChunks, chunk = piece % S::kChunks;
-    const int key = key0 + row;
-    raw[i] = key < kvalid ? ld16(reinterpret_cast<const unsigned char*>(Kh + (size_t)key * D) + chunk * 16)
-                          : zero_u4();
-  }
-}
-
-template <typename T, int D, int NL>
-__device__ __forceinline__ void kstage_put(unsigned char* st, const v4u (&raw)[NL], int lane) {
-  using S = KStage<T, D>;
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int piece = i * 64 + lane;
-    *reinterpret_cast<v4u*>(st + S::at(piece / S::kChunks, piece % S::kChunks)) = raw[i];
+template <typename T, int B, int D>
+__global__ __launch_bounds__(256) void k_ktile(const T* __restrict__ K, int64_t T_tot, int n_brow,
+                                               const int32_t* __restrict__ info,
+                                               unsigned char* __restrict__ ktile) {
+  using KT = KTile<T, D>;
+  constexpr int NT = B / 16;
+  constexpr int PER = NT * KT::kElems * 64;                                     // elements per (h, kb)
+  const int kb = blockIdx.x, h = blockIdx.y;
+  const BrowInfo bi = load_info(info, kb);
+  unsigned char* dst = ktile + ((size_t)h * n_brow + kb) * NT * KT::kSliceBytes;
+  for (int e = threadIdx.x; e < PER; e += 256) {
+    const int lane = e & 63, k = (e >> 6) % KT::kElems, nt = (e >> 6) / KT::kElems;
+    const int a = lane >> 4, c = lane & 15;
+    const int key = bi.I * B + 16 * nt + c;
+    const T* row = K + ((size_t)h * T_tot + bi.seq0 + key) * D;
+    if constexpr (sizeof(T) == 2) {
+      const v4u x = key < bi.n ? ld16(row + 32 * k + 8 * a) : zero_u4();
+      *reinterpret_cast<v4u*>(dst + (size_t)e * 16) = x;
+    } else {
+      const float x = key < bi.n ? row[4 * k + a] : 0.f;
+      *reinterpret_cast<float*>(dst + (size_t)e * 4) = x;
+    }
   }
 }
 
 template <int D>
-__device__ __forceinline__ void kstage_get(Frag<uint16_t, D>& f, const unsigned char* st, int a, int c) {
-  using S = KStage<uint16_t, D>;
+__device__ __forceinline__ void ktile_load(Frag<uint16_t, D>& f, const unsigned char* slice, int lane) {
 #pragma unroll
-  for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
-    f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(st + S::at(c, 4 * k + a)));
+  for (int k = 0; k < Frag<uint16_t, D>::N; ++k) f.v[k] = as_v8s(ld16(slice + (k * 64 + lane) * 16));
 }
 template <int D>
-__device__ __forceinline__ void kstage_get(Frag<float, D>& f, const unsigned char* st, int a, int c) {
-  using S = KStage<float, D>;
+__device__ __forceinline__ void ktile_load(Frag<float, D>& f, const unsigned char* slice, int lane) {
 #pragma unroll
-  for (int k = 0; k < Frag<float, D>::N; ++k)
-    f.v[k] = *reinterpret_cast<const float*>(st + S::at(c, k) + 4 * a);
+  for (int k = 0; k < Frag<float, D>::N; ++k) f.v[k] = *reinterpret_cast<const float*>(slice + (k * 64 + lane) * 4);
 }
 
 // Stream part q of NQ of a finished 8-head record tile (B x B records of 16 bytes) to HBM with the
@@ -494,17 +492,16 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
   }
 }
 
-template <typename T, int B, int D, int NL>
+template <typename T, int B, int D>
 __device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16][4],
-                                             Frag<T, D>& kf, v4u (&raw)[2][NL],
-                                             unsigned char* kst, const T* Kh, int J, int Jn, bool has_next,
-                                             int kvalid, int rows, int qdiag, float scale2,
-                                             unsigned char* tile, int w, int lane, int a, int c,
-                                             float (&rs)[B / 16][4], const unsigned char* prev,
+                                             Frag<T, D> (&kb)[B / 16], const unsigned char* ktj,
+                                             const unsigned char* ktn, bool has_next, int J, int rows,
+                                             int qdiag, float scale2, unsigned char* tile, int w, int lane,
+                                             int a, int c, float (&rs)[B / 16][4], const unsigned char* prev,
                                              unsigned char* prev_dst) {
   constexpr int MT = B / 16;   // 16-row tiles
-  constexpr int NT = B / 16;   // 16-key slices
-  static_assert(NT % 2 == 0, "key slices alternate between the two fetch buffers");
+  constexpr int NT = B / 16;   // 16-key slices; slice nt lives in kb[nt]
+  constexpr int SB = KTile<T, D>::kSliceBytes;
   // unit vectors (1, 0) and (0, 1) in bf16, kept in registers: as inline constants the compiler
   // would encode 1.0, which the dot2 reads as the pair (0, 1)
   uint32_t u0 = 0x00003F80u, u1 = 0x3F800000u;
@@ -513,15 +510,16 @@ __device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)
   const int slot = ((w + 2 * a) & 7) * 2;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    // key slice two ahead (of this block or the next) into the fetch buffer slice nt emptied
-    if (nt + 2 < NT) kstage_fetch<T, D, NL>(raw[nt & 1], Kh, J * B + 16 * (nt + 2), kvalid, lane);
-    else if (has_next) kstage_fetch<T, D, NL>(raw[nt & 1], Kh, Jn * B + 16 * (nt + 2 - NT), kvalid, lane);
+    // the slice NT-1 ahead (the last of this block, or one of the next block's) into the
+    // register set slice nt-1 has finished with
+    if (nt == 0) ktile_load<D>(kb[NT - 1], ktj + (NT - 1) * SB, lane);
+    else if (has_next) ktile_load<D>(kb[nt - 1], ktn + (nt - 1) * SB, lane);
     // a part of the previous block's tile goes out after the key loads, so no wait on a key
     // slice ever covers these stores (one counter, completed in issue order)
     if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v4f sc = dot_tile<D>(qf[mt], kf, zero4());
+      v4f sc = dot_tile<D>(qf[mt], kb[nt], zero4());
       if (masked) {
         // diagonal / partial blocks only: invisible keys and padding rows get -inf scores
         int kq = J * B + 16 * nt + c - qdiag - 4 * a;  // key - (first row of the lane's rows)
@@ -548,19 +546,16 @@ __device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)
         *reinterpret_cast<__bf16*>(rec + B * 16) = pk[1];
       }
     }
-    // next slice (fetched two slices ago) into MFMA operand layout
-    if (nt + 1 < NT || has_next) {
-      kstage_put<T, D, NL>(kst, raw[(nt + 1) & 1], lane);
-      kstage_get<D>(kf, kst, a, c);
-    }
   }
 }
+
+// kept blocks per gather work item
+constexpr int kGatherChunk = 16;
 
 template <typename T, int B, int D>
 struct GatherLds {
   static constexpr int kTile = B * B * 16;                               // 8-head records of a block
-  static constexpr int kStage = 8 * KStage<T, D>::kSliceBytes;           // per-wave key stages
-  static constexpr int kBufs = 2 * kTile + kStage <= 160 * 1024 ? 2 : 1;
+  static constexpr int kBufs = 2;
 };
 
 template <typename T, int B, int D>
@@ -572,22 +567,26 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
                                                 const int32_t* __restrict__ block_idx,
                                                 const int32_t* __restrict__ counters,
                                                 int64_t capacity, const float* __restrict__ lse2,
-                                                float scale2, uint16_t* __restrict__ probs,
-                                                float* __restrict__ part) {
+                                                float scale2, const unsigned char* __restrict__ ktile,
+                                                uint16_t* __restrict__ probs, float* __restrict__ part) {
   constexpr int MT = B / 16;
+  constexpr int NT = B / 16;
   using L = GatherLds<T, B, D>;
   constexpr int TILE = L::kTile;
   constexpr int NBUF = L::kBufs;
-  constexpr int SB = KStage<T, D>::kSliceBytes;
-  constexpr int NL = KStage<T, D>::kLoads;
+  constexpr int SB = KTile<T, D>::kSliceBytes;
   constexpr int PIECES = TILE / 16 / 512;
   static_assert(PIECES >= 1 && (TILE / 16) % 512 == 0, "tile must split evenly over 512 threads");
   __shared__ __attribute__((aligned(16))) unsigned char s_out[NBUF][TILE];
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[8][SB];
 
+  // work item (chunk k of a block row's kept list, head group, block row in LPT order), chunk
+  // index slowest: the workgroups in flight sweep the same range of key blocks, whose tiles then
+  // stay in L2 for all of them
   const int HG = (H_s + 7) >> 3;
-  const int hg = blockIdx.x / n_brow;
-  const int brow = order[blockIdx.x % n_brow];
+  const int p = blockIdx.x % n_brow;
+  const int hg = (blockIdx.x / n_brow) % HG;
+  const int chunk = blockIdx.x / (n_brow * HG);
+  const int brow = order[p];
   const BrowInfo bi = load_info(info, brow);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int rows = min(B, bi.n - bi.I * B);
@@ -595,8 +594,9 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
   const int h = 8 * hg + w;
   const bool active = h < H_s;                     // padding heads write zeros
   const int64_t nnzb = min((int64_t)counters[0], capacity);
-  const int t0 = (int)min((int64_t)block_ptr[brow], nnzb);
-  const int t1 = (int)min((int64_t)block_ptr[brow + 1], nnzb);
+  const int64_t r0 = block_ptr[brow] + (int64_t)chunk * kGatherChunk;
+  const int t0 = (int)min(r0, nnzb);
+  const int t1 = (int)min(min((int64_t)block_ptr[brow + 1], r0 + kGatherChunk), nnzb);
   if (t0 >= t1) return;
 
   const int hq = active ? h : 0;
@@ -612,20 +612,18 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
       l2[mt][i] = (active && rr < rows) ? lse2[(size_t)hq * T_tot + bi.tok0 + rr] : 0.f;
     }
   }
-  const T* Kh = K + (size_t)hq * T_tot * D + (size_t)bi.seq0 * D;
-  const int kvalid = active ? bi.n : 0;            // keys at or beyond it load as zeros
-  unsigned char* kst = s_k[w];
+  // this head's key operand tiles; key block J of the sequence is block row kbrow0 + J
+  const int kbrow0 = brow - bi.I;
+  const unsigned char* kth = ktile + (size_t)hq * n_brow * NT * SB;
+  auto kt_block = [&](int J) { return kth + (size_t)(kbrow0 + J) * NT * SB; };
 
-  // software pipeline over the row's key slices: frag(s) in kf, slices s+1 and s+2 in flight
-  Frag<T, D> kf;
-  v4u raw[2][NL];
+  // software pipeline over the row's key slices: slice nt of a block lives in kb[nt]; the first
+  // NT-1 slices of the first block are requested here, every later slice NT-1 slices ahead
+  Frag<T, D> kb[NT];
   {
-    constexpr int NT = B / 16;
-    const int J0 = block_idx[t0];
-    kstage_fetch<T, D, NL>(raw[0], Kh, J0 * B, kvalid, lane);
-    if (NT > 1) kstage_fetch<T, D, NL>(raw[1], Kh, J0 * B + 16, kvalid, lane);
-    kstage_put<T, D, NL>(kst, raw[0], lane);
-    kstage_get<D>(kf, kst, a, c);
+    const unsigned char* k0 = kt_block(block_idx[t0]);
+#pragma unroll
+    for (int nt = 0; nt + 1 < NT; ++nt) ktile_load<D>(kb[nt], k0 + nt * SB, lane);
   }
   for (int t = t0; t < t1; ++t) {
     const int J = block_idx[t];
@@ -641,9 +639,8 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     const bool overlap = NBUF == 2 && t > t0;
     const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
-    gather_block<T, B, D, NL>(!active || J == bi.I || rows < B, qf, l2, kf, raw, kst, Kh, J, Jn, has_next,
-                              kvalid, active ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev,
-                              prev_dst);
+    gather_block<T, B, D>(!active || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next,
+                          J, active ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev, prev_dst);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -697,9 +694,11 @@ template <typename T, int B, int D>
 static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
   const int HG = (a.H_s + 7) / 8;
   if (a.capacity == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gather<T, B, D>), dim3((unsigned)a.n_brow * HG), dim3(512), 0, s, (const T*)a.Q,
+  const unsigned chunks = (unsigned)((a.nb_max + kGatherChunk - 1) / kGatherChunk);
+  hipLaunchKernelGGL((k_gather<T, B, D>), dim3((unsigned)a.n_brow * HG * chunks), dim3(512), 0, s, (const T*)a.Q,
                      (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.block_ptr, a.block_idx,
-                     a.counters, a.capacity, a.lse2, a.scale2, a.probs, a.part);
+                     a.counters, a.capacity, a.lse2, a.scale2, (const unsigned char*)a.ktile, a.probs,
+                     a.part);
   return hipGetLastError();
 }
 
@@ -719,12 +718,22 @@ static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;                                                  \
   } while (0)
 
+template <typename T, int B, int D>
+static hipError_t ktile_t(const CompressArgs& a, hipStream_t s) {
+  if (a.n_brow == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_ktile<T, B, D>), dim3((unsigned)a.n_brow, (unsigned)a.H_s), dim3(256), 0, s,
+                     (const T*)a.K, a.T, a.n_brow, a.info, (unsigned char*)a.ktile);
+  return hipGetLastError();
+}
+
 static hipError_t stats_dispatch(const CompressArgs& a, hipStream_t s) { MF_DISPATCH_QK(plan_t, a, s); }
+static hipError_t ktile_dispatch(const CompressArgs& a, hipStream_t s) { MF_DISPATCH_QK(ktile_t, a, s); }
 static hipError_t gather_dispatch(const CompressArgs& a, hipStream_t s) { MF_DISPATCH_QK(gather_t, a, s); }
 
 hipError_t compress_plan(const CompressArgs& a, hipStream_t s) {
-  hipError_t e = stats_dispatch(a, s);
+  hipError_t e = ktile_dispatch(a, s);
   if (e != hipSuccess) return e;
+  if ((e = stats_dispatch(a, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_head_reduce, dim3(a.n_brow), dim3(256), 0, s, a.Mh, a.H_s, a.n_brow,
                      a.nb_max, a.info, a.M);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -30,6 +30,7 @@ struct CompressArgs {
   uint8_t* flags;        // [n_brow][nb_max] kept flags
   int32_t* counts;       // [n_brow]
   float* part;           // [capacity][H_s][B] per-block row sums of stored probs
+  void* ktile;           // [H_s][n_brow][B/16][fragment elements][64 lanes] key operands
   // the store
   int32_t* block_ptr;
   int32_t* block_idx;
