@@ -198,7 +198,7 @@ struct AhatLayout {
 // the bf16 "lo" part of the scaled weights, accumulating into the same fp32 tile: Ws = hi + lo
 // keeps ~16 bits of W while the kept probabilities enter the MFMA exactly.  HP = ceil(H_r / 8)
 // is the number of receiver heads each of the 8 waves owns in stage 2.
-template <int B, int D, int HP, int KC>
+template <int B, int D, int HP, int KC, int NSPLIT>
 __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const uint16_t* __restrict__ probs, const int32_t* __restrict__ block_ptr,
     const int32_t* __restrict__ block_idx, const int32_t* __restrict__ info,
@@ -220,12 +220,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   __shared__ int s_sexp[HR_MAX];
   __shared__ v4u s_wop[NTG][KC][2][64];
 
-  // ---- work item: XCD-aware (the row tiles of one block row share an XCD) --------------------
+  // ---- work item: XCD-aware (the row tiles and head splits of one block row share an XCD, so
+  // a P tile read by both halves of a split comes from HBM once) ----------------------------
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int q = b >> 3;
   const int rt = q % NRT;
-  const int gidx = (q / NRT) * 8 + xcd;
+  const int split = (q / NRT) % NSPLIT;
+  const int gidx = (q / (NRT * NSPLIT)) * 8 + xcd;
   if (gidx >= n_brow) return;
   const int brow = order[gidx];
   const BrowInfo bi = load_info(info, brow);
@@ -235,15 +237,25 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   const int row0 = RT_ROWS * rt;              // first row of the tile within the block row
   const int HGp = (H_s + 7) >> 3;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
+  // this workgroup's receiver heads: slots split*HR_MAX + j (j = 0..HR_MAX-1) of the kv-sorted
+  // head list; mixed maps, weights and denominators are indexed by the local slot j
+  const int slot0 = split * HR_MAX;
+  __shared__ int s_head[HR_MAX];
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < HR_MAX; ++j) s_head[j] = slot0 + j < H_r ? (int)hm.perm[slot0 + j] : -1;
+  }
+  __syncthreads();
+  auto head_of = [&](int j) { return s_head[j]; };
 
   // ---- setup: per-head scale, scaled weights, denominators ---------------------------------
   // scaled weights (hi + lo, fp32) live in the second mixed-map buffer until the loop needs it
   static_assert(HR_MAX * 64 * sizeof(float) <= HR_MAX * GB, "weights fit in one Ahat buffer");
   float (*s_w)[64] = reinterpret_cast<float (*)[64]>(s_ahat[1]);
   if (threadIdx.x < HR_MAX) {
-    const int g = threadIdx.x;
+    const int g = head_of(threadIdx.x);
     int e = 0;
-    if (g < H_r) {
+    if (g >= 0) {
       float sa = 0.f;
       for (int h = 0; h < H_s; ++h) sa += fabsf(W[g * H_s + h]);
       if (sa > 0.f && sa < __builtin_inff()) {
@@ -252,27 +264,27 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
         e = max(-100, min(100, 15 - ex));
       }
     }
-    s_sexp[g] = e;
+    s_sexp[threadIdx.x] = e;
   }
   __syncthreads();
   for (int t = threadIdx.x; t < HR_MAX * 64; t += blockDim.x) {
-    const int g = t >> 6, h = t & 63;
+    const int j = t >> 6, h = t & 63, g = head_of(j);
     float v = 0.f;
-    if (g < H_r && h < H_s) {
-      const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
+    if (g >= 0 && h < H_s) {
+      const float x = ldexpf(W[g * H_s + h], s_sexp[j]);
       const float hi = bf16_to_f32(f32_to_bf16(x));
       const float lo = bf16_to_f32(f32_to_bf16(x - hi));
       v = hi + lo;
     }
-    s_w[g][h] = v;
+    s_w[j][h] = v;
   }
   __syncthreads();
   for (int t = threadIdx.x; t < HR_MAX * RT_ROWS; t += blockDim.x) {
-    const int g = t / RT_ROWS, i = t % RT_ROWS;
+    const int j = t / RT_ROWS, i = t % RT_ROWS;
     float den = 0.f;
-    if (g < H_r && i < rows)
-      for (int h = 0; h < H_s; ++h) den += s_w[g][h] * rkm[(size_t)h * T_tot + bi.tok0 + row0 + i];
-    s_den[g][i] = den;
+    if (head_of(j) >= 0 && i < rows)
+      for (int h = 0; h < H_s; ++h) den += s_w[j][h] * rkm[(size_t)h * T_tot + bi.tok0 + row0 + i];
+    s_den[j][i] = den;
   }
 
   // stage-1 B operands (weights of virtual heads, bf16 hi / lo, head dims 32kc + 8a + e), kept in
@@ -280,7 +292,8 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   if (w == 0) {
 #pragma unroll
     for (int nt = 0; nt < NTG; ++nt) {
-      const int g = 16 * nt + c;
+      const int jn = 16 * nt + c;
+      const int g = jn < HR_MAX ? head_of(jn) : -1;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -293,8 +306,8 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
             for (int q2 = 0; q2 < 2; ++q2) {
               const int h = 32 * kc + 8 * a + 2 * e2 + q2;
               uint32_t bits = 0;
-              if (g < H_r && h < H_s) {
-                const float x = ldexpf(W[g * H_s + h], s_sexp[g]);
+              if (g >= 0 && h < H_s) {
+                const float x = ldexpf(W[g * H_s + h], s_sexp[jn]);
                 const uint16_t hb = f32_to_bf16(x);
                 bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
               }
@@ -307,13 +320,10 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     }
   }
 
-  // stage-2 ownership: slots w*HP .. w*HP+HP-1 of the kv-sorted head list
+  // stage-2 ownership: local slots w*HP .. w*HP+HP-1
   int sg[HP];
 #pragma unroll
-  for (int j = 0; j < HP; ++j) {
-    const int s = w * HP + j;
-    sg[j] = s < H_r ? (int)hm.perm[s] : -1;
-  }
+  for (int j = 0; j < HP; ++j) sg[j] = head_of(w * HP + j);
   v4f acc[HP][NDT];
 #pragma unroll
   for (int j = 0; j < HP; ++j)
@@ -384,9 +394,9 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
             }
             mix[half] = m4;
           }
-          // lane (a, c): receiver head 16 nt + c, keys 32 ch + 16 half + 4a + i -> 8 fp16 values
+          // lane (a, c): local head 16 nt + c, keys 32 ch + 16 half + 4a + i -> 8 fp16 values
           const int g = 16 * nt + c;
-          if (g < H_r) {
+          if (g < HR_MAX && slot0 + g < H_r) {          // the slot holds a head
             uint32_t pk[4];
 #pragma unroll
             for (int half = 0; half < 2; ++half)
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
         }
-        const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + g * GB + c * RB + (ch * 4 + a) * 16));
+        const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (w * HP + j) * GB + c * RB + (ch * 4 + a) * 16));
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
       }
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     for (int i = 0; i < 4; ++i) {
       const int ii = 4 * a + i;
       if (ii >= rows) continue;
-      const float inv = unscale / s_den[g][ii];
+      const float inv = unscale / s_den[w * HP + j][ii];
       float* orow = O + ((size_t)(bi.tok0 + row0 + ii) * H_r + g) * D;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
@@ -453,39 +463,40 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
 }
 
 bool retrieve_supported(int B, int d, int H_r, int H_s) {
-  return (B == 32 || B == 64) && (d == 64 || d == 128) && H_r >= 1 && H_r <= 32 && H_s >= 1 &&
+  return (B == 32 || B == 64) && (d == 64 || d == 128) && H_r >= 1 && H_r <= 48 && H_s >= 1 &&
          H_s <= 64;
 }
 
-template <int B, int D, int HP, int KC>
+template <int B, int D, int HP, int KC, int NSPLIT>
 static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
   constexpr int NRT = B / RT_ROWS;
   const unsigned groups = (unsigned)((a.n_brow + 7) / 8);
-  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC>), dim3(groups * 8 * NRT), dim3(RT_WAVES * 64), 0, s,
+  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC, NSPLIT>), dim3(groups * 8 * NRT * NSPLIT), dim3(RT_WAVES * 64), 0, s,
                      a.probs, a.block_ptr, a.block_idx, a.info, a.order, a.capacity, a.n_brow, a.H_s, a.T,
                      a.rkm, a.W, a.H_r, a.vfrag, a.vexps, a.hm, a.O);
   return hipGetLastError();
 }
 
+// Up to 24 receiver heads one workgroup mixes them all (each P tile is read once); beyond that
+// the heads are split over two workgroups of the same XCD that read each P tile one after the
+// other (the second read hits L2), which keeps the accumulators and operands in registers.
 template <int B, int D>
 static hipError_t retrieve_bd(const RetrieveArgs& a, hipStream_t s) {
-  const int HP = (a.H_r + 7) / 8;
+  const int NSPLIT = a.H_r <= 24 ? 1 : 2;
+  const int HP = (a.H_r + 8 * NSPLIT - 1) / (8 * NSPLIT);
   const int KC = ((a.H_s + 7) / 8 + 3) / 4;
-  if (KC == 1) {
-    switch (HP) {
-      case 1: return retrieve_t<B, D, 1, 1>(a, s);
-      case 2: return retrieve_t<B, D, 2, 1>(a, s);
-      case 3: return retrieve_t<B, D, 3, 1>(a, s);
-      case 4: return retrieve_t<B, D, 4, 1>(a, s);
-    }
-  } else {
-    switch (HP) {
-      case 1: return retrieve_t<B, D, 1, 2>(a, s);
-      case 2: return retrieve_t<B, D, 2, 2>(a, s);
-      case 3: return retrieve_t<B, D, 3, 2>(a, s);
-      case 4: return retrieve_t<B, D, 4, 2>(a, s);
-    }
+#define MF_RETRIEVE_CASES(KC_, NS_)                            \
+  switch (HP) {                                                \
+    case 1: return retrieve_t<B, D, 1, KC_, NS_>(a, s);        \
+    case 2: return retrieve_t<B, D, 2, KC_, NS_>(a, s);        \
+    case 3: return retrieve_t<B, D, 3, KC_, NS_>(a, s);        \
   }
+  if (NSPLIT == 1) {
+    if (KC == 1) { MF_RETRIEVE_CASES(1, 1) } else { MF_RETRIEVE_CASES(2, 1) }
+  } else {
+    if (KC == 1) { MF_RETRIEVE_CASES(1, 2) } else { MF_RETRIEVE_CASES(2, 2) }
+  }
+#undef MF_RETRIEVE_CASES
   return hipErrorInvalidValue;
 }
 

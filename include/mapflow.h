@@ -234,7 +234,9 @@ mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf);
  *                     gives IEEE inf/nan like the definition)
  *   kv_head_map_host  int32 [H_r], each in [0, H_kv)
  *   O                 fp32 [T][H_r][d] device; must not alias any input
- * Limits: H_r <= 32, H_s <= 64, d in {64, 128}, B in {32, 64}, vf geometry equal to the store's.
+ * Limits: H_r <= 48, H_s <= 64, d in {64, 128}, B in {32, 64}, vf geometry equal to the store's.
+ * Above 24 receiver heads the heads are mixed by two workgroups per row tile, each reading the
+ * tile (the second read is served by L2).
  * Rows of the mixed map are rounded to fp16 (scaled by a power of two per receiver head) before
  * the V product; sums are fp32.
  */

@@ -118,6 +118,8 @@ def _upload_oracle_store(mf, ref, x):
     dict(wl="varlen_14b8b", seed=0, lengths=[333, 70], heads=(40, 32, 8, 128)),
     dict(wl="pair_8b3b_8k", seed=2, lengths=[200], heads=(16, 12, 4, 64)),
     dict(wl="pair_8b3b_8k", seed=3, lengths=[190], heads=(8, 5, 5, 128)),
+    dict(wl="pair_8b3b_8k", seed=4, lengths=[170, 33], heads=(16, 48, 8, 64)),   # 48 heads: split
+    dict(wl="varlen_14b8b", seed=1, lengths=[150], heads=(40, 25, 5, 128)),      # split, 1 head left
 ])
 def test_retrieve_on_oracle_store(mf, case):
     wl = synth.WORKLOADS[case["wl"]]
