@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=16, help="block rows in the oracle sample")
+    p.add_argument("--no-fanout", action="store_true",
+                   help="skip the multi-receiver retrieve comparison run after the timed steps")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
                    help="size of the HBM copy probe run after the timed steps (0 = skip)")
     return p.parse_args()
@@ -122,6 +124,51 @@ def cpu_baseline(wl, args, mapped_layers, n_mapped, recompute_layers):
                        f"{n_mapped} mapped + {len(recompute_layers)} recomputed layers "
                        f"(est. {est:.0f} s per step)"),
             "extrapolated": True}
+
+
+def fanout(mf, torch, wl, args, store, recvs, pvs, kv_map, B, cu, ctx, dev):
+    """One sender layer's store read by several receivers: separate retrieves against one
+    mf_retrieve_multi launch.  Receivers: two of the benchmark's receiver shape (two mapped
+    layers' W and V), and that shape next to an 8B-like 32q/8kv receiver (synthetic W and V)."""
+    L = store.raw.T
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed + 7)
+    import synth
+    W32 = torch.from_numpy(synth.rng_for(args.seed, 1000, "w").dirichlet(np.full(wl.H_s, 0.5), size=32)
+                           .astype(np.float32)).to(dev)
+    V32 = torch.randn((L, 8, wl.d), generator=g, device=dev).to(torch.bfloat16)
+    pv32 = mf.v_prepare(V32, B, cu, ctx=ctx)
+    kv32 = [h // 4 for h in range(32)]
+    cases = {
+        f"{wl.H_r}q/{wl.H_kv}kv x2": [(recvs[0][0], pvs[0], kv_map), (recvs[1][0], pvs[1], kv_map)],
+        f"32q/8kv + {wl.H_r}q/{wl.H_kv}kv": [(W32, pv32, kv32), (recvs[1][0], pvs[1], kv_map)],
+    }
+    res = {}
+    for name, rs in cases.items():
+        outs = [torch.empty((L, W.shape[0], wl.d), dtype=torch.float32, device=dev) for W, _, _ in rs]
+
+        def separate():
+            for (W, pv, kvm), o in zip(rs, outs):
+                mf.retrieve_prepared(store, W, pv, kvm, out=o)
+
+        def fused():
+            mf.retrieve_multi(store, rs, outs=outs)
+
+        times = {}
+        for label, fn in (("separate", separate), ("fused", fused)):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(10):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times[label] = e0.elapsed_time(e1) / 10
+        res[name] = {"separate_ms": times["separate"], "fused_ms": times["fused"],
+                     "saving": 1.0 - times["fused"] / times["separate"]}
+        log(f"fan-out {name}: separate {times['separate']:.3f} ms, fused {times['fused']:.3f} ms")
+    return res
 
 
 def main():
@@ -321,6 +368,10 @@ def main():
         ms = e0.elapsed_time(e1) / reps
         out["hbm_copy_probe"] = {"bytes_moved": 2 * n * 4, "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}
         del src, dst
+
+    if not args.no_fanout and n_map >= 2:
+        out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [recv[l] for l in mapped[-2:]],
+                               [pv[l] for l in mapped[-2:]], kv_map, B, cu, ctx, dev)
 
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample (CPU)")

@@ -17,6 +17,7 @@ from .mapflow import (  # noqa: F401
     probs_canonical_to_store,
     probs_store_to_canonical,
     retrieve,
+    retrieve_multi,
     retrieve_prepared,
     v_prepare,
     version,

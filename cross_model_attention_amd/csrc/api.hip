@@ -732,28 +732,74 @@ MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {
   return MF_OK;
 }
 
-MF_EXPORT mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W,
-                                         int32_t H_r, const mf_vfrag* vf,
-                                         const int32_t* kvmap, float* O, void* stream) {
+// One launch for n_recv receivers of the same store: every receiver's head parts are splits of
+// one row-tile work item, so each stored probability tile is read from HBM once for all of them.
+static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, const float* const* W,
+                                 const int32_t* H_r, const mf_vfrag* const* vf,
+                                 const int32_t* const* kvmap, float* const* O, void* stream) {
   if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
-  if (!vf || !vf->_owner) return fail(MF_ERR_INVALID, "prepared V is NULL");
-  if (!W || !O) return fail(MF_ERR_INVALID, "W or O is NULL");
-  if (H_r < 1) return fail(MF_ERR_INVALID, "H_r must be >= 1");
-  if (vf->B != bsr->B || vf->n_brow != bsr->n_brow || vf->T != bsr->T)
-    return fail(MF_ERR_INVALID, "prepared V geometry (B=%d, %d block rows, T=%lld) differs from the store's "
-                "(B=%d, %d, T=%lld)", vf->B, vf->n_brow, (long long)vf->T, bsr->B, bsr->n_brow,
-                (long long)bsr->T);
-  const VfragOwner* vo = static_cast<const VfragOwner*>(vf->_owner);
+  if (n_recv < 1 || n_recv > mf::kMaxRecv)
+    return fail(MF_ERR_INVALID, "n_recv = %d outside [1, %d]", n_recv, mf::kMaxRecv);
+  if (!W || !H_r || !vf || !kvmap || !O) return fail(MF_ERR_INVALID, "receiver array is NULL");
   const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
-  if (vo->geom.cu != bo->geom.cu) return fail(MF_ERR_INVALID, "prepared V has different cu_seqlens");
-  if (!mf::retrieve_supported(bsr->B, vf->d, H_r, bsr->H_s))
-    return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", bsr->B, vf->d, H_r, bsr->H_s);
-  mf::HeadMap hm;
-  mf_status st = build_headmap(kvmap, H_r, vf->H_kv, hm);
-  if (st != MF_OK) return st;
-  if ((st = set_device(ctx)) != MF_OK) return st;
-  if (bsr->n_brow == 0) return MF_OK;
   mf::RetrieveArgs a{};
+  mf::HeadMap hm[mf::kMaxRecv];
+  for (int r = 0; r < n_recv; ++r) {
+    const mf_vfrag* v = vf[r];
+    if (!v || !v->_owner) return fail(MF_ERR_INVALID, "prepared V of receiver %d is NULL", r);
+    if (!W[r] || !O[r]) return fail(MF_ERR_INVALID, "W or O of receiver %d is NULL", r);
+    if (H_r[r] < 1) return fail(MF_ERR_INVALID, "H_r of receiver %d must be >= 1", r);
+    if (v->B != bsr->B || v->n_brow != bsr->n_brow || v->T != bsr->T)
+      return fail(MF_ERR_INVALID, "prepared V of receiver %d: geometry (B=%d, %d block rows, T=%lld) "
+                  "differs from the store's (B=%d, %d, T=%lld)", r, v->B, v->n_brow, (long long)v->T,
+                  bsr->B, bsr->n_brow, (long long)bsr->T);
+    const VfragOwner* vo = static_cast<const VfragOwner*>(v->_owner);
+    if (vo->geom.cu != bo->geom.cu)
+      return fail(MF_ERR_INVALID, "prepared V of receiver %d has different cu_seqlens", r);
+    if (v->d != vf[0]->d)
+      return fail(MF_ERR_INVALID, "receiver %d has head dim %d, receiver 0 has %d", r, v->d, vf[0]->d);
+    if (!mf::retrieve_supported(bsr->B, v->d, H_r[r], bsr->H_s))
+      return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", bsr->B, v->d,
+                  H_r[r], bsr->H_s);
+    mf::RecvArgs& rv = a.recv[r];
+    mf_status st = build_headmap(kvmap[r], H_r[r], v->H_kv, hm[r]);
+    if (st != MF_OK) return st;
+    rv.W = W[r];
+    rv.vfrag = v->frag;
+    rv.vexps = v->exps;
+    rv.O = O[r];
+    rv.H_r = H_r[r];
+    rv.H_kv = v->H_kv;
+  }
+  // Head splits.  Each receiver's heads (in KV order) form one part, or two equal parts above 24
+  // heads.  Parts are packed first-fit, largest first, into splits of at most 24 heads (a split
+  // may hold parts of several receivers).  A workgroup costs about the same per kept block
+  // whatever its head count within one width, and the splits of one row tile only share the P
+  // tile through L2 while they advance at the same rate, so splits are grouped by width
+  // (HP = ceil(heads / 8)) and each group is one launch.
+  struct Part { int r, g0, n; };
+  Part parts[2 * mf::kMaxRecv];
+  int n_parts = 0;
+  for (int r = 0; r < n_recv; ++r) {
+    const int halves = H_r[r] <= mf::kMaxSlots ? 1 : 2;
+    for (int p = 0, g0 = 0; p < halves; ++p) {
+      const int n = H_r[r] / halves + (p < H_r[r] % halves ? 1 : 0);
+      parts[n_parts++] = Part{r, g0, n};
+      g0 += n;
+    }
+  }
+  std::stable_sort(parts, parts + n_parts, [](const Part& x, const Part& y) { return x.n > y.n; });
+  int split_of[2 * mf::kMaxRecv], split_heads[2 * mf::kMaxRecv], n_split = 0;
+  for (int i = 0; i < n_parts; ++i) {
+    int k = 0;
+    while (k < n_split && split_heads[k] + parts[i].n > mf::kMaxSlots) ++k;
+    if (k == n_split) split_heads[n_split++] = 0;
+    split_heads[k] += parts[i].n;
+    split_of[i] = k;
+  }
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  if (bsr->n_brow == 0) return MF_OK;
   a.probs = bsr->probs;
   a.block_ptr = bsr->block_ptr;
   a.block_idx = bsr->block_idx;
@@ -763,18 +809,53 @@ MF_EXPORT mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const f
   a.n_brow = bsr->n_brow;
   a.H_s = bsr->H_s;
   a.B = bsr->B;
-  a.d = vf->d;
+  a.d = vf[0]->d;
   a.T = bsr->T;
   a.rkm = bsr->row_kept_mass;
-  a.W = W;
-  a.H_r = H_r;
-  a.H_kv = vf->H_kv;
-  a.vfrag = vf->frag;
-  a.vexps = vf->exps;
-  a.hm = hm;
-  a.O = O;
-  MF_HIP(mf::retrieve(a, static_cast<hipStream_t>(stream)), "retrieve launch");
+  a.n_recv = n_recv;
+  for (int HP = 1; HP <= 3; ++HP) {
+    a.HP = HP;
+    a.n_split = 0;
+    for (int k = 0; k < n_split; ++k) {
+      if ((split_heads[k] + 7) / 8 != HP) continue;
+      const int ks = a.n_split++;
+      int j = 0;
+      for (int i = 0; i < n_parts; ++i) {
+        if (split_of[i] != k) continue;
+        const Part& pt = parts[i];
+        for (int q = 0; q < pt.n; ++q, ++j) {
+          const int head = hm[pt.r].perm[pt.g0 + q];
+          a.slot_recv[ks][j] = (int8_t)pt.r;
+          a.slot_head[ks][j] = (int8_t)head;
+          a.slot_kv[ks][j] = hm[pt.r].kv[head];
+        }
+      }
+      a.split_nslots[ks] = (int8_t)j;
+      for (; j < mf::kMaxSlots; ++j) {
+        a.slot_recv[ks][j] = 0;
+        a.slot_head[ks][j] = -1;
+        a.slot_kv[ks][j] = 0;
+      }
+    }
+    if (a.n_split == 0) continue;
+    MF_HIP(mf::retrieve(a, static_cast<hipStream_t>(stream)), "retrieve launch");
+  }
   return MF_OK;
+}
+
+MF_EXPORT mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W,
+                                         int32_t H_r, const mf_vfrag* vf,
+                                         const int32_t* kvmap, float* O, void* stream) {
+  if (!W || !O) return fail(MF_ERR_INVALID, "W or O is NULL");
+  if (!vf || !vf->_owner) return fail(MF_ERR_INVALID, "prepared V is NULL");
+  return retrieve_launch(ctx, bsr, 1, &W, &H_r, &vf, &kvmap, &O, stream);
+}
+
+MF_EXPORT mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_recv,
+                                      const float* const* W, const int32_t* H_r,
+                                      const mf_vfrag* const* vf, const int32_t* const* kvmap,
+                                      float* const* O, void* stream) {
+  return retrieve_launch(ctx, bsr, n_recv, W, H_r, vf, kvmap, O, stream);
 }
 
 MF_EXPORT mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,

@@ -42,6 +42,14 @@ __device__ __forceinline__ v4u ld16_nt(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, v4u v) { *reinterpret_cast<v4u*>(p) = v; }
 
+// Device-memory pointers kept in LDS or registers lose the compiler's knowledge that they point
+// to global memory, and accesses through them become flat accesses (which also count against the
+// LDS wait counter).  This qualifier keeps them global.
+#define MF_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ v4u ld16(const MF_GLOBAL void* p) {
+  return *reinterpret_cast<const MF_GLOBAL v4u*>(p);
+}
+
 __device__ __forceinline__ v8s as_v8s(v4u v) { return __builtin_bit_cast(v8s, v); }
 __device__ __forceinline__ v8h as_v8h(v4u v) { return __builtin_bit_cast(v8h, v); }
 __device__ __forceinline__ v4u zero_u4() { return v4u{0u, 0u, 0u, 0u}; }

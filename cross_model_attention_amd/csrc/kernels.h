@@ -67,6 +67,19 @@ struct HeadMap {
   int8_t kv[64];    // KV head of each receiver head
 };
 
+// One receiver of a (possibly fanned-out) retrieve.
+struct RecvArgs {
+  const float* W;        // [H_r][H_s]
+  const uint16_t* vfrag; // prepared V tiles
+  const int32_t* vexps;  // per-KV-head scale exponents
+  float* O;              // [T][H_r][d]
+  int H_r, H_kv;
+};
+
+constexpr int kMaxRecv = 4;    // receivers per fused retrieve
+constexpr int kMaxSplit = 8;   // workgroups per row tile (head splits over all receivers)
+constexpr int kMaxSlots = 24;  // receiver heads per split (8 waves x 3)
+
 struct RetrieveArgs {
   const uint16_t* probs;
   const int32_t* block_ptr;
@@ -77,12 +90,13 @@ struct RetrieveArgs {
   int n_brow, H_s, B, d;
   int64_t T;
   const float* rkm;
-  const float* W;
-  int H_r, H_kv;
-  const uint16_t* vfrag;
-  const int32_t* vexps;
-  HeadMap hm;
-  float* O;
+  int n_recv, n_split;
+  int HP;                                  // heads per wave: a split holds up to 8*HP heads
+  int8_t split_nslots[kMaxSplit];          // heads in each split; they fill its leading slots
+  int8_t slot_recv[kMaxSplit][kMaxSlots];  // receiver of each slot
+  int8_t slot_head[kMaxSplit][kMaxSlots];  // head within that receiver; -1 = empty
+  int8_t slot_kv[kMaxSplit][kMaxSlots];    // KV head of that head
+  RecvArgs recv[kMaxRecv];
 };
 hipError_t retrieve(const RetrieveArgs& a, hipStream_t s);
 bool retrieve_supported(int B, int d, int H_r, int H_s);

@@ -193,20 +193,37 @@ struct AhatLayout {
   static_assert(!kWide || B * 2 <= 160, "row must fit its stride");
 };
 
-// Head mix on MFMA: N-tiles are receiver heads in chunks of 16 (NTG = ceil(H_r / 16) tiles), the
-// contraction runs over the sender heads twice, once against the bf16 "hi" part and once against
-// the bf16 "lo" part of the scaled weights, accumulating into the same fp32 tile: Ws = hi + lo
-// keeps ~16 bits of W while the kept probabilities enter the MFMA exactly.  HP = ceil(H_r / 8)
-// is the number of receiver heads each of the 8 waves owns in stage 2.
-template <int B, int D, int HP, int KC, int NSPLIT>
-__global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
-    const uint16_t* __restrict__ probs, const int32_t* __restrict__ block_ptr,
-    const int32_t* __restrict__ block_idx, const int32_t* __restrict__ info,
-    const int32_t* __restrict__ order, int64_t capacity, int n_brow, int H_s, int64_t T_tot,
-    const float* __restrict__ rkm, const float* __restrict__ W, int H_r,
-    const uint16_t* __restrict__ vfrag, const int32_t* __restrict__ vexps, HeadMap hm,
-    float* __restrict__ O) {
-  constexpr int NRT = B / RT_ROWS;         // row tiles per block row
+// Per-slot receiver data of a work item: the slot's weight row, its V operand tiles (KV head
+// already applied), its output column block and row stride, and V's scale exponent.
+struct SlotInfo {
+  const MF_GLOBAL float* w;
+  const MF_GLOBAL uint16_t* v;
+  MF_GLOBAL float* o;
+  int ostride;
+  int vexp;
+};
+
+// Head mix on MFMA: N-tiles are the split's receiver heads in chunks of 16 (NTG = ceil(HP / 2)
+// tiles), the contraction runs over the sender heads twice, once against the bf16 "hi" part and
+// once against the bf16 "lo" part of the scaled weights, accumulating into the same fp32 tile:
+// Ws = hi + lo keeps ~16 bits of W while the kept probabilities enter the MFMA exactly.  A split
+// holds up to 8*HP heads; each of the 8 waves owns HP of them in stage 2.
+//
+// Work items are XCD-aware: the row tiles and head splits of one block row share an XCD and run
+// one after the other, so every split after the first finds the P tile in that XCD's L2.  A
+// split's slots may hold heads of different receivers (a fan-out): each slot carries its own
+// weights, V and output.
+template <int B, int D, int HP, int KC>
+__global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs args) {
+  const uint16_t* __restrict__ probs = args.probs;
+  const int32_t* __restrict__ block_ptr = args.block_ptr;
+  const int32_t* __restrict__ block_idx = args.block_idx;
+  const int32_t* __restrict__ info = args.info;
+  const int32_t* __restrict__ order = args.order;
+  const int64_t capacity = args.capacity;
+  const int n_brow = args.n_brow, H_s = args.H_s;
+  const int64_t T_tot = args.T;
+  const float* __restrict__ rkm = args.rkm;
   constexpr int MT = B / 16;               // 16-key M-tiles per row
   constexpr int NCH = B / 32;              // 32-key chunks per block
   constexpr int NDT = D / 16;              // 16-column output tiles
@@ -218,16 +235,18 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   __shared__ __attribute__((aligned(16))) unsigned char s_ahat[2][HR_MAX * GB];
   __shared__ float s_den[HR_MAX][RT_ROWS];
   __shared__ int s_sexp[HR_MAX];
+  __shared__ int s_head[HR_MAX];
+  __shared__ SlotInfo s_slot[HR_MAX];
   __shared__ v4u s_wop[NTG][KC][2][64];
 
-  // ---- work item: XCD-aware (the row tiles and head splits of one block row share an XCD, so
-  // a P tile read by both halves of a split comes from HBM once) ----------------------------
+  constexpr int NRT = B / RT_ROWS;         // row tiles per block row
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int q = b >> 3;
   const int rt = q % NRT;
-  const int split = (q / NRT) % NSPLIT;
-  const int gidx = (q / (NRT * NSPLIT)) * 8 + xcd;
+  const int n_split = args.n_split;
+  const int split = (q / NRT) % n_split;
+  const int gidx = (q / (NRT * n_split)) * 8 + xcd;
   if (gidx >= n_brow) return;
   const int brow = order[gidx];
   const BrowInfo bi = load_info(info, brow);
@@ -237,13 +256,27 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   const int row0 = RT_ROWS * rt;              // first row of the tile within the block row
   const int HGp = (H_s + 7) >> 3;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
-  // this workgroup's receiver heads: slots split*HR_MAX + j (j = 0..HR_MAX-1) of the kv-sorted
-  // head list; mixed maps, weights and denominators are indexed by the local slot j
-  const int slot0 = split * HR_MAX;
-  __shared__ int s_head[HR_MAX];
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int j = 0; j < HR_MAX; ++j) s_head[j] = slot0 + j < H_r ? (int)hm.perm[slot0 + j] : -1;
+  // this workgroup's heads: slot j (j = 0..HR_MAX-1) holds head slot_head[split][j] (-1: empty;
+  // heads fill the leading slots) of receiver slot_recv[split][j], KV head slot_kv[split][j];
+  // mixed maps, weights and denominators are indexed by the slot
+  const int n_slots = args.split_nslots[split];
+  if (threadIdx.x < HR_MAX) {
+    const int j = threadIdx.x;
+    const int g = args.slot_head[split][j];
+    s_head[j] = g;
+    // an empty slot still names valid V tiles (receiver 0, KV head 0): a wave whose first slot
+    // is empty prefetches them and never uses them
+    const RecvArgs& rv = args.recv[args.slot_recv[split][j]];
+    const int kv = args.slot_kv[split][j];
+    SlotInfo si{nullptr, (const MF_GLOBAL uint16_t*)(rv.vfrag + (size_t)kv * n_brow * (NCH * NDT * 512)),
+                nullptr, 0, 0};
+    if (g >= 0) {
+      si.w = (const MF_GLOBAL float*)(rv.W + (size_t)g * H_s);
+      si.o = (MF_GLOBAL float*)(rv.O + (size_t)g * D);
+      si.ostride = rv.H_r * D;
+      si.vexp = rv.vexps[kv];
+    }
+    s_slot[j] = si;
   }
   __syncthreads();
   auto head_of = [&](int j) { return s_head[j]; };
@@ -256,8 +289,9 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const int g = head_of(threadIdx.x);
     int e = 0;
     if (g >= 0) {
+      const MF_GLOBAL float* wr = s_slot[threadIdx.x].w;
       float sa = 0.f;
-      for (int h = 0; h < H_s; ++h) sa += fabsf(W[g * H_s + h]);
+      for (int h = 0; h < H_s; ++h) sa += fabsf(wr[h]);
       if (sa > 0.f && sa < __builtin_inff()) {
         int ex;
         frexpf(sa, &ex);      // sum |W| <= 2^ex
@@ -271,7 +305,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const int j = t >> 6, h = t & 63, g = head_of(j);
     float v = 0.f;
     if (g >= 0 && h < H_s) {
-      const float x = ldexpf(W[g * H_s + h], s_sexp[j]);
+      const float x = ldexpf(s_slot[j].w[h], s_sexp[j]);
       const float hi = bf16_to_f32(f32_to_bf16(x));
       const float lo = bf16_to_f32(f32_to_bf16(x - hi));
       v = hi + lo;
@@ -294,6 +328,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     for (int nt = 0; nt < NTG; ++nt) {
       const int jn = 16 * nt + c;
       const int g = jn < HR_MAX ? head_of(jn) : -1;
+      const MF_GLOBAL float* wr = g >= 0 ? s_slot[jn].w : nullptr;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -307,7 +342,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
               const int h = 32 * kc + 8 * a + 2 * e2 + q2;
               uint32_t bits = 0;
               if (g >= 0 && h < H_s) {
-                const float x = ldexpf(W[g * H_s + h], s_sexp[jn]);
+                const float x = ldexpf(wr[h], s_sexp[jn]);
                 const uint16_t hb = f32_to_bf16(x);
                 bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
               }
@@ -355,14 +390,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
   if (t0 < t1) load_p(t0);
   __syncthreads();
 
-  // V operand tiles of the wave's first KV head for key chunk 0 are fetched before the head mix,
-  // so their latency hides under it; later chunks and other KV heads are loaded on use.
-  int kvj[HP];
+  // V operand tiles of the wave's first slot for key chunk 0 are fetched before the head mix,
+  // so their latency hides under it; later chunks and other V heads are loaded on use.
+  const MF_GLOBAL uint16_t* vj[HP];
 #pragma unroll
-  for (int j = 0; j < HP; ++j) kvj[j] = sg[j] >= 0 ? (int)hm.kv[sg[j]] : 0;
-  const int kv0 = kvj[0];
-  auto vtile = [&](int kv, int kbrow, int ch) {
-    return vfrag + ((((size_t)kv * n_brow + kbrow) * NCH + ch) * NDT) * 512 + lane * 8;
+  for (int j = 0; j < HP; ++j) vj[j] = s_slot[w * HP + j].v + lane * 8;
+  const MF_GLOBAL uint16_t* const v0 = vj[0];
+  auto vtile = [&](const MF_GLOBAL uint16_t* vb, int kbrow, int ch) {
+    return vb + (((size_t)kbrow * NCH + ch) * NDT) * 512;
   };
   for (int t = t0; t < t1; ++t) {
     unsigned char* buf = s_ahat[(t - t0) & 1];
@@ -370,7 +405,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const int kbrow = kbrow0 + J;
     v8h vpre[NCH][NDT];
     {
-      const uint16_t* vb = vtile(kv0, kbrow, 0);
+      const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, 0);
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
     }
@@ -396,7 +431,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
           }
           // lane (a, c): local head 16 nt + c, keys 32 ch + 16 half + 4a + i -> 8 fp16 values
           const int g = 16 * nt + c;
-          if (g < HR_MAX && slot0 + g < H_r) {          // the slot holds a head
+          if (g < n_slots) {                             // the slot holds a head
             uint32_t pk[4];
 #pragma unroll
             for (int half = 0; half < 2; ++half)
@@ -417,7 +452,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       if (ch > 0) {
-        const uint16_t* vb = vtile(kv0, kbrow, ch);
+        const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, ch);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
       }
@@ -425,13 +460,12 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
       for (int j = 0; j < HP; ++j) {
         const int g = sg[j];
         if (g < 0) continue;
-        const int kv = kvj[j];
         v8h vop[NDT];
-        if (kv == kv0) {
+        if (vj[j] == v0) {
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) vop[dt] = vpre[ch][dt];
         } else {
-          const uint16_t* vb = vtile(kv, kbrow, ch);
+          const MF_GLOBAL uint16_t* vb = vtile(vj[j], kbrow, ch);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
         }
@@ -449,13 +483,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(
     const int g = sg[j];
     if (g < 0) continue;
     // den carries the same 2^s_g as the mixed map, so only V's scale is undone here
-    const float unscale = ldexpf(1.f, -vexps[hm.kv[g]]);
+    const SlotInfo& si = s_slot[w * HP + j];
+    const float unscale = ldexpf(1.f, -si.vexp);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ii = 4 * a + i;
       if (ii >= rows) continue;
       const float inv = unscale / s_den[w * HP + j][ii];
-      float* orow = O + ((size_t)(bi.tok0 + row0 + ii) * H_r + g) * D;
+      MF_GLOBAL float* orow = si.o + (size_t)(bi.tok0 + row0 + ii) * si.ostride;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
     }
@@ -467,40 +502,42 @@ bool retrieve_supported(int B, int d, int H_r, int H_s) {
          H_s <= 64;
 }
 
-template <int B, int D, int HP, int KC, int NSPLIT>
+template <int B, int D, int HP, int KC>
 static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
   constexpr int NRT = B / RT_ROWS;
   const unsigned groups = (unsigned)((a.n_brow + 7) / 8);
-  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC, NSPLIT>), dim3(groups * 8 * NRT * NSPLIT), dim3(RT_WAVES * 64), 0, s,
-                     a.probs, a.block_ptr, a.block_idx, a.info, a.order, a.capacity, a.n_brow, a.H_s, a.T,
-                     a.rkm, a.W, a.H_r, a.vfrag, a.vexps, a.hm, a.O);
+  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
-// Up to 24 receiver heads one workgroup mixes them all (each P tile is read once); beyond that
-// the heads are split over two workgroups of the same XCD that read each P tile one after the
-// other (the second read hits L2), which keeps the accumulators and operands in registers.
 template <int B, int D>
 static hipError_t retrieve_bd(const RetrieveArgs& a, hipStream_t s) {
-  const int NSPLIT = a.H_r <= 24 ? 1 : 2;
-  const int HP = (a.H_r + 8 * NSPLIT - 1) / (8 * NSPLIT);
   const int KC = ((a.H_s + 7) / 8 + 3) / 4;
-#define MF_RETRIEVE_CASES(KC_, NS_)                            \
-  switch (HP) {                                                \
-    case 1: return retrieve_t<B, D, 1, KC_, NS_>(a, s);        \
-    case 2: return retrieve_t<B, D, 2, KC_, NS_>(a, s);        \
-    case 3: return retrieve_t<B, D, 3, KC_, NS_>(a, s);        \
+#define MF_RETRIEVE_CASES(KC_)                          \
+  switch (a.HP) {                                       \
+    case 1: return retrieve_t<B, D, 1, KC_>(a, s);      \
+    case 2: return retrieve_t<B, D, 2, KC_>(a, s);      \
+    case 3: return retrieve_t<B, D, 3, KC_>(a, s);      \
   }
-  if (NSPLIT == 1) {
-    if (KC == 1) { MF_RETRIEVE_CASES(1, 1) } else { MF_RETRIEVE_CASES(2, 1) }
-  } else {
-    if (KC == 1) { MF_RETRIEVE_CASES(1, 2) } else { MF_RETRIEVE_CASES(2, 2) }
-  }
+  if (KC == 1) { MF_RETRIEVE_CASES(1) } else { MF_RETRIEVE_CASES(2) }
 #undef MF_RETRIEVE_CASES
   return hipErrorInvalidValue;
 }
 
 hipError_t retrieve(const RetrieveArgs& a, hipStream_t s) {
+  if (a.n_recv < 1 || a.n_recv > kMaxRecv || a.n_split < 1 || a.n_split > kMaxSplit || a.HP < 1 || a.HP > 3)
+    return hipErrorInvalidValue;
+  for (int k = 0; k < a.n_split; ++k) {
+    const int n = a.split_nslots[k];
+    if (n < 1 || n > 8 * a.HP) return hipErrorInvalidValue;
+    for (int j = 0; j < 8 * a.HP; ++j) {
+      // every slot, empty or not, names a receiver and one of its KV heads
+      const int r = a.slot_recv[k][j], g = a.slot_head[k][j], kv = a.slot_kv[k][j];
+      if ((j < n) != (g >= 0)) return hipErrorInvalidValue;
+      if (r < 0 || r >= a.n_recv || kv < 0 || kv >= a.recv[r].H_kv || g >= a.recv[r].H_r)
+        return hipErrorInvalidValue;
+    }
+  }
   if (a.B == 64 && a.d == 128) return retrieve_bd<64, 128>(a, s);
   if (a.B == 64 && a.d == 64) return retrieve_bd<64, 64>(a, s);
   if (a.B == 32 && a.d == 128) return retrieve_bd<32, 128>(a, s);

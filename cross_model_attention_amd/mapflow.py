@@ -305,6 +305,38 @@ def retrieve_prepared(store: BlockStore, W: torch.Tensor, pv: PreparedV, kv_head
     return out
 
 
+def retrieve_multi(store: BlockStore, receivers, outs=None, stream=None) -> list[torch.Tensor]:
+    """mf_retrieve_multi: one launch for several receivers of the same store.
+
+    ``receivers`` is a sequence of ``(W, prepared_v, kv_head_map)``; returns one O [T, H_r, d] fp32
+    per receiver (or fills ``outs``)."""
+    receivers = list(receivers)
+    n = len(receivers)
+    if outs is not None and len(outs) != n:
+        raise ValueError("outs must have one tensor per receiver")
+    Ws, Hs, vfs, maps, Os, tensors = [], [], [], [], [], []
+    for r, (W, pv, kvmap) in enumerate(receivers):
+        if W.dtype != torch.float32 or W.dim() != 2 or W.shape[1] != store.raw.H_s:
+            raise ValueError(f"W of receiver {r} must be float32 [H_r, H_s]")
+        H_r = int(W.shape[0])
+        out = _out(None if outs is None else outs[r], store.raw.T, H_r, pv.raw.d, W)
+        m = i32_array(kvmap)
+        tensors.append(out)
+        Ws.append(_dev(W, "W"))
+        Hs.append(H_r)
+        vfs.append(ctypes.pointer(pv.raw))
+        maps.append(ctypes.cast(m, _lib._P_I32))
+        Os.append(_dev(out, "out"))
+    W_arr = (ctypes.c_void_p * n)(*Ws)
+    H_arr = (ctypes.c_int32 * n)(*Hs)
+    vf_arr = (ctypes.POINTER(MfVfrag) * n)(*vfs)
+    map_arr = (_lib._P_I32 * n)(*maps)
+    O_arr = (ctypes.c_void_p * n)(*Os)
+    check(_L.mf_retrieve_multi(store.ctx.handle, ctypes.byref(store.raw), n, W_arr, H_arr, vf_arr,
+                               map_arr, O_arr, _stream(stream)))
+    return tensors
+
+
 def retrieve(store: BlockStore, W: torch.Tensor, V: torch.Tensor, kv_head_map, page_table=None,
              page_size: int = 16, out=None, stream=None) -> torch.Tensor:
     """mf_retrieve: V preparation into context scratch + the fused retrieve kernel."""

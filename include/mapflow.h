@@ -235,14 +235,34 @@ mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf);
  *   kv_head_map_host  int32 [H_r], each in [0, H_kv)
  *   O                 fp32 [T][H_r][d] device; must not alias any input
  * Limits: H_r <= 48, H_s <= 64, d in {64, 128}, B in {32, 64}, vf geometry equal to the store's.
- * Above 24 receiver heads the heads are mixed by two workgroups per row tile, each reading the
- * tile (the second read is served by L2).
+ * Above 24 receiver heads the heads are mixed by two workgroups per row tile (equal halves),
+ * each reading the tile (the second read is served by L2).
  * Rows of the mixed map are rounded to fp16 (scaled by a power of two per receiver head) before
  * the V product; sums are fp32.
  */
 mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,
                                const mf_vfrag* vf, const int32_t* kv_head_map_host, float* O,
                                void* stream);
+
+/*
+ * Fused retrieve for several receivers of one sender state in a single launch.
+ * [MapFlow开源, section 多模型工作流端到端加速] and [Reuses Attention, the three-model workflow
+ * paragraph]: two downstream models share the attention state one upstream model produced.
+ * Receiver r computes exactly what mf_retrieve_prepared(ctx, bsr, W[r], H_r[r], vf[r],
+ * kv_head_map_host[r], O[r], stream) computes, bit for bit; the launch reads each kept block of
+ * the store from device memory once for all receivers instead of once per receiver.
+ *   n_recv            1..4
+ *   W, H_r, vf, kv_head_map_host, O   host arrays of n_recv entries; entry r has the meaning,
+ *                     layout and limits of the same argument of mf_retrieve_prepared
+ * All receivers share the head dimension d.  The heads of all receivers are cut into
+ * ceil(sum H_r / 24) near-equal runs, one workgroup per run and row tile; a run may hold heads
+ * of two receivers.  Outputs must not alias each other or any input.  Validation happens before
+ * any launch: on an error nothing is written.
+ */
+mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_recv, const float* const* W,
+                            const int32_t* H_r, const mf_vfrag* const* vf,
+                            const int32_t* const* kv_head_map_host, float* const* O,
+                            void* stream);
 
 /* mf_v_prepare into context scratch followed by mf_retrieve_prepared. */
 mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r, const void* V,

@@ -144,6 +144,43 @@ def test_retrieve_on_oracle_store(mf, case):
         assert_out_close(O2.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], kvm), "O_r (reversed kv map)")
 
 
+@pytest.mark.parametrize("case", [
+    # 14B-like sender fanned out to an 8B-like receiver (two head parts) and two small ones
+    dict(wl="varlen_14b8b", seed=2, lengths=[260, 45], H_s=40, d=128, recv=[(32, 8), (16, 2), (5, 5)]),
+    # 24 heads (one part) next to 48 heads (two parts), both at 3 heads per wave
+    dict(wl="pair_8b3b_8k", seed=5, lengths=[300], H_s=32, d=128, recv=[(24, 8), (48, 8)]),
+    # four receivers, B = 32, ragged lengths with a one-token sequence
+    dict(wl="tiny", seed=6, lengths=[90, 1, 75], H_s=16, d=64, recv=[(8, 2), (12, 4), (16, 8), (3, 1)]),
+])
+def test_retrieve_multi(mf, case):
+    """One launch for several receivers equals one retrieve per receiver, bit for bit, and the
+    oracle per receiver."""
+    wl = synth.WORKLOADS[case["wl"]]
+    H_s, d = case["H_s"], case["d"]
+    xs = [synth.make_layer_inputs(wl, case["seed"], layer=r, lengths=case["lengths"], H_s=H_s,
+                                  H_r=H_r, H_kv=H_kv, d=d)
+          for r, (H_r, H_kv) in enumerate(case["recv"])]
+    x = xs[0]
+    tau = _f32(wl.tau)
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B)
+    say(f"case: retrieve_multi {case} nnzb={len(ref.block_idx)}")
+    store = _upload_oracle_store(mf, ref, x)
+    recvs, singles = [], []
+    for xr in xs:
+        W = to_dev(xr["w"])
+        pv = mf.v_prepare(to_dev(xr["v_r"], wl.dtype), wl.B, cu_seqlens=xr["cu_seqlens"])
+        recvs.append((W, pv, xr["kv_head_map"]))
+        singles.append(mf.retrieve_prepared(store, W, pv, xr["kv_head_map"]))
+    outs = mf.retrieve_multi(store, recvs)
+    torch.cuda.synchronize()
+    for r, xr in enumerate(xs):
+        assert torch.equal(outs[r], singles[r]), f"receiver {r}"
+        assert_out_close(outs[r].cpu().numpy(), oracle.retrieve(ref, xr["w"], xr["v_r"], xr["kv_head_map"]),
+                         f"O_r receiver {r}")
+    with pytest.raises(RuntimeError):
+        mf.retrieve_multi(store, recvs[:1] * 5)          # more receivers than one launch takes
+
+
 def test_retrieve_paged_equals_contiguous_and_varlen_equals_per_sequence(mf):
     wl = synth.WORKLOADS["varlen_14b8b"]
     lengths = [300, 17, 129]

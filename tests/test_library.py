@@ -75,6 +75,9 @@ def test_invalid_arguments_rejected_before_any_gpu_work(lib):
     assert lib.mf_compress_into(None, None, None, 1, 64, 0.9, ctypes.byref(_lib.MfBsr()), None) == _lib.MF_ERR_INVALID
     # retrieve with missing pieces
     assert lib.mf_retrieve_prepared(None, ctypes.byref(_lib.MfBsr()), None, 2, None, None, None, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_retrieve_multi(None, ctypes.byref(_lib.MfBsr()), 1, None, None, None, None, None,
+                                 None) == _lib.MF_ERR_INVALID
+    assert "store" in lib.mf_last_error().decode()
     assert lib.mf_copy_probe(None, ctypes.c_void_p(16), ctypes.c_void_p(32), 15, None) == _lib.MF_ERR_INVALID
 
 
