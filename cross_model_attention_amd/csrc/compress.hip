@@ -140,9 +140,18 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
   __shared__ float s_lse[2][B];
 
-  // head-major grid: the key rows of the few heads in flight stay cache resident
-  const int h = blockIdx.x / n_pair;
-  const int pr = blockIdx.x % n_pair;
+  // head-major grid: the key rows of the few heads in flight stay cache resident.  With a multiple
+  // of 8 heads, head h runs on XCD h mod 8 (workgroup b runs on XCD b mod 8), so the workgroups
+  // in flight on one XCD sweep the keys of one head and share its L2.
+  int h, pr;
+  if ((H_s & 7) == 0) {
+    const int q = blockIdx.x >> 3;
+    h = (q / n_pair) * 8 + (blockIdx.x & 7);
+    pr = q % n_pair;
+  } else {
+    h = blockIdx.x / n_pair;
+    pr = blockIdx.x % n_pair;
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
   const int side = w / WR;                                 // 0: row I, 1: row I+1
   const int brow = pairs[2 * pr + side];                   // -1: the pair has one row
@@ -474,14 +483,15 @@ __device__ __forceinline__ void ktile_load(Frag<float, D>& f, const unsigned cha
 // head-slot rotation undone.  Each thread handles contiguous 16-byte pieces; the rotation of a
 // piece depends only on its row, which is uniform over a wave.
 template <int B>
-__device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned char* dst, int q, int NQ) {
+__device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned char* dst, int q, int NQ,
+                                            int w, int lane) {
   constexpr int PIECES = B * B / 512;              // pieces per thread per tile
   const int per = PIECES / NQ;
 #pragma unroll
   for (int u0 = 0; u0 < PIECES; ++u0) {
     if (u0 / per != q) continue;
-    const int piece = threadIdx.x + u0 * 512;
-    const int rot = ((piece / B) >> 2) & 3;
+    const int piece = 64 * w + lane + u0 * 512;
+    const int rot = (((64 * w + u0 * 512) / B) >> 2) & 3;   // uniform: a wave covers 1 or 2 rows of one group of 4
     const v4u x = *reinterpret_cast<const v4u*>(tile + piece * 16);
     v4u y;
     if (rot == 0) y = x;
@@ -516,7 +526,7 @@ __device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)
     else if (has_next) ktile_load<D>(kb[nt - 1], ktn + (nt - 1) * SB, lane);
     // a part of the previous block's tile goes out after the key loads, so no wait on a key
     // slice ever covers these stores (one counter, completed in issue order)
-    if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT);
+    if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT, w, lane);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       v4f sc = dot_tile<D>(qf[mt], kb[nt], zero4());
@@ -581,14 +591,28 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
 
   // work item (chunk k of a block row's kept list, head group, block row in LPT order), chunk
   // index slowest: the workgroups in flight sweep the same range of key blocks, whose tiles then
-  // stay in L2 for all of them
+  // stay in L2 for all of them.  When the head groups divide the 8 XCDs, each XCD (workgroup
+  // b runs on XCD b mod 8) serves one head group, so its L2 only holds that group's key tiles.
   const int HG = (H_s + 7) >> 3;
-  const int p = blockIdx.x % n_brow;
-  const int hg = (blockIdx.x / n_brow) % HG;
-  const int chunk = blockIdx.x / (n_brow * HG);
+  int p, hg, chunk;
+  if ((8 % HG) == 0) {
+    const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
+    const int nparts = 8 / HG, rp = (n_brow + nparts - 1) / nparts;
+    hg = xcd % HG;
+    chunk = q / rp;
+    p = (q % rp) * nparts + xcd / HG;
+    if (p >= n_brow) return;
+  } else {
+    p = blockIdx.x % n_brow;
+    hg = (blockIdx.x / n_brow) % HG;
+    chunk = blockIdx.x / (n_brow * HG);
+  }
   const int brow = order[p];
   const BrowInfo bi = load_info(info, brow);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
+  // the wave index is made scalar so that head-dependent choices (padding heads, masking) and the
+  // tile rotation branch on the scalar unit instead of through the execution mask
+  const int lane = threadIdx.x & 63, a = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rows = min(B, bi.n - bi.I * B);
   const int qdiag = bi.I * B;
   const int h = 8 * hg + w;
@@ -641,22 +665,27 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
     gather_block<T, B, D>(!active || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next,
                           J, active ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev, prev_dst);
+    {
+      // per-row sums over the block's 64 keys: lane c of group a ends with row 16 (c/4) + 4a + c%4
+      float flat[MT * 4];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = row16_sum(rs[mt][i]);
-        if (c == 0 && active) part[((size_t)t * H_s + h) * B + 16 * mt + 4 * a + i] = v;
-      }
+        for (int i = 0; i < 4; ++i) flat[4 * mt + i] = rs[mt][i];
+      const float v = row16_reduce_scatter<MT * 4>(flat, c);
+      if (active && c < MT * 4) part[((size_t)t * H_s + h) * B + 16 * (c >> 2) + 4 * a + (c & 3)] = v;
+    }
     __syncthreads();
     if (NBUF == 1) {                               // single buffer: stream now, then reuse
-      stream_tile<B>(tile, reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE, 0, 1);
+      stream_tile<B>(tile, reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE, 0, 1, w,
+                     lane);
       __syncthreads();
     }
   }
   if (NBUF == 2)                                   // the last block's tile
     stream_tile<B>(s_out[(t1 - 1 - t0) % NBUF],
-                   reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1);
+                   reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1, w,
+                   lane);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -695,7 +724,10 @@ static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
   const int HG = (a.H_s + 7) / 8;
   if (a.capacity == 0) return hipSuccess;
   const unsigned chunks = (unsigned)((a.nb_max + kGatherChunk - 1) / kGatherChunk);
-  hipLaunchKernelGGL((k_gather<T, B, D>), dim3((unsigned)a.n_brow * HG * chunks), dim3(512), 0, s, (const T*)a.Q,
+  // grid: with the XCD mapping, 8 XCDs x ceil(n_brow / (8 / HG)) block rows x chunks
+  const unsigned items = (8 % HG) == 0 ? 8u * (unsigned)((a.n_brow + 8 / HG - 1) / (8 / HG)) * chunks
+                                       : (unsigned)a.n_brow * HG * chunks;
+  hipLaunchKernelGGL((k_gather<T, B, D>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
                      (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.block_ptr, a.block_idx,
                      a.counters, a.capacity, a.lse2, a.scale2, (const unsigned char*)a.ktile, a.probs,
                      a.part);
