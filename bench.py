@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=16, help="block rows in the oracle sample")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the fused sender-prefill comparison run after the timed steps")
     p.add_argument("--no-fanout", action="store_true",
                    help="skip the multi-receiver retrieve comparison run after the timed steps")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
@@ -168,6 +170,41 @@ def fanout(mf, torch, wl, args, store, recvs, pvs, kv_map, B, cu, ctx, dev):
         res[name] = {"separate_ms": times["separate"], "fused_ms": times["fused"],
                      "saving": 1.0 - times["fused"] / times["separate"]}
         log(f"fan-out {name}: separate {times['separate']:.3f} ms, fused {times['fused']:.3f} ms")
+    return res
+
+
+def prefill(mf, torch, wl, args, send, store, tau, ctx, dev):
+    """Compression taken from the sender's own prefill: on one mapped layer, time the plain
+    compress, the sender's causal attention alone (mf_dense_attention over its heads), and the
+    fused pass that gives both (mf_compress_prefill_into)."""
+    Q, K = send
+    H_s, L, d = Q.shape
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed + 11)
+    V = torch.randn((L, H_s, d), generator=g, device=dev).to(Q.dtype)
+    Qt, Kt = Q.transpose(0, 1).contiguous(), K.transpose(0, 1).contiguous()
+    O = torch.empty((L, H_s, d), dtype=torch.float32, device=dev)
+    ident = list(range(H_s))
+    runs = {
+        "compress_ms": lambda: mf.compress_into(store, Q, K, tau),
+        "sender_attention_ms": lambda: mf.dense_attention(Qt, Kt, V, ident, out=O, ctx=ctx),
+        "fused_prefill_ms": lambda: mf.compress_prefill_into(store, Q, K, V, tau, out=O),
+    }
+    res = {}
+    for name, fn in runs.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(3):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / 3
+    res["compress_added_to_prefill_ms"] = res["fused_prefill_ms"] - res["sender_attention_ms"]
+    log(f"prefill: compress {res['compress_ms']:.2f} ms, sender attention {res['sender_attention_ms']:.2f} ms, "
+        f"fused {res['fused_prefill_ms']:.2f} ms")
+    del Qt, Kt, V, O
     return res
 
 
@@ -368,6 +405,9 @@ def main():
         ms = e0.elapsed_time(e1) / reps
         out["hbm_copy_probe"] = {"bytes_moved": 2 * n * 4, "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}
         del src, dst
+
+    if not args.no_prefill and n_map >= 1:
+        out["prefill"] = prefill(mf, torch, wl, args, send[mapped[-1]], slots[(n_map - 1) % k], tau, ctx, dev)
 
     if not args.no_fanout and n_map >= 2:
         out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [recv[l] for l in mapped[-2:]],

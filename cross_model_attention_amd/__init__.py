@@ -11,6 +11,7 @@ from .mapflow import (  # noqa: F401
     check_layer_map,
     compress,
     compress_into,
+    compress_prefill_into,
     copy_probe,
     dense_attention,
     map_layers,

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "mf_bsr_free": (c_int, [c_void_p, POINTER(MfBsr)]),
     "mf_compress_into": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_float,
                                  POINTER(MfBsr), c_void_p]),
+    "mf_compress_prefill_into": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int32, c_float,
+                                         POINTER(MfBsr), c_void_p, c_void_p]),
     "mf_bsr_sync": (c_int, [c_void_p, POINTER(MfBsr), c_void_p]),
     "mf_compress": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32, _P_I32, c_int32,
                             c_float, c_int32, c_void_p, POINTER(MfBsr)]),

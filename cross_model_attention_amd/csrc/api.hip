@@ -151,6 +151,7 @@ struct mf_ctx {
   Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
+  mf_vfrag vf_prefill{};    // context-owned prepared sender V (mf_compress_prefill_into)
   // cached device copies of the dense-attention geometry
   Scratch dense_tables;
   std::vector<int32_t> dense_cu;
@@ -461,6 +462,7 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
     if (s->p) (void)hipFree(s->p);
   vfrag_release(&ctx->vf_retrieve);
   vfrag_release(&ctx->vf_dense);
+  vfrag_release(&ctx->vf_prefill);
   delete ctx;
   return MF_OK;
 }
@@ -637,6 +639,29 @@ MF_EXPORT mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, 
   if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
+  MF_HIP(mf::compress_fill(a, s), "compress gather launch");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const void* K, const void* V,
+                                             mf_dtype dtype, int32_t d, float tau, mf_bsr* bsr, float* O,
+                                             void* stream) {
+  mf_status st = validate_compress(Q, K, dtype, d, tau, bsr);
+  if (st != MF_OK) return st;
+  if (!V || !O) return fail(MF_ERR_INVALID, "V or O is NULL");
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  if (bsr->n_brow == 0) return MF_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
+  st = vfrag_prepare(ctx, bo->geom.cu.data(), bsr->n_seq, bsr->B, V, dtype, bsr->H_s, d, nullptr, 0, 0,
+                     &ctx->vf_prefill, true, s);
+  if (st != MF_OK) return st;
+  mf::CompressArgs a;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  a.attn_vfrag = ctx->vf_prefill.frag;
+  a.attn_vexps = ctx->vf_prefill.exps;
+  a.attn_out = O;
+  MF_HIP(mf::compress_plan(a, s), "fused prefill statistics / selection launch");
   MF_HIP(mf::compress_fill(a, s), "compress gather launch");
   return MF_OK;
 }
@@ -896,11 +921,15 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
   if (g.n_brow == 0) return MF_OK;
   // geometry tables (info, order) cached on the device while cu_seqlens stays the same
   if (ctx->dense_cu != g.cu) {
-    if ((st = ensure(ctx->dense_tables, (size_t)g.n_brow * 20 + 512, "dense geometry")) != MF_OK) return st;
+    const size_t o_order = align_up((size_t)g.n_brow * 16, 256);
+    const size_t o_pairs = align_up(o_order + (size_t)g.n_brow * 4, 256);
+    if ((st = ensure(ctx->dense_tables, o_pairs + (size_t)g.n_pair * 8 + 256, "dense geometry")) != MF_OK) return st;
     char* base = static_cast<char*>(ctx->dense_tables.p);
     MF_HIP(hipMemcpy(base, g.info.data(), (size_t)g.n_brow * 16, hipMemcpyHostToDevice), "uploading geometry");
-    MF_HIP(hipMemcpy(base + align_up((size_t)g.n_brow * 16, 256), g.order.data(), (size_t)g.n_brow * 4,
-                     hipMemcpyHostToDevice), "uploading geometry");
+    MF_HIP(hipMemcpy(base + o_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice),
+           "uploading geometry");
+    MF_HIP(hipMemcpy(base + o_pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice),
+           "uploading geometry");
     ctx->dense_cu = g.cu;
     ctx->dense_nbrow = g.n_brow;
   }
@@ -918,6 +947,9 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
   a.n_brow = g.n_brow;
   a.info = reinterpret_cast<const int32_t*>(base);
   a.order = reinterpret_cast<const int32_t*>(base + align_up((size_t)g.n_brow * 16, 256));
+  a.pairs = reinterpret_cast<const int32_t*>(
+      base + align_up(align_up((size_t)g.n_brow * 16, 256) + (size_t)g.n_brow * 4, 256));
+  a.n_pair = g.n_pair;
   a.vfrag = ctx->vf_dense.frag;
   a.vexps = ctx->vf_dense.exps;
   a.hm = hm;

@@ -21,129 +21,15 @@
 // scale.
 #include "common.h"
 #include "kernels.h"
+#include "sweep.h"
 
 namespace mf {
 
-// One lane's slice of a 16-row x D operand tile (rows are queries or keys, K-dim = head dim).
-template <typename T, int D>
-struct Frag;
-
-template <int D>
-struct Frag<uint16_t, D> {
-  static constexpr int N = D / 32;
-  v8s v[N];
-  __device__ __forceinline__ void load(const uint16_t* row, bool valid, int a) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = valid ? as_v8s(ld16(row + 32 * k + 8 * a)) : as_v8s(zero_u4());
-  }
-};
-
-template <int D>
-struct Frag<float, D> {
-  static constexpr int N = D / 4;
-  float v[N];
-  __device__ __forceinline__ void load(const float* row, bool valid, int a) {
-#pragma unroll
-    for (int k = 0; k < N; ++k) v[k] = valid ? row[4 * k + a] : 0.f;
-  }
-};
-
-// acc += A B^T over the head dimension, A and B both 16-row fragments.
-template <int D>
-__device__ __forceinline__ v4f dot_tile(const Frag<uint16_t, D>& A, const Frag<uint16_t, D>& B, v4f acc) {
-#pragma unroll
-  for (int k = 0; k < Frag<uint16_t, D>::N; ++k) acc = mfma_bf16(A.v[k], B.v[k], acc);
-  return acc;
-}
-template <int D>
-__device__ __forceinline__ v4f dot_tile(const Frag<float, D>& A, const Frag<float, D>& B, v4f acc) {
-#pragma unroll
-  for (int k = 0; k < Frag<float, D>::N; ++k) acc = mfma_f32(A.v[k], B.v[k], acc);
-  return acc;
-}
-
-constexpr float kNegInf = -__builtin_inff();
-
-template <int D>
-__device__ __forceinline__ void load_lds_frag(Frag<uint16_t, D>& f, const unsigned char* row, int a) {
-#pragma unroll
-  for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
-    f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(row + (32 * k + 8 * a) * 2));
-}
-template <int D>
-__device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned char* row, int a) {
-#pragma unroll
-  for (int k = 0; k < Frag<float, D>::N; ++k) f.v[k] = *reinterpret_cast<const float*>(row + (4 * k + a) * 4);
-}
-
-
-// ------------------------------------------------------------------------------------------
-// k_stats: one workgroup per (pair of consecutive block rows I, I+1 of one sequence, sender
-// head), 2 B/32 waves; the waves of each row own 32 of its queries (two 16-query tiles), so each
-// key fragment read from LDS serves 32 queries, and each key tile staged in LDS serves both rows.
-// One pass over the key blocks 0..I+1: each block's key tile is staged in LDS (fetched two
-// blocks ahead, double buffered), scores are formed transposed (keys x queries) on MFMA, and for
-// every (query i, key block J) the block-local maximum r_iJ and z_iJ = sum_{j in J} 2^(s_ij c -
-// r_iJ) are stored (c folds log2(e) / sqrt(d)), while each lane keeps the running row logsumexp
-// (fp64) of its queries.  Exactly as a softmax over the row would:
-//     lse2_i   = log2 sum_J z_iJ 2^(r_iJ)                       (row logsumexp, base 2)
-//     M_h[I,J] = sum_{i in I} z_iJ 2^(r_iJ - lse2_i)            (block mass of head h)
-// the second sum in fp64, one coalesced read of the stored pairs per block and wave: one
-// exponential per score instead of two, and one score pass instead of two.
-// ------------------------------------------------------------------------------------------
-// Statistics of one (query, key block) pair from the transposed score tiles s[mt] (lane (a, c):
-// keys 16 mt + 4 a + i of the block, query c): block maximum r (scaled, base 2) and
-// z = sum_j 2^(s_j c - r).  MASKED: keys with (key - query) > 0 are invisible, as is every key of
-// a query beyond the sequence; kq = first key of the lane minus the query.
-template <int MT, bool MASKED>
-__device__ __forceinline__ float2 block_stats(v4f (&s)[MT], int kq, bool qvalid, float scale2) {
-  if (MASKED) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!(qvalid && kq + 16 * mt + i <= 0)) s[mt][i] = kNegInf;
-  }
-  float bm = kNegInf;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-    bm = __builtin_fmaxf(bm, __builtin_fmaxf(__builtin_fmaxf(s[mt][0], s[mt][1]), __builtin_fmaxf(s[mt][2], s[mt][3])));
-  bm = xrow_max(bm);
-  const bool none = MASKED && bm == kNegInf;            // nothing visible: z = 0
-  const float r = none ? 0.f : bm * scale2;
-  float z = 0.f;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z += fast_exp2(fmaf(s[mt][i], scale2, -r));
-  z = xrow_sum(z);
-  return make_float2(z, none ? kNegInf : r);
-}
-
-template <typename T, int B, int D>
-__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_stats(const T* __restrict__ Q, const T* __restrict__ K,
-                                                 int H_s, int64_t T_tot,
-                                                 const int32_t* __restrict__ info,
-                                                 const int32_t* __restrict__ pairs, int n_pair,
-                                                 const int32_t* __restrict__ coff, int64_t n_causal,
-                                                 int n_brow, int nb_max, float scale2,
-                                                 float2* __restrict__ zbuf,
-                                                 float* __restrict__ lse2,
-                                                 float* __restrict__ Mh) {
-  constexpr int WR = B / 32;                               // waves per block row
-  constexpr int MT = B / 16;                               // 16-key tiles per block
-  constexpr int QT = 2;                                    // 16-query tiles per wave
-  constexpr int NTHR = B * 4;
-  constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
-  constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int CPT = B * CPR / NTHR;
-  __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
-  __shared__ float s_lse[2][B];
-
-  // head-major grid: the key rows of the few heads in flight stay cache resident.  With a multiple
-  // of 8 heads, head h runs on XCD h mod 8 (workgroup b runs on XCD b mod 8), so the workgroups
-  // in flight on one XCD sweep the keys of one head and share its L2.
-  int h, pr;
+// Work item of the statistics grid: head-major, so the key rows of the few heads in flight stay
+// cache resident.  With a multiple of 8 heads, head h runs on XCD h mod 8 (workgroup b runs on
+// XCD b mod 8), so the workgroups in flight on one XCD sweep the keys of one head and share its
+// L2.
+__device__ __forceinline__ void stats_item(int H_s, int n_pair, int& h, int& pr) {
   if ((H_s & 7) == 0) {
     const int q = blockIdx.x >> 3;
     h = (q / n_pair) * 8 + (blockIdx.x & 7);
@@ -152,108 +38,34 @@ __global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void
     h = blockIdx.x / n_pair;
     pr = blockIdx.x % n_pair;
   }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
-  const int side = w / WR;                                 // 0: row I, 1: row I+1
-  const int brow = pairs[2 * pr + side];                   // -1: the pair has one row
-  const BrowInfo b0 = load_info(info, pairs[2 * pr]);
-  const int Jend = pairs[2 * pr + 1] >= 0 ? b0.I + 1 : b0.I;  // last key block of the sweep
-  const bool mine = brow >= 0;
-  const BrowInfo bi = mine ? load_info(info, brow) : b0;
-  const int rows = mine ? min(B, bi.n - bi.I * B) : 0;
-  const bool partial = rows < B;
-  const int q0 = 32 * (w % WR);                            // first query of this wave in its row
-  const unsigned char* Kh = reinterpret_cast<const unsigned char*>(K + (size_t)h * T_tot * D + (size_t)b0.seq0 * D);
-  float2* zrow = zbuf + ((size_t)h * n_causal + (mine ? coff[brow] : 0)) * B;
+}
 
-  Frag<T, D> qf[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    const int qr = q0 + 16 * qt + c;
-    qf[qt].load(Q + (size_t)h * T_tot * D + (size_t)(bi.tok0 + qr) * D, qr < rows, a);
-  }
+template <typename T, int B, int D>
+__global__ __launch_bounds__(B * 4) __attribute__((amdgpu_waves_per_eu(4))) void k_stats(
+    const T* __restrict__ Q, const T* __restrict__ K, int H_s, int64_t T_tot, const int32_t* __restrict__ info,
+    const int32_t* __restrict__ pairs, int n_pair, const int32_t* __restrict__ coff, int64_t n_causal, int n_brow,
+    int nb_max, float scale2, float2* __restrict__ zbuf, float* __restrict__ lse2, float* __restrict__ Mh) {
+  int h, pr;
+  stats_item(H_s, n_pair, h, pr);
+  const SweepHead<T> hd{Q + (size_t)h * T_tot * D, D, K + (size_t)h * T_tot * D, D, h, nullptr, 0};
+  sweep_body<T, B, D, false, true>(hd, h, pr, T_tot, info, pairs, coff, n_causal, n_brow, nb_max, scale2, zbuf,
+                                   lse2, Mh, AttnOut{nullptr, nullptr});
+}
 
-  // key tiles: registers -> LDS, fetched two blocks ahead (LDS double buffered)
-  auto fetch_k = [&](v4u (&kst)[CPT], int J) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int piece = threadIdx.x + u * NTHR;
-      const int row = piece / CPR, col = piece % CPR;
-      const int key = J * B + row;
-      kst[u] = key < b0.n ? ld16(Kh + (size_t)key * D * sizeof(T) + col * 16) : zero_u4();
-    }
-  };
-  auto stage_k = [&](const v4u (&kst)[CPT], int buf) {
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int piece = threadIdx.x + u * NTHR;
-      *reinterpret_cast<v4u*>(&s_k[buf][(piece / CPR) * ROWB + (piece % CPR) * 16]) = kst[u];
-    }
-  };
-
-  // running base-2 logsumexp of this lane's queries (every row a of the wave holds the same ones)
-  float m_run[QT];
-  double l_run[QT];
-#pragma unroll
-  for (int qt = 0; qt < QT; ++qt) {
-    m_run[qt] = kNegInf;
-    l_run[qt] = 0.0;
-  }
-  v4u kst[CPT];
-  auto block = [&](int J) {
-    if (J + 1 <= Jend) fetch_k(kst, J + 1);
-    if (mine && J <= bi.I) {
-      const unsigned char* kt = s_k[J & 1];
-      v4f s[QT][MT];
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        Frag<T, D> kf;
-        load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) s[qt][mt] = dot_tile<D>(kf, qf[qt], zero4());
-      }
-      // only the diagonal block and blocks of a partial row need the causal / length mask
-      const bool masked = J == bi.I || partial;
-#pragma unroll
-      for (int qt = 0; qt < QT; ++qt) {
-        const int qr = q0 + 16 * qt + c;
-        const int qloc = bi.I * B + qr;
-        const float2 zr = masked ? block_stats<MT, true>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
-                                 : block_stats<MT, false>(s[qt], 0, true, scale2);
-        if (a == 0) zrow[(size_t)J * B + qr] = zr;
-        if (zr.x > 0.f) {
-          const float mn = __builtin_fmaxf(m_run[qt], zr.y);
-          l_run[qt] = l_run[qt] * (double)fast_exp2(m_run[qt] - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
-          m_run[qt] = mn;
-        }
-      }
-    }
-    if (J + 1 <= Jend) stage_k(kst, (J + 1) & 1);
-    __syncthreads();
-  };
-  fetch_k(kst, 0);
-  stage_k(kst, 0);
-  __syncthreads();
-  for (int J = 0; J <= Jend; ++J) block(J);
-  // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
-  if (mine && a == 0) {
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-      const int qr = q0 + 16 * qt + c;
-      const float v = (float)((double)m_run[qt] + log2(l_run[qt]));
-      s_lse[side][qr] = v;
-      if (qr < rows) lse2[(size_t)h * T_tot + bi.tok0 + qr] = v;
-    }
-  }
-  __syncthreads();                                         // every wave reaches it
-  if (!mine) return;
-  float* out = Mh + ((size_t)h * n_brow + brow) * nb_max;
-  const float lq = lane < rows ? s_lse[side][lane] : 0.f;
-  for (int J = w % WR; J <= bi.I; J += WR) {
-    const float2 e = lane < B ? zrow[(size_t)J * B + lane] : make_float2(0.f, kNegInf);
-    const double v = (lane < rows && e.y > kNegInf) ? (double)e.x * (double)fast_exp2(e.y - lq) : 0.0;
-    const double t = wave_sum_f64(v);
-    if (lane == 0) out[J] = (float)t;
-  }
+// The fused prefill: the same statistics (bit for bit: the same code computes them) plus the
+// sender's own causal attention output [T][H_s][D] from the same scores.
+template <typename T, int B, int D>
+__global__ __launch_bounds__(B * 4) void k_prefill(
+    const T* __restrict__ Q, const T* __restrict__ K, int H_s, int64_t T_tot, const int32_t* __restrict__ info,
+    const int32_t* __restrict__ pairs, int n_pair, const int32_t* __restrict__ coff, int64_t n_causal, int n_brow,
+    int nb_max, float scale2, float2* __restrict__ zbuf, float* __restrict__ lse2, float* __restrict__ Mh,
+    AttnOut ao, float* __restrict__ O) {
+  int h, pr;
+  stats_item(H_s, n_pair, h, pr);
+  const SweepHead<T> hd{Q + (size_t)h * T_tot * D, D, K + (size_t)h * T_tot * D, D, h, O + (size_t)h * D,
+                        (int64_t)H_s * D};
+  sweep_body<T, B, D, true, true>(hd, h, pr, T_tot, info, pairs, coff, n_causal, n_brow, nb_max, scale2, zbuf,
+                                  lse2, Mh, ao);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -713,9 +525,16 @@ bool compress_supported(int dtype, int B, int d) {
 
 template <typename T, int B, int D>
 static hipError_t plan_t(const CompressArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_pair * a.H_s), dim3(B * 4), 0, s,
-                     (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.pairs, a.n_pair, a.coff,
-                     a.n_causal, a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh);
+  if (a.attn_out) {
+    hipLaunchKernelGGL((k_prefill<T, B, D>), dim3((unsigned)a.n_pair * a.H_s), dim3(B * 4), 0, s,
+                       (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.pairs, a.n_pair, a.coff,
+                       a.n_causal, a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh,
+                       AttnOut{a.attn_vfrag, a.attn_vexps}, a.attn_out);
+  } else {
+    hipLaunchKernelGGL((k_stats<T, B, D>), dim3((unsigned)a.n_pair * a.H_s), dim3(B * 4), 0, s,
+                       (const T*)a.Q, (const T*)a.K, a.H_s, a.T, a.info, a.pairs, a.n_pair, a.coff,
+                       a.n_causal, a.n_brow, a.nb_max, a.scale2, a.zbuf, a.lse2, a.Mh);
+  }
   return hipGetLastError();
 }
 

@@ -31,6 +31,11 @@ struct CompressArgs {
   int32_t* counts;       // [n_brow]
   float* part;           // [capacity][H_s][B] per-block row sums of stored probs
   void* ktile;           // [H_s][n_brow][B/16][fragment elements][64 lanes] key operands
+  // fused prefill (attn_out != NULL): the statistics pass also writes the sender's own causal
+  // attention output [T][H_s][d] fp32, from V prepared per sender head (fp16 tiles, exponents)
+  const uint16_t* attn_vfrag;
+  const int32_t* attn_vexps;
+  float* attn_out;
   // the store
   int32_t* block_ptr;
   int32_t* block_idx;
@@ -109,6 +114,8 @@ struct DenseArgs {
   int n_brow;            // 64-token block rows
   const int32_t* info;
   const int32_t* order;
+  const int32_t* pairs;  // [n_pair][2] block rows (I, I+1) of one sequence, second may be -1
+  int n_pair;
   const uint16_t* vfrag; // prepared V with B = 64
   const int32_t* vexps;
   HeadMap hm;

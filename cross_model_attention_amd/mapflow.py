@@ -260,6 +260,22 @@ def compress_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, tau: floa
                               float(tau), ctypes.byref(store.raw), _stream(stream)))
 
 
+def compress_prefill_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tau: float,
+                          out=None, stream=None) -> torch.Tensor:
+    """mf_compress_prefill_into: the sender's causal attention O [T, H_s, d] fp32 and the store,
+    from one pass over the scores.  V: [T, H_s, d], dtype as Q."""
+    _check_qk(Q, K)
+    H_s, T, d = Q.shape
+    if H_s != store.raw.H_s or T != store.raw.T:
+        raise ValueError("Q/K shape does not match the store's geometry")
+    if V.shape != (T, H_s, d) or V.dtype != Q.dtype:
+        raise ValueError("V must be [T, H_s, d] with Q's dtype")
+    out = _out(out, T, H_s, d, Q)
+    check(_L.mf_compress_prefill_into(store.ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dtype(Q), int(d),
+                                      float(tau), ctypes.byref(store.raw), _dev(out, "out"), _stream(stream)))
+    return out
+
+
 def _paged(page_table, page_size):
     if page_table is None:
         return None, 0, 0

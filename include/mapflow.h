@@ -191,6 +191,26 @@ mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr);
 mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype, int32_t d,
                            float tau, mf_bsr* bsr, void* stream);
 
+/*
+ * The sender's own prefill attention and the compression of its map in one pass over the scores.
+ * [MapFlow开源, section 只存重要的:块稀疏压缩]: the map is compressed without first assembling the
+ * dense matrix; here the score tiles that the sender's causal attention forms anyway also give
+ * the block statistics, so no separate statistics pass runs.
+ * Fills *bsr exactly as mf_compress_into(ctx, Q, K, dtype, d, tau, bsr, stream) does, bit for bit
+ * (the statistics come from the same code), and also writes
+ *     O[i, h, :] = sum_j softmax_j(q_i . k_j / sqrt(d), j <= i within i's sequence) V[j, h, :]
+ *   Q, K   [H_s][T][d] as for mf_compress_into
+ *   V      sender values, [T][H_s][d] (one value head per sender head), dtype as Q
+ *   O      fp32 [T][H_s][d] device; must not alias any input
+ * Probabilities enter the P.V product as fp16 scaled by 2^15 and V as fp16 with a power-of-two
+ * scale per head (as in mf_dense_attention); sums are fp32.  The prepared V lives in context
+ * scratch (may allocate on the first call of a size).  Errors as mf_compress_into, plus
+ * MF_ERR_INVALID for a NULL V or O.
+ */
+mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const void* K, const void* V,
+                                   mf_dtype dtype, int32_t d, float tau, mf_bsr* bsr, float* O,
+                                   void* stream);
+
 /* Wait for `stream`, read the kept-block count into bsr->nnzb; MF_ERR_CAPACITY on overflow. */
 mf_status mf_bsr_sync(mf_ctx* ctx, mf_bsr* bsr, void* stream);
 

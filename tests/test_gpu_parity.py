@@ -181,6 +181,35 @@ def test_retrieve_multi(mf, case):
         mf.retrieve_multi(store, recvs[:1] * 5)          # more receivers than one launch takes
 
 
+@pytest.mark.parametrize("case", [
+    dict(wl="tiny", seed=8, lengths=[90, 1, 75], H_s=4, d=64, dtype="f32"),
+    dict(wl="pair_8b3b_8k", seed=9, lengths=[200, 70], H_s=8, d=128, dtype="bf16"),
+    dict(wl="pair_8b3b_8k", seed=10, lengths=[129], H_s=16, d=64, dtype="bf16"),
+])
+def test_compress_prefill(mf, case):
+    """The fused sender prefill fills the store bit for bit like the plain compress, and its
+    attention output matches the oracle's causal attention of the sender heads."""
+    wl = synth.WORKLOADS[case["wl"]]
+    H_s, d = case["H_s"], case["d"]
+    x = synth.make_layer_inputs(wl, case["seed"], lengths=case["lengths"], H_s=H_s, H_r=2, H_kv=1, d=d)
+    v = synth.make_dense_inputs(wl, case["seed"], layer=1, lengths=case["lengths"], H_q=H_s, H_kv=H_s, d=d)["v"]
+    tau = _f32(wl.tau)
+    say(f"case: prefill {case}")
+    Q, K, V = to_dev(x["q_s"], case["dtype"]), to_dev(x["k_s"], case["dtype"]), to_dev(v, case["dtype"])
+    plain = mf.BlockStore.create(H_s, wl.B, x["cu_seqlens"])
+    fused = mf.BlockStore.create(H_s, wl.B, x["cu_seqlens"])
+    mf.compress_into(plain, Q, K, tau)
+    O = mf.compress_prefill_into(fused, Q, K, V, tau)
+    plain.sync()
+    fused.sync()
+    hp, hf = plain.to_host(), fused.to_host()
+    for key in ["block_ptr", "block_idx", "probs_bits", "row_kept_mass"]:
+        assert np.array_equal(hp[key], hf[key]), key
+    ref = oracle.dense_causal_attention(x["q_s"].transpose(1, 0, 2), x["k_s"].transpose(1, 0, 2), v,
+                                        x["cu_seqlens"], list(range(H_s)))
+    assert_out_close(O.cpu().numpy(), ref, "sender O")
+
+
 def test_retrieve_paged_equals_contiguous_and_varlen_equals_per_sequence(mf):
     wl = synth.WORKLOADS["varlen_14b8b"]
     lengths = [300, 17, 129]
