@@ -44,10 +44,11 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=16, help="block rows in the oracle sample")
-    p.add_argument("--no-prefill", action="store_true",
-                   help="skip the fused sender-prefill comparison run after the timed steps")
-    p.add_argument("--no-fanout", action="store_true",
-                   help="skip the multi-receiver retrieve comparison run after the timed steps")
+    p.add_argument("--extras", action="store_true",
+                   help="after the timed steps, also compare the fused sender prefill with the plain "
+                        "compress, and multi-receiver retrieves with separate ones (extra objects "
+                        "'prefill' and 'fanout'); off by default so that the kernel trace of a default "
+                        "run holds only the step's launches")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
                    help="size of the HBM copy probe run after the timed steps (0 = skip)")
     return p.parse_args()
@@ -406,10 +407,10 @@ def main():
         out["hbm_copy_probe"] = {"bytes_moved": 2 * n * 4, "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}
         del src, dst
 
-    if not args.no_prefill and n_map >= 1:
+    if args.extras and n_map >= 1:
         out["prefill"] = prefill(mf, torch, wl, args, send[mapped[-1]], slots[(n_map - 1) % k], tau, ctx, dev)
 
-    if not args.no_fanout and n_map >= 2:
+    if args.extras and n_map >= 2:
         out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [recv[l] for l in mapped[-2:]],
                                [pv[l] for l in mapped[-2:]], kv_map, B, cu, ctx, dev)
 
