@@ -8,6 +8,7 @@ from .mapflow import (  # noqa: F401
     BlockStore,
     Context,
     PreparedV,
+    PrefixCache,
     check_layer_map,
     compress,
     compress_into,
@@ -16,6 +17,7 @@ from .mapflow import (  # noqa: F401
     dense_attention,
     map_layers,
     probs_canonical_to_store,
+    prefix_hashes,
     probs_store_to_canonical,
     retrieve,
     retrieve_multi,

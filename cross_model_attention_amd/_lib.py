@@ -4,7 +4,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_uint16, c_void_p
+from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_uint16, c_uint64, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmapflow.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mapflow.h")
@@ -18,7 +18,7 @@ STATUS_NAMES = {0: "MF_OK", 1: "MF_ERR_INVALID", 2: "MF_ERR_UNSUPPORTED", 3: "MF
 class MfBsr(ctypes.Structure):
     _fields_ = [
         ("B", c_int32), ("H_s", c_int32), ("n_seq", c_int32), ("n_brow", c_int32),
-        ("nb_max", c_int32), ("_pad", c_int32), ("T", c_int64), ("n_causal", c_int64),
+        ("nb_max", c_int32), ("n_order", c_int32), ("T", c_int64), ("n_causal", c_int64),
         ("capacity", c_int64), ("nnzb", c_int64),
         ("brow_info", c_void_p), ("brow_order", c_void_p), ("brow_coff", c_void_p),
         ("block_ptr", c_void_p),
@@ -43,6 +43,7 @@ _SIGNATURES = {
     "mf_map_layers": (c_int, [c_int32, c_int32, c_int32, _P_I32]),
     "mf_check_layer_map": (c_int, [_P_I32, c_int32, c_int32, c_int32]),
     "mf_bsr_create": (c_int, [c_void_p, c_int32, c_int32, _P_I32, c_int32, c_int64, POINTER(MfBsr)]),
+    "mf_bsr_create_range": (c_int, [c_void_p, c_int32, c_int32, _P_I32, c_int32, _P_I32, c_int64, POINTER(MfBsr)]),
     "mf_bsr_download": (c_int, [c_void_p, POINTER(MfBsr), _P_I32, _P_I32, POINTER(c_uint16),
                                 POINTER(c_float)]),
     "mf_bsr_download_blocks": (c_int, [c_void_p, POINTER(MfBsr), c_int64, c_int64, _P_I32, POINTER(c_uint16)]),
@@ -68,6 +69,12 @@ _SIGNATURES = {
     "mf_dense_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32,
                                    c_int32, _P_I32, c_int32, _P_I32, c_void_p, c_void_p]),
     "mf_copy_probe": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mf_prefix_hashes": (c_int, [_P_I32, c_int64, c_int32, POINTER(c_uint64)]),
+    "mf_cache_create": (c_int, [c_void_p, c_int64, POINTER(c_void_p)]),
+    "mf_cache_destroy": (c_int, [c_void_p]),
+    "mf_cache_info": (c_int, [c_void_p, POINTER(c_int64), POINTER(c_int64)]),
+    "mf_cache_insert": (c_int, [c_void_p, c_int32, _P_I32, c_int64, c_int32, POINTER(MfBsr), c_int32, c_void_p]),
+    "mf_cache_lookup": (c_int, [c_void_p, c_int32, _P_I32, c_int64, c_int32, POINTER(c_int32), POINTER(MfBsr)]),
 }
 
 _lib = None

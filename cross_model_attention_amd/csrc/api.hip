@@ -8,7 +8,9 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <memory>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/mapflow.h"
@@ -50,10 +52,18 @@ struct Geometry {
   std::vector<int32_t> coff;      // [n_brow] causal blocks of all earlier block rows
   std::vector<int32_t> pairs;     // [n_pair][2] block rows (I, I+1) of one sequence (-1: none)
   std::vector<int32_t> cu;        // copy of cu_seqlens
+  std::vector<int32_t> row_begin; // [n_seq] first block row compressed / retrieved per sequence
+  std::vector<uint8_t> active;    // [n_brow] row >= its sequence's row_begin
   int n_pair = 0;
+  int n_order = 0;                // active rows (the entries of order)
+  bool ranged = false;            // some row_begin > 0
 };
 
-mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& g) {
+// Block-row geometry of a packed batch.  row_begin (per sequence, NULL = all 0) restricts the rows
+// that are compressed and retrieved to I >= row_begin[s] (chunked prefill); every row still
+// exists as a key block row.
+mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& g,
+                         const int32_t* row_begin = nullptr) {
   if (cu == nullptr) return fail(MF_ERR_INVALID, "cu_seqlens_host is NULL");
   if (n_seq < 1) return fail(MF_ERR_INVALID, "n_seq must be >= 1 (got %d)", n_seq);
   if (B != 16 && B != 32 && B != 64 && B != 128)
@@ -68,26 +78,34 @@ mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& 
       return fail(MF_ERR_INVALID, "cu_seqlens must be non-decreasing (entry %d)", s + 1);
     const int n = cu[s + 1] - cu[s];
     const int nb = (n + B - 1) / B;
+    const int rb = row_begin ? row_begin[s] : 0;
+    if (rb < 0 || rb > nb)
+      return fail(MF_ERR_INVALID, "row_begin[%d] = %d outside [0, %d]", s, rb, nb);
+    g.row_begin.push_back(rb);
+    g.ranged |= rb > 0;
     g.nb_max = std::max(g.nb_max, nb);
     g.n_causal += (int64_t)nb * (nb + 1) / 2;
     for (int I = 0; I < nb; ++I) {
       g.info.insert(g.info.end(), {cu[s] + I * B, cu[s], n, I});
       g.brow_seq.push_back(s);
+      g.active.push_back(I >= rb ? 1 : 0);
       g.coff.push_back((int32_t)std::min<int64_t>(g.n_causal - (int64_t)nb * (nb + 1) / 2 + (int64_t)I * (I + 1) / 2,
                                                   INT32_MAX));
     }
   }
   g.T = cu[n_seq];
   g.n_brow = (int)g.brow_seq.size();
-  g.order.resize(g.n_brow);
-  for (int b = 0; b < g.n_brow; ++b) g.order[b] = b;
+  for (int b = 0; b < g.n_brow; ++b)
+    if (g.active[b]) g.order.push_back(b);
+  g.n_order = (int)g.order.size();
   std::stable_sort(g.order.begin(), g.order.end(), [&](int x, int y) {
     return g.info[4 * x + 3] > g.info[4 * y + 3];
   });
-  // pairs of consecutive block rows of one sequence, the one with the larger row first
+  // pairs of consecutive active block rows of one sequence (from its first active row), the one
+  // with the larger row first
   std::vector<std::pair<int, int>> pr;
   for (int b = 0; b < g.n_brow; ++b) {
-    if (g.info[4 * b + 3] % 2 != 0) continue;
+    if (!g.active[b] || (g.info[4 * b + 3] - g.row_begin[g.brow_seq[b]]) % 2 != 0) continue;
     const bool has_next = b + 1 < g.n_brow && g.brow_seq[b + 1] == g.brow_seq[b];
     pr.emplace_back(b, has_next ? b + 1 : -1);
   }
@@ -131,6 +149,8 @@ struct BsrOwner {
   void* meta = nullptr;
   void* data = nullptr;
   int32_t* pairs = nullptr;       // device copy of geom.pairs (inside meta)
+  uint8_t* active = nullptr;      // device copy of geom.active when the store is ranged (inside meta)
+  bool cache_owned = false;       // an entry of an mf_cache: freed by the cache only
   Geometry geom;
 };
 
@@ -182,7 +202,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
   const size_t o_cnt = align_up(o_rkm + (size_t)H_s * g.T * 4, 256);
   const size_t o_pairs = o_cnt + 256;
-  const size_t total = align_up(o_pairs + (size_t)g.n_pair * 8, 256) + 256;
+  const size_t o_active = align_up(o_pairs + (size_t)g.n_pair * 8, 256);
+  const size_t total = align_up(o_active + (size_t)g.n_brow, 256) + 256;
   if (hipMalloc(&own->meta, total) != hipSuccess) {
     (void)hipGetLastError();
     own->meta = nullptr;
@@ -196,6 +217,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
   out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
   own->pairs = reinterpret_cast<int32_t*>(base + o_pairs);
+  own->active = g.ranged ? reinterpret_cast<uint8_t*>(base + o_active) : nullptr;
+  out->n_order = g.n_order;
   hipError_t e = hipSuccess;
   if (g.n_brow > 0) {
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
@@ -205,6 +228,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
       e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess && g.n_pair > 0)
       e = hipMemcpy(own->pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess && own->active)
+      e = hipMemcpy(own->active, g.active.data(), (size_t)g.n_brow, hipMemcpyHostToDevice);
   }
   if (e == hipSuccess) e = hipMemset(out->block_ptr, 0, (size_t)(g.n_brow + 1) * 4);
   if (e == hipSuccess) e = hipMemset(out->counters, 0, 256);
@@ -283,6 +308,8 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.coff = bsr->brow_coff;
   a.pairs = static_cast<const BsrOwner*>(bsr->_owner)->pairs;
   a.n_pair = static_cast<const BsrOwner*>(bsr->_owner)->geom.n_pair;
+  a.active = static_cast<const BsrOwner*>(bsr->_owner)->active;
+  a.n_order = bsr->n_order;
   a.n_causal = bsr->n_causal;
   a.tau = (double)tau;
   a.scale2 = (float)(1.4426950408889634 / std::sqrt((double)d));
@@ -496,12 +523,12 @@ MF_EXPORT mf_status mf_check_layer_map(const int32_t* pi, int32_t n_recv, int32_
   return MF_OK;
 }
 
-MF_EXPORT mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu,
-                                  int32_t n_seq, int64_t capacity, mf_bsr* out) {
+static mf_status bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu, int32_t n_seq,
+                            const int32_t* row_begin, int64_t capacity, mf_bsr* out) {
   if (!out) return fail(MF_ERR_INVALID, "out is NULL");
   if (H_s < 1 || H_s > 64) return fail(MF_ERR_INVALID, "H_s must be in [1, 64] (got %d)", H_s);
   Geometry g;
-  mf_status st = build_geometry(cu, n_seq, B, g);
+  mf_status st = build_geometry(cu, n_seq, B, g, row_begin);
   if (st != MF_OK) return st;
   if ((st = set_device(ctx)) != MF_OK) return st;
   BsrOwner* own = new (std::nothrow) BsrOwner();
@@ -514,7 +541,11 @@ MF_EXPORT mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int
   b.nb_max = g.nb_max;
   b.T = g.T;
   b.n_causal = g.n_causal;
-  if (capacity < 0) capacity = g.n_causal;
+  if (capacity < 0) {                  // every causal block of the rows that are compressed
+    capacity = 0;
+    for (int r = 0; r < g.n_brow; ++r)
+      if (g.active[r]) capacity += g.info[4 * r + 3] + 1;
+  }
   if ((st = alloc_bsr_meta(g, H_s, &b, own)) != MF_OK) {
     delete own;
     return st;
@@ -530,9 +561,22 @@ MF_EXPORT mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu,
+                                  int32_t n_seq, int64_t capacity, mf_bsr* out) {
+  return bsr_create(ctx, H_s, B, cu, n_seq, nullptr, capacity, out);
+}
+
+MF_EXPORT mf_status mf_bsr_create_range(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu,
+                                        int32_t n_seq, const int32_t* row_begin, int64_t capacity,
+                                        mf_bsr* out) {
+  if (!row_begin) return fail(MF_ERR_INVALID, "row_begin_host is NULL");
+  return bsr_create(ctx, H_s, B, cu, n_seq, row_begin, capacity, out);
+}
+
 MF_EXPORT mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr) {
   if (!bsr) return MF_OK;
   BsrOwner* own = static_cast<BsrOwner*>(bsr->_owner);
+  if (own && own->cache_owned) return fail(MF_ERR_INVALID, "this store belongs to a prefix cache");
   if (own) {
     if (ctx) (void)hipSetDevice(ctx->device);
     if (own->meta) (void)hipFree(own->meta);
@@ -634,7 +678,7 @@ MF_EXPORT mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, 
   mf_status st = validate_compress(Q, K, dtype, d, tau, bsr);
   if (st != MF_OK) return st;
   if ((st = set_device(ctx)) != MF_OK) return st;
-  if (bsr->n_brow == 0) return MF_OK;
+  if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
   mf::CompressArgs a;
   if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -650,7 +694,7 @@ MF_EXPORT mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const v
   if (st != MF_OK) return st;
   if (!V || !O) return fail(MF_ERR_INVALID, "V or O is NULL");
   if ((st = set_device(ctx)) != MF_OK) return st;
-  if (bsr->n_brow == 0) return MF_OK;
+  if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
   hipStream_t s = static_cast<hipStream_t>(stream);
   const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
   st = vfrag_prepare(ctx, bo->geom.cu.data(), bsr->n_seq, bsr->B, V, dtype, bsr->H_s, d, nullptr, 0, 0,
@@ -824,7 +868,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   }
   mf_status st = set_device(ctx);
   if (st != MF_OK) return st;
-  if (bsr->n_brow == 0) return MF_OK;
+  if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
   a.probs = bsr->probs;
   a.block_ptr = bsr->block_ptr;
   a.block_idx = bsr->block_idx;
@@ -832,6 +876,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   a.order = bsr->brow_order;
   a.capacity = bsr->capacity;
   a.n_brow = bsr->n_brow;
+  a.n_order = bsr->n_order;
   a.H_s = bsr->H_s;
   a.B = bsr->B;
   a.d = vf[0]->d;
@@ -955,6 +1000,227 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
   a.hm = hm;
   a.O = O;
   MF_HIP(mf::dense_attention(a, s), "dense attention launch");
+  return MF_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Prefix-hash cache of compressed block rows.
+// ------------------------------------------------------------------------------------------
+
+namespace {
+
+// FNV-1a, 64-bit (offset basis 0xcbf29ce484222325, prime 0x100000001b3), over little-endian bytes.
+uint64_t fnv1a64(uint64_t h, const void* data, size_t n) {
+  const unsigned char* p = static_cast<const unsigned char*>(data);
+  for (size_t i = 0; i < n; ++i) {
+    h ^= p[i];
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+
+void prefix_hashes(const int32_t* tokens, int64_t n_rows, int32_t B, uint64_t* out) {
+  uint64_t h = fnv1a64(0xcbf29ce484222325ull, &B, 4);
+  for (int64_t r = 0; r < n_rows; ++r) {
+    h = fnv1a64(0xcbf29ce484222325ull, &h, 8);
+    h = fnv1a64(h, tokens + r * B, (size_t)B * 4);
+    out[r] = h;
+  }
+}
+
+struct CacheKey {
+  int32_t layer, rows;
+  uint64_t hash;
+  bool operator==(const CacheKey& o) const { return layer == o.layer && rows == o.rows && hash == o.hash; }
+};
+struct CacheKeyHash {
+  size_t operator()(const CacheKey& k) const {
+    return (size_t)(k.hash ^ ((uint64_t)(uint32_t)k.layer << 32) ^ (uint64_t)(uint32_t)k.rows * 0x9e3779b97f4a7c15ull);
+  }
+};
+
+struct CacheEntry {
+  mf_bsr bsr{};                   // single sequence of rows * B tokens, every row compressed
+  std::vector<int32_t> tokens;    // the prefix, to confirm a hash match
+  size_t bytes = 0;
+  uint64_t last_use = 0;
+};
+
+}  // namespace
+
+struct mf_cache {
+  mf_ctx* ctx = nullptr;
+  int64_t budget = 0, used = 0;
+  uint64_t clock = 0;
+  std::unordered_map<CacheKey, std::unique_ptr<CacheEntry>, CacheKeyHash> map;
+};
+
+namespace {
+
+void cache_drop(mf_cache* c, std::unordered_map<CacheKey, std::unique_ptr<CacheEntry>, CacheKeyHash>::iterator it) {
+  CacheEntry* e = it->second.get();
+  BsrOwner* own = static_cast<BsrOwner*>(e->bsr._owner);
+  if (own) {
+    own->cache_owned = false;
+    mf_bsr_free(c->ctx, &e->bsr);
+  }
+  c->used -= (int64_t)e->bytes;
+  c->map.erase(it);
+}
+
+}  // namespace
+
+MF_EXPORT mf_status mf_prefix_hashes(const int32_t* tokens, int64_t n_tokens, int32_t B, uint64_t* out) {
+  if (n_tokens < 0) return fail(MF_ERR_INVALID, "n_tokens must be >= 0");
+  if (B < 1) return fail(MF_ERR_INVALID, "B must be >= 1");
+  if (n_tokens / B > 0 && (!tokens || !out)) return fail(MF_ERR_INVALID, "tokens or hashes_out is NULL");
+  prefix_hashes(tokens, n_tokens / B, B, out);
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_cache_create(mf_ctx* ctx, int64_t budget_bytes, mf_cache** out) {
+  if (!ctx) return fail(MF_ERR_INVALID, "context is NULL");
+  if (!out) return fail(MF_ERR_INVALID, "out is NULL");
+  if (budget_bytes <= 0) return fail(MF_ERR_INVALID, "budget_bytes must be > 0");
+  mf_cache* c = new (std::nothrow) mf_cache();
+  if (!c) return fail(MF_ERR_OOM, "host allocation failed");
+  c->ctx = ctx;
+  c->budget = budget_bytes;
+  *out = c;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_cache_destroy(mf_cache* cache) {
+  if (!cache) return MF_OK;
+  if (cache->ctx) (void)hipSetDevice(cache->ctx->device);
+  (void)hipDeviceSynchronize();
+  while (!cache->map.empty()) cache_drop(cache, cache->map.begin());
+  delete cache;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_cache_info(const mf_cache* cache, int64_t* entries, int64_t* used_bytes) {
+  if (!cache) return fail(MF_ERR_INVALID, "cache is NULL");
+  if (entries) *entries = (int64_t)cache->map.size();
+  if (used_bytes) *used_bytes = cache->used;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_cache_insert(mf_cache* cache, int32_t layer, const int32_t* tokens, int64_t n_tokens,
+                                    int32_t n_parts, const mf_bsr* parts, int32_t rows, void* stream) {
+  if (!cache) return fail(MF_ERR_INVALID, "cache is NULL");
+  if (n_parts < 1 || !parts) return fail(MF_ERR_INVALID, "need at least one part store");
+  const int B = parts[0].B, H_s = parts[0].H_s;
+  if (rows < 1 || (int64_t)rows * B > n_tokens)
+    return fail(MF_ERR_INVALID, "rows = %d must be in [1, n_tokens / B = %lld]", rows, (long long)(n_tokens / B));
+  if (!tokens) return fail(MF_ERR_INVALID, "tokens is NULL");
+  // every row 0..rows-1 comes from the first part that compresses it
+  std::vector<int> src(rows, -1);
+  for (int k = 0; k < n_parts; ++k) {
+    const mf_bsr& p = parts[k];
+    const BsrOwner* po = static_cast<const BsrOwner*>(p._owner);
+    if (!po) return fail(MF_ERR_INVALID, "part %d is not a store", k);
+    if (p.n_seq != 1) return fail(MF_ERR_INVALID, "part %d holds %d sequences; parts are single sequences", k, p.n_seq);
+    if (p.B != B || p.H_s != H_s) return fail(MF_ERR_INVALID, "part %d has B = %d, H_s = %d; part 0 has %d, %d", k, p.B, p.H_s, B, H_s);
+    for (int r = 0; r < rows && r < p.n_brow; ++r) {
+      // a row's content depends on its full block of queries: only rows complete in the part count
+      if (src[r] < 0 && po->geom.active[r] && (int64_t)(r + 1) * B <= p.T) src[r] = k;
+    }
+  }
+  for (int r = 0; r < rows; ++r)
+    if (src[r] < 0) return fail(MF_ERR_INVALID, "block row %d is compressed (complete) in none of the parts", r);
+  mf_status st = set_device(cache->ctx);
+  if (st != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // block counts per row from the parts' block_ptr
+  std::vector<std::vector<int32_t>> ptrs(n_parts);
+  for (int k = 0; k < n_parts; ++k) {
+    ptrs[k].resize((size_t)parts[k].n_brow + 1);
+    MF_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");
+    MF_HIP(hipMemcpy(ptrs[k].data(), parts[k].block_ptr, ptrs[k].size() * 4, hipMemcpyDeviceToHost), "reading block_ptr");
+  }
+  std::vector<int32_t> new_ptr(rows + 1, 0);
+  for (int r = 0; r < rows; ++r) new_ptr[r + 1] = new_ptr[r] + ptrs[src[r]][r + 1] - ptrs[src[r]][r];
+  const int64_t nnzb = new_ptr[rows];
+  const size_t bytes = (size_t)nnzb * (8 + probs_block_bytes(H_s, B)) + (size_t)H_s * rows * B * 4 + (size_t)rows * 64;
+  if ((int64_t)bytes > cache->budget)
+    return fail(MF_ERR_CAPACITY, "entry of %zu bytes exceeds the cache budget %lld", bytes, (long long)cache->budget);
+  uint64_t h_last = 0;
+  {
+    std::vector<uint64_t> hs(rows);
+    prefix_hashes(tokens, rows, B, hs.data());
+    h_last = hs[rows - 1];
+  }
+  const CacheKey key{layer, rows, h_last};
+  auto found = cache->map.find(key);
+  if (found != cache->map.end() && std::equal(found->second->tokens.begin(), found->second->tokens.end(), tokens)) {
+    found->second->last_use = ++cache->clock;       // already cached
+    return MF_OK;
+  }
+  if (found != cache->map.end()) cache_drop(cache, found);   // a colliding prefix: replace it
+  while (cache->used + (int64_t)bytes > cache->budget && !cache->map.empty()) {
+    auto lru = cache->map.begin();
+    for (auto it = cache->map.begin(); it != cache->map.end(); ++it)
+      if (it->second->last_use < lru->second->last_use) lru = it;
+    cache_drop(cache, lru);
+  }
+  auto e = std::make_unique<CacheEntry>();
+  const int32_t cu[2] = {0, rows * B};
+  if ((st = bsr_create(cache->ctx, H_s, B, cu, 1, nullptr, nnzb, &e->bsr)) != MF_OK) return st;
+  mf_bsr& d = e->bsr;
+  MF_HIP(hipMemcpyAsync(d.block_ptr, new_ptr.data(), (size_t)(rows + 1) * 4, hipMemcpyHostToDevice, s), "copy block_ptr");
+  const size_t pb = probs_block_bytes(H_s, B);
+  for (int r = 0; r < rows;) {
+    // one copy per run of rows from the same part
+    int r1 = r + 1;
+    while (r1 < rows && src[r1] == src[r]) ++r1;
+    const mf_bsr& p = parts[src[r]];
+    const int64_t a0 = ptrs[src[r]][r], a1 = ptrs[src[r]][r1], n = a1 - a0;
+    if (n > 0) {
+      MF_HIP(hipMemcpyAsync(d.block_idx + new_ptr[r], p.block_idx + a0, (size_t)n * 4, hipMemcpyDeviceToDevice, s), "copy block_idx");
+      MF_HIP(hipMemcpyAsync(d.block_row + new_ptr[r], p.block_row + a0, (size_t)n * 4, hipMemcpyDeviceToDevice, s), "copy block_row");
+      MF_HIP(hipMemcpyAsync(reinterpret_cast<char*>(d.probs) + (size_t)new_ptr[r] * pb,
+                            reinterpret_cast<const char*>(p.probs) + (size_t)a0 * pb, (size_t)n * pb,
+                            hipMemcpyDeviceToDevice, s), "copy probs");
+    }
+    MF_HIP(hipMemcpy2DAsync(d.row_kept_mass + (size_t)r * B, (size_t)rows * B * 4, p.row_kept_mass + (size_t)r * B,
+                            (size_t)p.T * 4, (size_t)(r1 - r) * B * 4, H_s, hipMemcpyDeviceToDevice, s), "copy kept mass");
+    r = r1;
+  }
+  const int32_t cnt[2] = {(int32_t)nnzb, 0};
+  MF_HIP(hipMemcpyAsync(d.counters, cnt, sizeof(cnt), hipMemcpyHostToDevice, s), "copy counters");
+  MF_HIP(hipStreamSynchronize(s), "hipStreamSynchronize");   // host sources above are stack / vector memory
+  d.nnzb = nnzb;
+  static_cast<BsrOwner*>(d._owner)->cache_owned = true;
+  e->tokens.assign(tokens, tokens + (size_t)rows * B);
+  e->bytes = bytes;
+  e->last_use = ++cache->clock;
+  cache->used += (int64_t)bytes;
+  cache->map.emplace(key, std::move(e));
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_cache_lookup(mf_cache* cache, int32_t layer, const int32_t* tokens, int64_t n_tokens,
+                                    int32_t B, int32_t* rows_out, mf_bsr* view_out) {
+  if (!cache) return fail(MF_ERR_INVALID, "cache is NULL");
+  if (!rows_out || !view_out) return fail(MF_ERR_INVALID, "rows_out or view_out is NULL");
+  if (B < 1 || n_tokens < 0) return fail(MF_ERR_INVALID, "bad B or n_tokens");
+  *rows_out = 0;
+  std::memset(view_out, 0, sizeof(*view_out));
+  const int64_t full = n_tokens / B;
+  if (full == 0 || cache->map.empty()) return MF_OK;
+  if (!tokens) return fail(MF_ERR_INVALID, "tokens is NULL");
+  std::vector<uint64_t> hs((size_t)full);
+  prefix_hashes(tokens, full, B, hs.data());
+  for (int64_t r = full; r >= 1; --r) {
+    auto it = cache->map.find(CacheKey{layer, (int32_t)r, hs[(size_t)r - 1]});
+    if (it == cache->map.end() || it->second->bsr.B != B) continue;
+    if (!std::equal(it->second->tokens.begin(), it->second->tokens.end(), tokens)) continue;
+    it->second->last_use = ++cache->clock;
+    *rows_out = (int32_t)r;
+    *view_out = it->second->bsr;
+    return MF_OK;
+  }
   return MF_OK;
 }
 

@@ -92,10 +92,15 @@ __device__ __forceinline__ bool sel_before(double ka, int ia, double kb, int ib)
 __global__ __launch_bounds__(256) void k_select(const double* __restrict__ M,
                                                 const int32_t* __restrict__ info, int nb_max,
                                                 int H_s, int B, double tau,
+                                                const uint8_t* __restrict__ active,
                                                 uint8_t* __restrict__ flags,
                                                 int32_t* __restrict__ counts) {
   extern __shared__ unsigned char sm_raw[];
   const int brow = blockIdx.x;
+  if (active != nullptr && !active[brow]) {        // a row outside the compressed range keeps nothing
+    if (threadIdx.x == 0) counts[brow] = 0;
+    return;
+  }
   const BrowInfo bi = load_info(info, brow);
   const int I = bi.I, n = I + 1;
   const int rows = min(B, bi.n - I * B);
@@ -194,10 +199,12 @@ __global__ __launch_bounds__(1024) void k_scan(const int32_t* __restrict__ count
 __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
                                               const int32_t* __restrict__ block_ptr,
                                               const int32_t* __restrict__ info, int nb_max,
-                                              int64_t capacity, int32_t* __restrict__ block_idx,
+                                              int64_t capacity, const uint8_t* __restrict__ active,
+                                              int32_t* __restrict__ block_idx,
                                               int32_t* __restrict__ block_row) {
   __shared__ int wtot[4];
   const int brow = blockIdx.x;
+  if (active != nullptr && !active[brow]) return;   // its flags are stale scratch
   const int I = info[4 * brow + 3];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint8_t* frow = flags + (size_t)brow * nb_max;
@@ -384,7 +391,7 @@ template <typename T, int B, int D>
 __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
                                                 int H_s, int64_t T_tot,
                                                 const int32_t* __restrict__ info,
-                                                const int32_t* __restrict__ order, int n_brow,
+                                                const int32_t* __restrict__ order, int n_brow, int n_order,
                                                 const int32_t* __restrict__ block_ptr,
                                                 const int32_t* __restrict__ block_idx,
                                                 const int32_t* __restrict__ counters,
@@ -409,15 +416,15 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
   int p, hg, chunk;
   if ((8 % HG) == 0) {
     const int xcd = blockIdx.x & 7, q = blockIdx.x >> 3;
-    const int nparts = 8 / HG, rp = (n_brow + nparts - 1) / nparts;
+    const int nparts = 8 / HG, rp = (n_order + nparts - 1) / nparts;
     hg = xcd % HG;
     chunk = q / rp;
     p = (q % rp) * nparts + xcd / HG;
-    if (p >= n_brow) return;
+    if (p >= n_order) return;
   } else {
-    p = blockIdx.x % n_brow;
-    hg = (blockIdx.x / n_brow) % HG;
-    chunk = blockIdx.x / (n_brow * HG);
+    p = blockIdx.x % n_order;
+    hg = (blockIdx.x / n_order) % HG;
+    chunk = blockIdx.x / (n_order * HG);
   }
   const int brow = order[p];
   const BrowInfo bi = load_info(info, brow);
@@ -544,10 +551,10 @@ static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
   if (a.capacity == 0) return hipSuccess;
   const unsigned chunks = (unsigned)((a.nb_max + kGatherChunk - 1) / kGatherChunk);
   // grid: with the XCD mapping, 8 XCDs x ceil(n_brow / (8 / HG)) block rows x chunks
-  const unsigned items = (8 % HG) == 0 ? 8u * (unsigned)((a.n_brow + 8 / HG - 1) / (8 / HG)) * chunks
-                                       : (unsigned)a.n_brow * HG * chunks;
+  const unsigned items = (8 % HG) == 0 ? 8u * (unsigned)((a.n_order + 8 / HG - 1) / (8 / HG)) * chunks
+                                       : (unsigned)a.n_order * HG * chunks;
   hipLaunchKernelGGL((k_gather<T, B, D>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
-                     (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.block_ptr, a.block_idx,
+                     (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.n_order, a.block_ptr, a.block_idx,
                      a.counters, a.capacity, a.lse2, a.scale2, (const unsigned char*)a.ktile, a.probs,
                      a.part);
   return hipGetLastError();
@@ -592,7 +599,7 @@ hipError_t compress_plan(const CompressArgs& a, hipStream_t s) {
   while (N < a.nb_max) N <<= 1;
   const size_t lds = (size_t)N * (sizeof(double) + sizeof(int));
   hipLaunchKernelGGL(k_select, dim3(a.n_brow), dim3(256), lds, s, a.M, a.info, a.nb_max, a.H_s,
-                     a.B, a.tau, a.flags, a.counts);
+                     a.B, a.tau, a.active, a.flags, a.counts);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, a.counts, a.n_brow, a.capacity,
                      a.block_ptr, a.counters);
@@ -601,7 +608,7 @@ hipError_t compress_plan(const CompressArgs& a, hipStream_t s) {
 
 hipError_t compress_fill(const CompressArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_emit, dim3(a.n_brow), dim3(256), 0, s, a.flags, a.block_ptr, a.info,
-                     a.nb_max, a.capacity, a.block_idx, a.block_row);
+                     a.nb_max, a.capacity, a.active, a.block_idx, a.block_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = gather_dispatch(a, s)) != hipSuccess) return e;

@@ -19,6 +19,8 @@ struct CompressArgs {
   const int32_t* coff;   // [n_brow] causal block offset of each block row
   const int32_t* pairs;  // [n_pair][2] block rows (I, I+1) of one sequence, second may be -1
   int n_pair;
+  const uint8_t* active; // [n_brow] rows to compress (NULL: all); order[] lists exactly these
+  int n_order;           // entries of order[]
   int64_t n_causal;
   double tau;
   float scale2;          // log2(e) / sqrt(d)
@@ -93,6 +95,7 @@ struct RetrieveArgs {
   const int32_t* order;
   int64_t capacity;      // blocks allocated in the store (clamps block_ptr after an overflow)
   int n_brow, H_s, B, d;
+  int n_order;           // block rows to retrieve: the first n_order entries of order[]
   int64_t T;
   const float* rkm;
   int n_recv, n_split;

@@ -247,7 +247,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   const int n_split = args.n_split;
   const int split = (q / NRT) % n_split;
   const int gidx = (q / (NRT * n_split)) * 8 + xcd;
-  if (gidx >= n_brow) return;
+  if (gidx >= args.n_order) return;
   const int brow = order[gidx];
   const BrowInfo bi = load_info(info, brow);
   const int rows_blk = min(B, bi.n - bi.I * B);
@@ -505,7 +505,7 @@ bool retrieve_supported(int B, int d, int H_r, int H_s) {
 template <int B, int D, int HP, int KC>
 static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
   constexpr int NRT = B / RT_ROWS;
-  const unsigned groups = (unsigned)((a.n_brow + 7) / 8);
+  const unsigned groups = (unsigned)((a.n_order + 7) / 8);
   hipLaunchKernelGGL((k_retrieve<B, D, HP, KC>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }

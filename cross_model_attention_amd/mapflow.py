@@ -114,11 +114,19 @@ class BlockStore:
         self.cu_seqlens = cu
 
     @classmethod
-    def create(cls, H_s: int, B: int, cu_seqlens, capacity: int = -1, ctx=None) -> "BlockStore":
+    def create(cls, H_s: int, B: int, cu_seqlens, capacity: int = -1, ctx=None, row_begin=None) -> "BlockStore":
+        """mf_bsr_create, or mf_bsr_create_range when ``row_begin`` (first block row per sequence)
+        is given."""
         ctx = _ctx(ctx)
         cu_arr, n_seq, cu = _cu(cu_seqlens, 0)
         raw = MfBsr()
-        check(_L.mf_bsr_create(ctx.handle, int(H_s), int(B), cu_arr, n_seq, int(capacity), ctypes.byref(raw)))
+        if row_begin is None:
+            check(_L.mf_bsr_create(ctx.handle, int(H_s), int(B), cu_arr, n_seq, int(capacity), ctypes.byref(raw)))
+        else:
+            if len(row_begin) != n_seq:
+                raise ValueError("row_begin needs one entry per sequence")
+            check(_L.mf_bsr_create_range(ctx.handle, int(H_s), int(B), cu_arr, n_seq, i32_array(row_begin),
+                                         int(capacity), ctypes.byref(raw)))
         return cls(ctx, raw, cu)
 
     def __getattr__(self, name):
@@ -190,12 +198,73 @@ class BlockStore:
                                rkm.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
 
     def free(self):
+        if self.__dict__.get("borrowed_from") is not None:
+            return                                   # a prefix-cache entry: the cache owns it
         if self.__dict__.get("raw") is not None and self.raw._owner:
             _L.mf_bsr_free(self.ctx.handle, ctypes.byref(self.raw))
 
     def __del__(self):
         try:
             self.free()
+        except Exception:
+            pass
+
+
+def _tokens(tokens):
+    t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+    return t, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def prefix_hashes(tokens, B: int) -> np.ndarray:
+    """mf_prefix_hashes: chained hash of every full B-token block of ``tokens`` (host only)."""
+    t, tp = _tokens(tokens)
+    out = np.zeros(len(t) // int(B), dtype=np.uint64)
+    check(_L.mf_prefix_hashes(tp, len(t), int(B), out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64))))
+    return out
+
+
+class PrefixCache:
+    """mf_cache: compressed block rows of token prefixes, per layer, found by prefix hash."""
+
+    def __init__(self, budget_bytes: int, ctx=None):
+        self.ctx = _ctx(ctx)
+        h = ctypes.c_void_p()
+        check(_L.mf_cache_create(self.ctx.handle, int(budget_bytes), ctypes.byref(h)))
+        self.handle = h
+
+    def insert(self, layer: int, tokens, parts, rows: int, stream=None) -> None:
+        """Cache block rows 0..rows-1 of ``tokens``, taking each row from the first of ``parts``
+        (single-sequence stores, e.g. a looked-up prefix and a row-range store) that compressed it."""
+        t, tp = _tokens(tokens)
+        arr = (MfBsr * len(parts))(*[p.raw for p in parts])
+        check(_L.mf_cache_insert(self.handle, int(layer), tp, len(t), len(parts), arr, int(rows), _stream(stream)))
+
+    def lookup(self, layer: int, tokens, B: int):
+        """Longest cached prefix: (rows, store view of rows 0..rows-1) or (0, None).  The view
+        stays valid until an insert evicts it or the cache is closed."""
+        t, tp = _tokens(tokens)
+        rows = ctypes.c_int32(0)
+        raw = MfBsr()
+        check(_L.mf_cache_lookup(self.handle, int(layer), tp, len(t), int(B), ctypes.byref(rows), ctypes.byref(raw)))
+        if rows.value == 0:
+            return 0, None
+        view = BlockStore(self.ctx, raw, [0, rows.value * int(B)])
+        view.borrowed_from = self
+        return rows.value, view
+
+    def info(self):
+        n, used = ctypes.c_int64(0), ctypes.c_int64(0)
+        check(_L.mf_cache_info(self.handle, ctypes.byref(n), ctypes.byref(used)))
+        return n.value, used.value
+
+    def close(self):
+        if self.__dict__.get("handle"):
+            _L.mf_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
         except Exception:
             pass
 

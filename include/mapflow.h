@@ -43,6 +43,7 @@ typedef enum mf_status {
 typedef enum mf_dtype { MF_F32 = 0, MF_BF16 = 1 } mf_dtype;
 
 typedef struct mf_ctx mf_ctx;
+typedef struct mf_cache mf_cache;
 
 /*
  * Block-sparse (BSR) store of one sender layer's compressed attention map.
@@ -75,7 +76,8 @@ typedef struct mf_bsr {
   int32_t n_seq;      /* sequences in the packed batch                        */
   int32_t n_brow;     /* block rows over all sequences                        */
   int32_t nb_max;     /* largest per-sequence block count                     */
-  int32_t _pad;
+  int32_t n_order;    /* block rows compressed and retrieved (n_brow unless the store was
+                         created with a row range by mf_bsr_create_range)              */
   int64_t T;          /* tokens in the packed batch                           */
   int64_t n_causal;   /* causal (lower-triangular) blocks over all sequences  */
   int64_t capacity;   /* blocks allocated in block_idx / block_row / probs    */
@@ -141,6 +143,22 @@ mf_status mf_check_layer_map(const int32_t* pi_host, int32_t n_recv, int32_t n_s
  */
 mf_status mf_bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu_seqlens_host,
                         int32_t n_seq, int64_t capacity_blocks, mf_bsr* out);
+
+/*
+ * A block store for chunked prefill: like mf_bsr_create, but only block rows I >= row_begin[s]
+ * of each sequence s are compressed and retrieved (row_begin_host: int32 [n_seq], each in
+ * [0, ceil(n_s / B)]).  [MapFlow开源, section 算得省的:融合内核执行] names chunked prefill among
+ * the serving features the retrieval works with; rows of an earlier chunk come from another
+ * store, for example a cached prefix (mf_cache_lookup).  Every row still exists as a key block
+ * row, so Q and K (and V for the retrieve) are passed for the whole sequence as usual; row
+ * selection, probabilities and kept mass of a compressed row are exactly those of the same row
+ * in an mf_bsr_create store.  Rows outside the range keep no blocks, their kept mass is 0, and
+ * mf_retrieve* / mf_compress_prefill_into leave their output rows untouched.
+ * capacity_blocks < 0 allocates every causal block of the compressed rows.
+ */
+mf_status mf_bsr_create_range(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu_seqlens_host,
+                              int32_t n_seq, const int32_t* row_begin_host, int64_t capacity_blocks,
+                              mf_bsr* out);
 
 /*
  * Copy a store to host memory (synchronous; waits for the device).  Any destination may be NULL
@@ -300,6 +318,55 @@ mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K, const vo
                              mf_dtype dtype, int32_t H_q, int32_t H_kv, int32_t d,
                              const int32_t* cu_seqlens_host, int32_t n_seq,
                              const int32_t* kv_head_map_host, float* O, void* stream);
+
+/*
+ * Prefix-hash cache of compressed sender state.  [MapFlow开源, section 找得快的:基于前缀哈希的缓存管理]
+ * and [Reuses Attention, second component]: the sparse blocks kept per layer and position vary in
+ * number; they are indexed by a hash that carries the preceding context, so a receiver reusing
+ * the state finds its blocks through that index.
+ *
+ * mf_prefix_hashes (host only): for each full block r of B tokens (r < n_tokens / B),
+ *     h_{-1} = FNV1a64(4 little-endian bytes of B),
+ *     h_r    = FNV1a64(8 little-endian bytes of h_{r-1} || 4 little-endian bytes of each token of
+ *              block r),
+ * FNV-1a 64-bit with offset basis 0xcbf29ce484222325 and prime 0x100000001b3, restarted from the
+ * offset basis for every h_r.  h_r depends on every token up to the end of block r and on B, so it
+ * names a block row's compressed content, which depends on exactly those tokens.
+ */
+mf_status mf_prefix_hashes(const int32_t* tokens_host, int64_t n_tokens, int32_t B, uint64_t* hashes_out);
+
+/*
+ * A cache of compressed token prefixes in device memory, at most budget_bytes (entries are
+ * evicted least recently used first).  Not thread-safe: one thread uses a cache at a time.
+ */
+mf_status mf_cache_create(mf_ctx* ctx, int64_t budget_bytes, mf_cache** out);
+/* Synchronises the device, frees every entry (views from mf_cache_lookup become invalid). */
+mf_status mf_cache_destroy(mf_cache* cache);
+/* Number of entries and bytes held. */
+mf_status mf_cache_info(const mf_cache* cache, int64_t* entries, int64_t* used_bytes);
+
+/*
+ * Cache block rows 0..rows-1 of one sequence for `layer`, keyed by (layer, rows, h_{rows-1}) of
+ * tokens_host[0 .. n_tokens) and confirmed by the tokens themselves on lookup.  Each row is copied
+ * (device to device, on `stream`, which is synchronised) from the first of parts[0 .. n_parts)
+ * that compressed it completely: parts are single-sequence stores of the same B and H_s whose
+ * token 0 is token 0 of tokens_host (a store of the whole sequence, or a looked-up prefix and a
+ * mf_bsr_create_range store of the rows after it).  MF_ERR_INVALID when a row is in no part;
+ * MF_ERR_CAPACITY when the entry alone exceeds the budget.  Inserting an existing prefix only
+ * refreshes it.  May evict other entries, invalidating their views.
+ */
+mf_status mf_cache_insert(mf_cache* cache, int32_t layer, const int32_t* tokens_host, int64_t n_tokens,
+                          int32_t n_parts, const mf_bsr* parts, int32_t rows, void* stream);
+
+/*
+ * Longest cached prefix of tokens_host for `layer` with block size B: *rows_out = its block rows
+ * (0 when nothing matches) and *view_out = a store of exactly those rows (one sequence of
+ * rows * B tokens), owned by the cache: read it (mf_retrieve*, mf_bsr_download, as a part of
+ * mf_cache_insert), never free it (mf_bsr_free refuses); valid until evicted or the cache is
+ * destroyed.  The rows after it are compressed with an mf_bsr_create_range store.
+ */
+mf_status mf_cache_lookup(mf_cache* cache, int32_t layer, const int32_t* tokens_host, int64_t n_tokens,
+                          int32_t B, int32_t* rows_out, mf_bsr* view_out);
 
 /*
  * HBM probe: copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from src to dst with

@@ -2,6 +2,8 @@
 seeded inputs small enough for the oracle to finish in seconds but spanning several tiles and a
 ragged tail.  Edge cases: single partial block, one-token sequences, tau = 1, forced-only
 selection, varlen with an empty sequence, paged V."""
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -302,3 +304,127 @@ def test_copy_probe(mf):
     mf.copy_probe(dst, src)
     torch.cuda.synchronize()
     assert torch.equal(src, dst)
+
+
+def _rows_of(host, r):
+    a, b = int(host["block_ptr"][r]), int(host["block_ptr"][r + 1])
+    return host["block_idx"][a:b], host["probs_bits"][a:b]
+
+
+def test_chunked_prefill_rows_equal_the_full_store(mf):
+    """A row-range store compresses exactly the rows of the full store it covers (bit for bit),
+    keeps nothing elsewhere, and its retrieve and fused prefill touch only its rows."""
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    lengths = [300, 129, 64]
+    x = synth.make_layer_inputs(wl, 11, lengths=lengths, H_s=8, H_r=12, H_kv=4, d=128)
+    v_s = synth.make_dense_inputs(wl, 11, layer=1, lengths=lengths, H_q=8, H_kv=8, d=128)["v"]
+    tau = _f32(wl.tau)
+    row_begin = [2, 0, 1]                               # block rows: 5, 3, 1 (the last sequence: none)
+    say(f"case: chunked prefill lengths={lengths} row_begin={row_begin}")
+    Q, K = to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16")
+    full = mf.BlockStore.create(8, wl.B, x["cu_seqlens"])
+    part = mf.BlockStore.create(8, wl.B, x["cu_seqlens"], row_begin=row_begin)
+    assert part.raw.n_order == 3 + 3 + 0 and full.raw.n_order == full.raw.n_brow == 9
+    mf.compress_into(full, Q, K, tau)
+    mf.compress_into(part, Q, K, tau)
+    full.sync()
+    part.sync()
+    hf, hp = full.to_host(), part.to_host()
+    cu = x["cu_seqlens"]
+    active_tok = np.zeros(int(cu[-1]), dtype=bool)
+    r = 0
+    for s, n in enumerate(lengths):
+        for I in range((n + wl.B - 1) // wl.B):
+            if I >= row_begin[s]:
+                for a_, b_ in zip(_rows_of(hf, r), _rows_of(hp, r)):
+                    assert np.array_equal(a_, b_), f"row {r}"
+                active_tok[int(cu[s]) + I * wl.B: int(cu[s]) + min(n, (I + 1) * wl.B)] = True
+            else:
+                assert len(_rows_of(hp, r)[0]) == 0, f"row {r} outside the range kept blocks"
+            r += 1
+    assert np.array_equal(hf["row_kept_mass"][:, active_tok], hp["row_kept_mass"][:, active_tok])
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
+    O_full = mf.retrieve(full, W, V, x["kv_head_map"])
+    O_part = torch.full_like(O_full, float("nan"))
+    mf.retrieve(part, W, V, x["kv_head_map"], out=O_part)
+    torch.cuda.synchronize()
+    act = torch.from_numpy(active_tok).cuda()
+    assert torch.equal(O_part[act], O_full[act])
+    assert torch.isnan(O_part[~act]).all()
+    # the fused prefill on the range store: same store, attention rows of the range only
+    pre = mf.BlockStore.create(8, wl.B, x["cu_seqlens"], row_begin=row_begin)
+    Vs = to_dev(v_s, "bf16")
+    O_pre = torch.full((int(cu[-1]), 8, 128), float("nan"), device="cuda")
+    mf.compress_prefill_into(pre, Q, K, Vs, tau, out=O_pre)
+    pre.sync()
+    O_pre_full = mf.compress_prefill_into(mf.BlockStore.create(8, wl.B, x["cu_seqlens"]), Q, K, Vs, tau)
+    torch.cuda.synchronize()
+    hq = pre.to_host()
+    for key in ["block_ptr", "block_idx", "probs_bits", "row_kept_mass"]:
+        assert np.array_equal(hq[key], hp[key]), key
+    assert torch.equal(O_pre[act], O_pre_full[act]) and torch.isnan(O_pre[~act]).all()
+
+
+def test_prefix_cache_reuses_a_previous_request(mf):
+    """Request 2 extends request 1: its cached prefix plus a row-range store of the new rows give
+    the same retrieve output as compressing request 2 whole; inserting the combined prefix gives
+    the rows of the whole compression, bit for bit."""
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    B = wl.B
+    n1, n2 = 5 * B + 10, 9 * B + 3
+    x = synth.make_layer_inputs(wl, 12, lengths=[n2], H_s=8, H_r=12, H_kv=4, d=128)
+    tokens = np.random.default_rng(12).integers(0, 50000, size=n2, dtype=np.int32)
+    tau = _f32(wl.tau)
+    say(f"case: prefix cache n1={n1} n2={n2}")
+    Q, K = to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16")
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
+    cache = mf.PrefixCache(1 << 30)
+    # request 1: compress it whole, cache its complete rows
+    s1 = mf.BlockStore.create(8, B, [0, n1])
+    mf.compress_into(s1, Q[:, :n1].contiguous(), K[:, :n1].contiguous(), tau)
+    s1.sync()
+    cache.insert(3, tokens[:n1], [s1], n1 // B)
+    assert cache.info()[0] == 1
+    assert cache.lookup(3, tokens[:n1], B)[0] == 5
+    assert cache.lookup(4, tokens[:n1], B)[0] == 0               # other layer
+    changed = tokens.copy()
+    changed[2 * B + 1] += 1
+    assert cache.lookup(3, changed, B)[0] == 0                   # the cached prefix no longer matches
+    # request 2: cached rows 0..4, new rows 5..9
+    rows, view = cache.lookup(3, tokens, B)
+    assert rows == 5 and view.raw.T == 5 * B
+    new = mf.BlockStore.create(8, B, [0, n2], row_begin=[rows])
+    mf.compress_into(new, Q, K, tau)
+    new.sync()
+    O = torch.empty((n2, 12, 128), device="cuda")
+    mf.retrieve(view, W, V[: rows * B].contiguous(), x["kv_head_map"], out=O[: rows * B])
+    mf.retrieve(new, W, V, x["kv_head_map"], out=O)
+    whole = mf.BlockStore.create(8, B, [0, n2])
+    mf.compress_into(whole, Q, K, tau)
+    whole.sync()
+    O_whole = mf.retrieve(whole, W, V, x["kv_head_map"])
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_whole)
+    # cache request 2's complete rows from the view and the new rows
+    cache.insert(3, tokens, [view, new], n2 // B)
+    rows2, view2 = cache.lookup(3, tokens, B)
+    assert rows2 == 9 and cache.info()[0] == 2
+    hv, hw = view2.to_host(), whole.to_host()
+    nb = int(hv["block_ptr"][rows2])
+    assert np.array_equal(hv["block_ptr"], hw["block_ptr"][: rows2 + 1])
+    assert np.array_equal(hv["block_idx"], hw["block_idx"][:nb])
+    assert np.array_equal(hv["probs_bits"], hw["probs_bits"][:nb])
+    assert np.array_equal(hv["row_kept_mass"], hw["row_kept_mass"][:, : rows2 * B])
+    # the oracle agrees with the cached rows
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    assert np.array_equal(hv["block_idx"], ref.block_idx[: len(hv["block_idx"])])
+    # a small budget evicts the least recently used entry
+    small = mf.PrefixCache(int(cache.info()[1] * 0.8))
+    small.insert(3, tokens[:n1], [s1], 5)
+    small.insert(3, tokens, [view, new], 9)
+    assert small.info()[0] == 1 and small.lookup(3, tokens[:n1], B)[0] == 0
+    # a view belongs to the cache: the library refuses to free it
+    from cross_model_attention_amd import _lib
+    assert _lib.load().mf_bsr_free(None, ctypes.byref(view2.raw)) == _lib.MF_ERR_INVALID
+    cache.close()
+    small.close()
