@@ -46,9 +46,10 @@ def parse():
     p.add_argument("--cpu-rows", type=int, default=16, help="block rows in the oracle sample")
     p.add_argument("--extras", action="store_true",
                    help="after the timed steps, also compare the fused sender prefill with the plain "
-                        "compress, and multi-receiver retrieves with separate ones (extra objects "
-                        "'prefill' and 'fanout'); off by default so that the kernel trace of a default "
-                        "run holds only the step's launches")
+                        "compress, a prefix-cache hit with a whole compression, and multi-receiver "
+                        "retrieves with separate ones (extra objects 'prefill', 'prefix_reuse' and "
+                        "'fanout'); off by default so that the kernel trace of a default run holds only "
+                        "the step's launches")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
                    help="size of the HBM copy probe run after the timed steps (0 = skip)")
     return p.parse_args()
@@ -206,6 +207,60 @@ def prefill(mf, torch, wl, args, send, store, tau, ctx, dev):
     log(f"prefill: compress {res['compress_ms']:.2f} ms, sender attention {res['sender_attention_ms']:.2f} ms, "
         f"fused {res['fused_prefill_ms']:.2f} ms")
     del Qt, Kt, V, O
+    return res
+
+
+def prefix_reuse(mf, torch, wl, args, send, recv, kv_map, tau, ctx, dev):
+    """A second request that extends a first one (3/4 of L, then L): compress + retrieve of the
+    whole second request against a prefix-cache hit for its first 3/4 plus a block-row range store
+    for the rest.  Inserting the first request's rows is timed apart."""
+    Q, K = send
+    W, V = recv
+    H_s, L, d = Q.shape
+    B = wl.B
+    n1 = (3 * L // 4) // B * B
+    tokens = np.random.default_rng(args.seed + 13).integers(0, 50000, size=L, dtype=np.int32)
+    cache = mf.PrefixCache(64 << 30, ctx=ctx)
+    first = mf.BlockStore.create(H_s, B, [0, n1], ctx=ctx)
+    mf.compress_into(first, Q[:, :n1].contiguous(), K[:, :n1].contiguous(), tau)
+    first.sync()
+    O = torch.empty((L, wl.H_r, d), dtype=torch.float32, device=dev)
+    whole = mf.BlockStore.create(H_s, B, [0, L], ctx=ctx)
+    new = mf.BlockStore.create(H_s, B, [0, L], ctx=ctx, row_begin=[n1 // B])
+    V1 = V[:n1].contiguous()
+    pv_all, pv_1 = mf.v_prepare(V, B, [0, L], ctx=ctx), mf.v_prepare(V1, B, [0, n1], ctx=ctx)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t0 = time.perf_counter()
+    cache.insert(0, tokens[:n1], [first], n1 // B)
+    insert_ms = (time.perf_counter() - t0) * 1e3
+
+    def full_path():
+        mf.compress_into(whole, Q, K, tau)
+        mf.retrieve_prepared(whole, W, pv_all, kv_map, out=O)
+
+    def cached_path():
+        rows, view = cache.lookup(0, tokens, B)
+        mf.compress_into(new, Q, K, tau)
+        mf.retrieve_prepared(view, W, pv_1, kv_map, out=O[: rows * B])
+        mf.retrieve_prepared(new, W, pv_all, kv_map, out=O)
+
+    res = {"prefix_tokens": n1, "tokens": L, "whole_ms": timed(full_path), "cached_ms": timed(cached_path),
+           "insert_ms": insert_ms}
+    res["saving"] = 1.0 - res["cached_ms"] / res["whole_ms"]
+    log(f"prefix reuse: whole {res['whole_ms']:.2f} ms, cached prefix {res['cached_ms']:.2f} ms, "
+        f"insert {insert_ms:.1f} ms")
+    cache.close()
     return res
 
 
@@ -409,6 +464,10 @@ def main():
 
     if args.extras and n_map >= 1:
         out["prefill"] = prefill(mf, torch, wl, args, send[mapped[-1]], slots[(n_map - 1) % k], tau, ctx, dev)
+
+    if args.extras and n_map >= 1:
+        out["prefix_reuse"] = prefix_reuse(mf, torch, wl, args, send[mapped[-1]], recv[mapped[-1]], kv_map, tau,
+                                           ctx, dev)
 
     if args.extras and n_map >= 2:
         out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [recv[l] for l in mapped[-2:]],
