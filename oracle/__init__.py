@@ -34,6 +34,7 @@ from .mapflow_oracle import (  # noqa: F401
     mix_heads,
     renormalise,
     retrieve,
+    retrieve_layers,
     retrieve_block_row,
     select_blocks,
 )

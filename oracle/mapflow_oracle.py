@@ -123,18 +123,20 @@ def select_blocks(M_row: np.ndarray, I: int, T_I: float, tau: float) -> dict:
 # ----------------------------------------------------------------------------------------------
 # O4-O7 for one block row: block masses, selection, bf16 probs, kept row mass
 # ----------------------------------------------------------------------------------------------
-def block_masses(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: int, B: int):
+def block_masses(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: int, B: int,
+                 per_head: bool = False):
     """Block-level statistics of block row I of one sequence: the first stage of the staged
     compression in [MapFlow开源, 只存重要的:块稀疏压缩].
 
     M[J] = sum_h sum_{i in I} sum_{j in J} A[h, i, j] for J = 0..I (explicit block sums over the
-    causal softmax map of every sender head); also returns lse [H_s, rows].
+    causal softmax map of every sender head); also returns lse [H_s, rows].  With ``per_head``,
+    M[h, J] is the same sum without the sum over h.
     """
     H_s = Q.shape[0]
     r0 = I * B
     r1 = min(seq_len, (I + 1) * B)
     rows = r1 - r0
-    M = np.zeros(I + 1, dtype=F64)
+    Mh = np.zeros((H_s, I + 1), dtype=F64)
     lse = np.zeros((H_s, rows), dtype=F64)
     for h in range(H_s):
         q = Q[h, seq_start: seq_start + seq_len]
@@ -143,12 +145,18 @@ def block_masses(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: 
         for J in range(I + 1):
             c0 = J * B
             c1 = min(seq_len, (J + 1) * B)
-            M[J] += A[:, c0:c1].sum()
+            Mh[h, J] = A[:, c0:c1].sum()
+    if per_head:
+        return Mh, lse
+    M = np.zeros(I + 1, dtype=F64)
+    for h in range(H_s):
+        M += Mh[h]
     return M, lse
 
 
 def block_row_compress(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: int, I: int,
-                       B: int, tau: float, keep_exact: bool = False) -> dict:
+                       B: int, tau: float, keep_exact: bool = False, per_head_select: bool = False,
+                       per_head_norm: bool = False) -> dict:
     """Compress block row I of one sequence (all sender heads).
 
     Q, K: [H_s, T, d] (the packed batch); the sequence occupies tokens
@@ -159,22 +167,48 @@ def block_row_compress(Q: np.ndarray, K: np.ndarray, seq_start: int, seq_len: in
     select  as ``select_blocks``
     pass 2  probs[J][h, r, c] = bf16(A[h, I*B + r, J*B + c]) for kept J (zero outside the valid /
             causal region); row_kept_mass[h, r] = sum over kept J and c of probs (in fp64).
+
+    Variants the wording allows ([MapFlow 方案, 二] names cross-layer and cross-head mapping;
+    [MapFlow开源, the head-mapping bullet] mixes sender heads), off by default:
+    per_head_select  every sender head selects its own blocks from its own masses M[h, J] with
+                     total mass ``rows`` (same forced blocks, order and stopping rule); the store
+                     keeps the union of the heads' sets and a head's probabilities are 0 in the
+                     blocks it did not select
+    per_head_norm    each head's row is divided by that head's mass over its kept blocks (exact)
+                     before the bf16 rounding, so a head's stored row sums to about 1
     """
     H_s = Q.shape[0]
     r0 = I * B
     r1 = min(seq_len, (I + 1) * B)
     rows = r1 - r0
-    M, lse = block_masses(Q, K, seq_start, seq_len, I, B)
-    T_I = float(H_s * rows)
-    sel = select_blocks(M, I, T_I, tau)
-    kept = sel["kept"]
+    if per_head_select:
+        Mh, lse = block_masses(Q, K, seq_start, seq_len, I, B, per_head=True)
+        sel_h = [select_blocks(Mh[h], I, float(rows), tau) for h in range(H_s)]
+        head_kept = [set(sh["kept"]) for sh in sel_h]
+        kept = sorted(set().union(*head_kept))
+        M = Mh.sum(axis=0)
+        sel = {"kept": kept, "per_head": sel_h}
+        T_I = float(H_s * rows)
+    else:
+        M, lse = block_masses(Q, K, seq_start, seq_len, I, B)
+        T_I = float(H_s * rows)
+        sel = select_blocks(M, I, T_I, tau)
+        kept = sel["kept"]
+        head_kept = [set(kept) for _ in range(H_s)]
     probs = {J: np.zeros((H_s, B, B), dtype=F64) for J in kept}
     exact = {J: np.zeros((H_s, B, B), dtype=F64) for J in kept} if keep_exact else None
     for h in range(H_s):
         q = Q[h, seq_start: seq_start + seq_len]
         k = K[h, seq_start: seq_start + seq_len]
         A, _ = attention_rows(q, k, r0, r1)
+        if per_head_norm:
+            mass = np.zeros(rows, dtype=F64)
+            for J in sorted(head_kept[h]):
+                mass += A[:, J * B: min(seq_len, (J + 1) * B)].sum(axis=1)
+            A = A / mass[:, None]
         for J in kept:
+            if J not in head_kept[h]:
+                continue
             c0 = J * B
             c1 = min(seq_len, (J + 1) * B)
             tile = A[:, c0:c1]
@@ -206,8 +240,10 @@ class OracleBSR:
     exact: np.ndarray | None = None   # unrounded probabilities of the kept blocks, same layout
 
 
-def compress(Q, K, cu_seqlens, tau: float, B: int, keep_exact: bool = False) -> OracleBSR:
-    """mf_compress's definition over a packed batch: every sequence and block row in turn.
+def compress(Q, K, cu_seqlens, tau: float, B: int, keep_exact: bool = False,
+             per_head_select: bool = False, per_head_norm: bool = False) -> OracleBSR:
+    """mf_compress's definition over a packed batch: every sequence and block row in turn
+    (``per_head_select`` / ``per_head_norm``: the variants of ``block_row_compress``).
 
     Varlen reading: each sequence has its own block grid starting at its first token, and its
     block column 0 is its own sink block.
@@ -222,7 +258,7 @@ def compress(Q, K, cu_seqlens, tau: float, B: int, keep_exact: bool = False) -> 
     for s in range(len(cu) - 1):
         n = int(cu[s + 1] - cu[s])
         for I in range((n + B - 1) // B):
-            r = block_row_compress(Q, K, int(cu[s]), n, I, B, tau, keep_exact)
+            r = block_row_compress(Q, K, int(cu[s]), n, I, B, tau, keep_exact, per_head_select, per_head_norm)
             rows.append(r)
             brow_seq.append(s)
             brow_I.append(I)
@@ -343,6 +379,42 @@ def retrieve(bsr: OracleBSR, W, V, kv_head_map, page_table=None, page_size: int 
         blocks = {int(bsr.block_idx[t]): src[t] for t in range(lo, hi)}
         O[tok0: tok0 + rows] = retrieve_block_row(blocks, bsr.B, rows, tok0, s, int(cu[s]), n, W,
                                                   V, kv_head_map, page_table, page_size)
+    return O
+
+
+def retrieve_layers(bsrs, Ws, V, kv_head_map) -> np.ndarray:
+    """One receiver layer from the stores of several sender layers (contiguous V only).
+
+    [MapFlow 方案, 二]: the mapping is linear across layers and across heads.  Reading: the mixed
+    map of receiver head g is sum over layers l and sender heads h of W_l[g, h] P_l[h], with P_l
+    zero outside layer l's kept blocks; the row is renormalised over the union of kept blocks and
+    multiplied by the receiver's V, as for one layer.
+    """
+    first = bsrs[0]
+    B = first.B
+    cu = first.cu_seqlens
+    Ws = [np.asarray(W, dtype=F64) for W in Ws]
+    H_r = Ws[0].shape[0]
+    T = first.row_kept_mass.shape[1]
+    O = np.zeros((T, H_r, V.shape[-1]), dtype=F64)
+    for b in range(len(first.brow_seq)):
+        s = int(first.brow_seq[b])
+        I = int(first.brow_I[b])
+        n = int(cu[s + 1] - cu[s])
+        rows = min(n, (I + 1) * B) - I * B
+        tok0 = int(cu[s]) + I * B
+        union = sorted({int(bsr.block_idx[t]) for bsr in bsrs
+                        for t in range(int(bsr.block_ptr[b]), int(bsr.block_ptr[b + 1]))})
+        Ahat = None
+        for bsr, W in zip(bsrs, Ws):
+            lo, hi = int(bsr.block_ptr[b]), int(bsr.block_ptr[b + 1])
+            blocks = {int(bsr.block_idx[t]): bsr.probs[t] for t in range(lo, hi)}
+            full = {J: blocks.get(J, np.zeros((bsr.H_s, B, B), dtype=F64)) for J in union}
+            P, keys = gather_row_probs(full, B, rows, int(cu[s]), n)
+            part = mix_heads(P, W)
+            Ahat = part if Ahat is None else Ahat + part
+        Abar, _ = renormalise(Ahat)
+        O[tok0: tok0 + rows] = apply_v(Abar, keys, V, kv_head_map)
     return O
 
 

@@ -424,6 +424,84 @@ def _catches(monkeypatch, name, bad, pin):
             pin()
 
 
+# ------------------------------------------------------------------ variants (next row 4 of the scope)
+def test_per_head_selection_reduces_to_shared_selection_with_one_head():
+    rng = np.random.default_rng(21)
+    q, k = _rand_qk(rng, 1, 150, 16)
+    cu = [0, 150]
+    a = oracle.compress(q, k, cu, 0.6, 32)
+    b = oracle.compress(q, k, cu, 0.6, 32, per_head_select=True)
+    assert np.array_equal(a.block_idx, b.block_idx) and np.array_equal(a.probs, b.probs)
+    assert np.array_equal(a.row_kept_mass, b.row_kept_mass)
+
+
+def test_per_head_selection_invariants_by_brute_force():
+    """Each head's own set is the brute-force selection of its own masses (total = rows); the
+    store keeps their union and a head's probabilities vanish outside its own set."""
+    rng = np.random.default_rng(22)
+    q, k = _rand_qk(rng, 3, 170, 16)
+    cu = [0, 170]
+    B, tau = 32, 0.55
+    st = oracle.compress(q, k, cu, tau, B, per_head_select=True)
+    full = oracle.compress(q, k, cu, 1.0, B)                 # every block, exact per-head values
+    for b, r in enumerate(st.rows):
+        I, rows = r["I"], r["rows"]
+        union = set()
+        for h in range(3):
+            A, _ = mo.attention_rows(q[h].astype(np.float64), k[h].astype(np.float64), I * B, I * B + rows)
+            masses = np.array([A[:, J * B: min(170, (J + 1) * B)].sum() for J in range(I + 1)])
+            own = _brute_select(masses, I, float(rows), tau)
+            union |= set(own)
+            lo, hi = int(st.block_ptr[b]), int(st.block_ptr[b + 1])
+            for t in range(lo, hi):
+                J = int(st.block_idx[t])
+                ref = full.probs[int(full.block_ptr[b]) + J][h]
+                assert np.array_equal(st.probs[t][h], ref if J in own else np.zeros_like(ref))
+        assert sorted(union) == list(st.block_idx[int(st.block_ptr[b]): int(st.block_ptr[b + 1])])
+
+
+def test_per_head_normalisation():
+    rng = np.random.default_rng(23)
+    q, k = _rand_qk(rng, 2, 140, 16)
+    cu = [0, 140]
+    # every block kept: each head's kept mass is exactly 1, so nothing changes
+    a = oracle.compress(q, k, cu, 1.0, 32)
+    b = oracle.compress(q, k, cu, 1.0, 32, per_head_norm=True)
+    assert np.array_equal(a.probs, b.probs)
+    # otherwise each head's stored row sums to 1 up to its bf16 roundings, and the values are the
+    # exact map divided by the head's exact kept mass
+    st = oracle.compress(q, k, cu, 0.5, 32, per_head_norm=True, keep_exact=True)
+    plain = oracle.compress(q, k, cu, 0.5, 32, keep_exact=True)
+    assert np.array_equal(st.block_idx, plain.block_idx)
+    for b, r in enumerate(st.rows):
+        lo, hi = int(st.block_ptr[b]), int(st.block_ptr[b + 1])
+        rows = r["rows"]
+        s = st.probs[lo:hi, :, :rows].sum(axis=(0, 3))                       # [H, rows]
+        assert np.all(np.abs(s - 1.0) <= 2.0 ** -8)
+        mass = plain.exact[lo:hi, :, :rows].sum(axis=(0, 3))                 # exact kept mass
+        ratio = plain.exact[lo:hi, :, :rows] / mass[None, :, :, None]
+        assert np.allclose(st.exact[lo:hi, :, :rows], ratio, rtol=1e-12, atol=0)
+
+
+def test_cross_layer_retrieve_reductions():
+    """One layer is the single-layer retrieve; two copies of one store with W split between them
+    give the retrieve with the whole W; two layers with one-hot weights on one layer's heads give
+    that layer's retrieve restricted to the union of blocks (zeros elsewhere do not count)."""
+    x = synth.make_layer_inputs(synth.WORKLOADS["tiny"], 24, lengths=[160], H_s=4, H_r=3, H_kv=3, d=16)
+    a = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], 0.6, 32)
+    W = x["w"].astype(np.float64)                # split exactly: 0.25 W + 0.75 W == W in fp64
+    ref = oracle.retrieve(a, W, x["v_r"], x["kv_head_map"])
+    assert np.allclose(oracle.retrieve_layers([a], [W], x["v_r"], x["kv_head_map"]), ref, rtol=1e-12, atol=1e-12)
+    split = oracle.retrieve_layers([a, a], [0.25 * W, 0.75 * W], x["v_r"], x["kv_head_map"])
+    assert np.allclose(split, ref, rtol=1e-12, atol=1e-12)
+    y = synth.make_layer_inputs(synth.WORKLOADS["tiny"], 25, lengths=[160], H_s=4, H_r=3, H_kv=3, d=16)
+    b = oracle.compress(y["q_s"], y["k_s"], y["cu_seqlens"], 0.6, 32)
+    only_a = oracle.retrieve_layers([a, b], [W, np.zeros_like(W)], x["v_r"], x["kv_head_map"])
+    assert np.allclose(only_a, ref, rtol=1e-12, atol=1e-12)
+    both = oracle.retrieve_layers([a, b], [W, W], x["v_r"], x["kv_head_map"])
+    assert not np.allclose(both, ref)            # the second layer does contribute
+
+
 def test_pins_catch_planted_mistakes(monkeypatch):
     orig_rows = mo.attention_rows
     orig_mix = mo.mix_heads
