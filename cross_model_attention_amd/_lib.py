@@ -54,6 +54,8 @@ _SIGNATURES = {
                                  POINTER(MfBsr), c_void_p]),
     "mf_compress_prefill_into": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int32, c_float,
                                          POINTER(MfBsr), c_void_p, c_void_p]),
+    "mf_compress_into_ex": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_float, ctypes.c_uint32,
+                                    POINTER(MfBsr), c_void_p]),
     "mf_bsr_sync": (c_int, [c_void_p, POINTER(MfBsr), c_void_p]),
     "mf_compress": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32, _P_I32, c_int32,
                             c_float, c_int32, c_void_p, POINTER(MfBsr)]),

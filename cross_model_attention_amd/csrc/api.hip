@@ -168,7 +168,7 @@ struct VfragOwner {
 
 struct mf_ctx {
   int device = 0;
-  Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile;
+  Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile, hflags, lse2n;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
   mf_vfrag vf_prefill{};    // context-owned prepared sender V (mf_compress_prefill_into)
@@ -485,7 +485,7 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
   for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf, &ctx->ktile,
-                     &ctx->dense_tables})
+                     &ctx->hflags, &ctx->lse2n, &ctx->dense_tables})
     if (s->p) (void)hipFree(s->p);
   vfrag_release(&ctx->vf_retrieve);
   vfrag_release(&ctx->vf_dense);
@@ -681,6 +681,32 @@ MF_EXPORT mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, 
   if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
   mf::CompressArgs a;
   if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
+  MF_HIP(mf::compress_fill(a, s), "compress gather launch");
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_compress_into_ex(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
+                                        int32_t d, float tau, uint32_t options, mf_bsr* bsr, void* stream) {
+  if (options & ~(uint32_t)(MF_SELECT_PER_HEAD | MF_NORM_PER_HEAD))
+    return fail(MF_ERR_INVALID, "unknown option bits 0x%x", options);
+  mf_status st = validate_compress(Q, K, dtype, d, tau, bsr);
+  if (st != MF_OK) return st;
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress
+  mf::CompressArgs a;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  a.options = (int)options;
+  if (options & MF_SELECT_PER_HEAD) {
+    if ((st = ensure(ctx->hflags, (size_t)bsr->H_s * bsr->n_brow * bsr->nb_max + 256, "per-head flags")) != MF_OK)
+      return st;
+    a.hflags = static_cast<uint8_t*>(ctx->hflags.p);
+  }
+  if (options & MF_NORM_PER_HEAD) {
+    if ((st = ensure(ctx->lse2n, (size_t)bsr->H_s * bsr->T * 4 + 256, "per-head logsumexp")) != MF_OK) return st;
+    a.lse2n = static_cast<float*>(ctx->lse2n.p);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
   MF_HIP(mf::compress_fill(a, s), "compress gather launch");

@@ -89,26 +89,16 @@ __device__ __forceinline__ bool sel_before(double ka, int ia, double kb, int ib)
   return ka > kb || (ka == kb && ia < ib);
 }
 
-__global__ __launch_bounds__(256) void k_select(const double* __restrict__ M,
-                                                const int32_t* __restrict__ info, int nb_max,
-                                                int H_s, int B, double tau,
-                                                const uint8_t* __restrict__ active,
-                                                uint8_t* __restrict__ flags,
-                                                int32_t* __restrict__ counts) {
-  extern __shared__ unsigned char sm_raw[];
-  const int brow = blockIdx.x;
-  if (active != nullptr && !active[brow]) {        // a row outside the compressed range keeps nothing
-    if (threadIdx.x == 0) counts[brow] = 0;
-    return;
-  }
-  const BrowInfo bi = load_info(info, brow);
-  const int I = bi.I, n = I + 1;
-  const int rows = min(B, bi.n - I * B);
-  const double* Mrow = M + (size_t)brow * nb_max;
-  uint8_t* frow = flags + (size_t)brow * nb_max;
+// One block row's selection over masses Mrow[0..I] (total mass heads * rows): forced sink and
+// diagonal, then a bitonic sort of (-mass, column) in LDS and a sequential walk by one lane.
+template <typename MT>
+__device__ __forceinline__ void select_row(const MT* __restrict__ Mrow, int I, int rows, int heads, double tau,
+                                           uint8_t* __restrict__ frow, int32_t* __restrict__ count_out,
+                                           unsigned char* sm_raw) {
+  const int n = I + 1;
   if (tau >= 1.0) {
     for (int J = threadIdx.x; J < n; J += blockDim.x) frow[J] = 1;
-    if (threadIdx.x == 0) counts[brow] = n;
+    if (threadIdx.x == 0 && count_out) *count_out = n;
     return;
   }
   int N = 1;
@@ -117,7 +107,7 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ M,
   int* idx = reinterpret_cast<int*>(sm_raw + sizeof(double) * N);
   for (int t = threadIdx.x; t < N; t += blockDim.x) {
     const bool real = t < n && t != 0 && t != I;
-    key[t] = real ? Mrow[t] : -1.0;   // masses are >= 0; -1 marks forced / padding slots
+    key[t] = real ? (double)Mrow[t] : -1.0;   // masses are >= 0; -1 marks forced / padding slots
     idx[t] = t;
     if (t < n) frow[t] = (t == 0 || t == I) ? 1 : 0;
   }
@@ -143,21 +133,108 @@ __global__ __launch_bounds__(256) void k_select(const double* __restrict__ M,
     }
   }
   if (threadIdx.x == 0) {
-    double c = Mrow[0];
+    double c = (double)Mrow[0];
     int cnt = 1;
     if (I > 0) {
-      c += Mrow[I];
+      c += (double)Mrow[I];
       cnt = 2;
     }
-    const double target = tau * (double)(H_s * rows);
+    const double target = tau * (double)(heads * rows);
     for (int t = 0; t < N; ++t) {
       if (key[t] < 0.0 || c >= target) break;
       frow[idx[t]] = 1;
       c += key[t];
       ++cnt;
     }
-    counts[brow] = cnt;
+    if (count_out) *count_out = cnt;
   }
+}
+
+__global__ __launch_bounds__(256) void k_select(const double* __restrict__ M,
+                                                const int32_t* __restrict__ info, int nb_max,
+                                                int H_s, int B, double tau,
+                                                const uint8_t* __restrict__ active,
+                                                uint8_t* __restrict__ flags,
+                                                int32_t* __restrict__ counts) {
+  extern __shared__ unsigned char sm_raw[];
+  const int brow = blockIdx.x;
+  if (active != nullptr && !active[brow]) {        // a row outside the compressed range keeps nothing
+    if (threadIdx.x == 0) counts[brow] = 0;
+    return;
+  }
+  const BrowInfo bi = load_info(info, brow);
+  const int rows = min(B, bi.n - bi.I * B);
+  select_row<double>(M + (size_t)brow * nb_max, bi.I, rows, H_s, tau, flags + (size_t)brow * nb_max, counts + brow,
+                     sm_raw);
+}
+
+// Selection per sender head (the per-head variant): head h = blockIdx.y selects from its own
+// block masses with total mass rows; the kept flags of every head are then united by k_union.
+__global__ __launch_bounds__(256) void k_select_heads(const float* __restrict__ Mh,
+                                                      const int32_t* __restrict__ info, int n_brow,
+                                                      int nb_max, int B, double tau,
+                                                      const uint8_t* __restrict__ active,
+                                                      uint8_t* __restrict__ hflags) {
+  extern __shared__ unsigned char sm_raw[];
+  const int brow = blockIdx.x, h = blockIdx.y;
+  if (active != nullptr && !active[brow]) return;
+  const BrowInfo bi = load_info(info, brow);
+  const int rows = min(B, bi.n - bi.I * B);
+  const size_t off = ((size_t)h * n_brow + brow) * nb_max;
+  select_row<float>(Mh + off, bi.I, rows, 1, tau, hflags + off, nullptr, sm_raw);
+}
+
+// Kept flags of a block row = union over the heads' own selections; counts for the scan.
+__global__ __launch_bounds__(256) void k_union(const uint8_t* __restrict__ hflags, int H_s, int n_brow,
+                                               int nb_max, const int32_t* __restrict__ info,
+                                               const uint8_t* __restrict__ active,
+                                               uint8_t* __restrict__ flags, int32_t* __restrict__ counts) {
+  __shared__ int part[4];
+  const int brow = blockIdx.x;
+  if (active != nullptr && !active[brow]) {
+    if (threadIdx.x == 0) counts[brow] = 0;
+    return;
+  }
+  const int I = info[4 * brow + 3];
+  int cnt = 0;
+  for (int J = threadIdx.x; J <= I; J += blockDim.x) {
+    uint8_t f = 0;
+    for (int h = 0; h < H_s; ++h) f |= hflags[((size_t)h * n_brow + brow) * nb_max + J];
+    flags[(size_t)brow * nb_max + J] = f ? 1 : 0;
+    cnt += f ? 1 : 0;
+  }
+  cnt = (int)wave_sum((float)cnt);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) counts[brow] = part[0] + part[1] + part[2] + part[3];
+}
+
+// Per-head normalisation (variant): each head's kept mass of every query row, from the block
+// statistics (z, r) of its kept blocks, folded into that head's logsumexp for the gather:
+// lse2n = lse2 + log2(sum over kept J of z_iJ 2^(r_iJ - lse2)).
+__global__ void k_keptnorm(const float2* __restrict__ zbuf, const float* __restrict__ lse2,
+                           const int32_t* __restrict__ block_ptr, const int32_t* __restrict__ block_idx,
+                           const int32_t* __restrict__ info, const int32_t* __restrict__ coff,
+                           const int32_t* __restrict__ counters, const uint8_t* __restrict__ active,
+                           const uint8_t* __restrict__ hflags, int n_brow, int nb_max, int B, int64_t n_causal,
+                           int64_t T_tot, int64_t capacity, float* __restrict__ lse2n) {
+  const int brow = blockIdx.x, h = blockIdx.y, r = threadIdx.x;
+  if (active != nullptr && !active[brow]) return;
+  const BrowInfo bi = load_info(info, brow);
+  const int rows = min(B, bi.n - bi.I * B);
+  if (r >= rows) return;
+  const int64_t nnzb = min((int64_t)counters[0], capacity);
+  const int64_t lo = min((int64_t)block_ptr[brow], nnzb), hi = min((int64_t)block_ptr[brow + 1], nnzb);
+  const float2* zrow = zbuf + ((size_t)h * n_causal + coff[brow]) * B;
+  const float l = lse2[(size_t)h * T_tot + bi.tok0 + r];
+  double s = 0.0;
+  for (int64_t t = lo; t < hi; ++t) {
+    const int J = block_idx[t];
+    if (hflags != nullptr && !hflags[((size_t)h * n_brow + brow) * nb_max + J]) continue;
+    const float2 e = zrow[(size_t)J * B + r];
+    if (e.y > kNegInf) s += (double)e.x * (double)fast_exp2(e.y - l);
+  }
+  lse2n[(size_t)h * T_tot + bi.tok0 + r] = s > 0.0 ? (float)((double)l + log2(s)) : l;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -397,6 +474,7 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
                                                 const int32_t* __restrict__ counters,
                                                 int64_t capacity, const float* __restrict__ lse2,
                                                 float scale2, const unsigned char* __restrict__ ktile,
+                                                const uint8_t* __restrict__ hflags, int nb_max,
                                                 uint16_t* __restrict__ probs, float* __restrict__ part) {
   constexpr int MT = B / 16;
   constexpr int NT = B / 16;
@@ -482,8 +560,10 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     const bool overlap = NBUF == 2 && t > t0;
     const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
-    gather_block<T, B, D>(!active || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next,
-                          J, active ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev, prev_dst);
+    // a head that did not select this block (per-head selection) stores zeros
+    const bool keep = active && (hflags == nullptr || hflags[((size_t)h * n_brow + brow) * nb_max + J]);
+    gather_block<T, B, D>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next,
+                          J, keep ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev, prev_dst);
     {
       // per-row sums over the block's 64 keys: lane c of group a ends with row 16 (c/4) + 4a + c%4
       float flat[MT * 4];
@@ -555,7 +635,8 @@ static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
                                        : (unsigned)a.n_order * HG * chunks;
   hipLaunchKernelGGL((k_gather<T, B, D>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
                      (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.n_order, a.block_ptr, a.block_idx,
-                     a.counters, a.capacity, a.lse2, a.scale2, (const unsigned char*)a.ktile, a.probs,
+                     a.counters, a.capacity, (a.options & 2) ? a.lse2n : a.lse2, a.scale2,
+                     (const unsigned char*)a.ktile, (a.options & 1) ? a.hflags : nullptr, a.nb_max, a.probs,
                      a.part);
   return hipGetLastError();
 }
@@ -592,14 +673,22 @@ hipError_t compress_plan(const CompressArgs& a, hipStream_t s) {
   hipError_t e = ktile_dispatch(a, s);
   if (e != hipSuccess) return e;
   if ((e = stats_dispatch(a, s)) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_head_reduce, dim3(a.n_brow), dim3(256), 0, s, a.Mh, a.H_s, a.n_brow,
-                     a.nb_max, a.info, a.M);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   int N = 1;
   while (N < a.nb_max) N <<= 1;
   const size_t lds = (size_t)N * (sizeof(double) + sizeof(int));
-  hipLaunchKernelGGL(k_select, dim3(a.n_brow), dim3(256), lds, s, a.M, a.info, a.nb_max, a.H_s,
-                     a.B, a.tau, a.active, a.flags, a.counts);
+  if (a.options & 1) {                            // per-head selection, then the union
+    hipLaunchKernelGGL(k_select_heads, dim3(a.n_brow, a.H_s), dim3(256), lds, s, a.Mh, a.info, a.n_brow,
+                       a.nb_max, a.B, a.tau, a.active, a.hflags);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_union, dim3(a.n_brow), dim3(256), 0, s, a.hflags, a.H_s, a.n_brow, a.nb_max, a.info,
+                       a.active, a.flags, a.counts);
+  } else {
+    hipLaunchKernelGGL(k_head_reduce, dim3(a.n_brow), dim3(256), 0, s, a.Mh, a.H_s, a.n_brow,
+                       a.nb_max, a.info, a.M);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_select, dim3(a.n_brow), dim3(256), lds, s, a.M, a.info, a.nb_max, a.H_s,
+                       a.B, a.tau, a.active, a.flags, a.counts);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, a.counts, a.n_brow, a.capacity,
                      a.block_ptr, a.counters);
@@ -611,6 +700,12 @@ hipError_t compress_fill(const CompressArgs& a, hipStream_t s) {
                      a.nb_max, a.capacity, a.active, a.block_idx, a.block_row);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.options & 2) {                            // per-head normalisation: fold kept mass into lse
+    hipLaunchKernelGGL(k_keptnorm, dim3(a.n_brow, a.H_s), dim3(a.B), 0, s, a.zbuf, a.lse2, a.block_ptr,
+                       a.block_idx, a.info, a.coff, a.counters, a.active, (a.options & 1) ? a.hflags : nullptr,
+                       a.n_brow, a.nb_max, a.B, a.n_causal, a.T, a.capacity, a.lse2n);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if ((e = gather_dispatch(a, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_rowmass, dim3(a.n_brow, a.H_s), dim3(a.B), 0, s, a.part, a.block_ptr,
                      a.info, a.counters, a.H_s, a.B, a.T, a.capacity, a.rkm);

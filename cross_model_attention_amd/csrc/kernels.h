@@ -23,6 +23,9 @@ struct CompressArgs {
   int n_order;           // entries of order[]
   int64_t n_causal;
   double tau;
+  int options;           // MF_SELECT_PER_HEAD | MF_NORM_PER_HEAD (variants), 0 = the method as read
+  uint8_t* hflags;       // [H_s][n_brow][nb_max] per-head kept flags (per-head selection)
+  float* lse2n;          // [H_s][T] logsumexp plus log2 of the head's kept mass (per-head normalisation)
   float scale2;          // log2(e) / sqrt(d)
   // context scratch
   float2* zbuf;          // [H_s][n_causal][B] per (query, key block): {z, block max}

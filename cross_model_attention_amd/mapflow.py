@@ -320,13 +320,20 @@ def compress(Q: torch.Tensor, K: torch.Tensor, tau: float, B: int, cu_seqlens=No
     return BlockStore(ctx, raw, cu)
 
 
-def compress_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, tau: float, stream=None) -> None:
-    """mf_compress_into: asynchronous compress into a preallocated store."""
+def compress_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, tau: float, stream=None,
+                  per_head_select: bool = False, per_head_norm: bool = False) -> None:
+    """mf_compress_into (or mf_compress_into_ex with the variant options): asynchronous compress
+    into a preallocated store."""
     _check_qk(Q, K)
     if Q.shape[0] != store.raw.H_s or Q.shape[1] != store.raw.T:
         raise ValueError("Q/K shape does not match the store's geometry")
-    check(_L.mf_compress_into(store.ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dtype(Q), int(Q.shape[2]),
-                              float(tau), ctypes.byref(store.raw), _stream(stream)))
+    opts = (1 if per_head_select else 0) | (2 if per_head_norm else 0)
+    if opts:
+        check(_L.mf_compress_into_ex(store.ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dtype(Q), int(Q.shape[2]),
+                                     float(tau), opts, ctypes.byref(store.raw), _stream(stream)))
+    else:
+        check(_L.mf_compress_into(store.ctx.handle, _dev(Q, "Q"), _dev(K, "K"), _dtype(Q), int(Q.shape[2]),
+                                  float(tau), ctypes.byref(store.raw), _stream(stream)))
 
 
 def compress_prefill_into(store: BlockStore, Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, tau: float,

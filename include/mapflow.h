@@ -229,6 +229,21 @@ mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const void* K, co
                                    mf_dtype dtype, int32_t d, float tau, mf_bsr* bsr, float* O,
                                    void* stream);
 
+/*
+ * Variants of the compression that the pages' wording allows ([MapFlow 方案, 二]: cross-layer and
+ * cross-head linear mapping; [MapFlow开源, the head-mapping bullet]).  Option bits:
+ *   MF_SELECT_PER_HEAD  every sender head selects its own blocks (forced sink and diagonal, then
+ *                       its own block masses in descending order until tau * rows); the store
+ *                       keeps the union, and a head stores zeros in blocks it did not select
+ *   MF_NORM_PER_HEAD    each head's kept row is divided by that head's mass over its kept blocks
+ *                       before rounding to bf16 (so each head's stored row sums to ~1); the
+ *                       retrieve then mixes the normalised heads and renormalises as usual
+ * options = 0 is mf_compress_into.  The store layout and every retrieve call are unchanged.
+ */
+enum { MF_SELECT_PER_HEAD = 1, MF_NORM_PER_HEAD = 2 };
+mf_status mf_compress_into_ex(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype, int32_t d,
+                              float tau, uint32_t options, mf_bsr* bsr, void* stream);
+
 /* Wait for `stream`, read the kept-block count into bsr->nnzb; MF_ERR_CAPACITY on overflow. */
 mf_status mf_bsr_sync(mf_ctx* ctx, mf_bsr* bsr, void* stream);
 

@@ -428,3 +428,42 @@ def test_prefix_cache_reuses_a_previous_request(mf):
     assert _lib.load().mf_bsr_free(None, ctypes.byref(view2.raw)) == _lib.MF_ERR_INVALID
     cache.close()
     small.close()
+
+
+@pytest.mark.parametrize("case", [
+    dict(wl="tiny", seed=13, lengths=[150, 1, 90], H_s=4, d=64, dtype="f32", sel=True, norm=False),
+    dict(wl="pair_8b3b_8k", seed=14, lengths=[260, 70], H_s=8, d=128, dtype="bf16", sel=True, norm=False),
+    dict(wl="pair_8b3b_8k", seed=15, lengths=[260, 70], H_s=8, d=128, dtype="bf16", sel=False, norm=True),
+    dict(wl="pair_8b3b_8k", seed=16, lengths=[200], H_s=16, d=64, dtype="bf16", sel=True, norm=True),
+])
+def test_compress_variants(mf, case):
+    """Per-head selection and per-head normalisation against the oracle's variants: the same kept
+    sets (the union of the heads' own sets), zeros where a head did not select a block, stored
+    values within one bf16 ulp of the oracle's, kept mass the sum of the stored values; then the
+    unchanged retrieve against the oracle's retrieve of its own variant store."""
+    wl = synth.WORKLOADS[case["wl"]]
+    x = synth.make_layer_inputs(wl, case["seed"], lengths=case["lengths"], H_s=case["H_s"], H_r=6, H_kv=2,
+                                d=case["d"])
+    tau = _f32(wl.tau if case["wl"] != "tiny" else 0.7)
+    say(f"case: compress variant {case}")
+    Q, K = to_dev(x["q_s"], case["dtype"]), to_dev(x["k_s"], case["dtype"])
+    store = mf.BlockStore.create(case["H_s"], wl.B, x["cu_seqlens"])
+    mf.compress_into(store, Q, K, tau, per_head_select=case["sel"], per_head_norm=case["norm"])
+    store.sync()
+    host = store.to_host()
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B, per_head_select=case["sel"],
+                          per_head_norm=case["norm"])
+    assert np.array_equal(host["block_ptr"], ref.block_ptr)
+    assert np.array_equal(host["block_idx"], ref.block_idx)
+    assert np.all(np.abs(host["probs"] - ref.probs) <= ulp_bf16(ref.probs) + 1e-6)
+    cu, B = x["cu_seqlens"], wl.B
+    for b, (s, I) in enumerate(brow_table(cu, B)):
+        n = int(cu[s + 1] - cu[s])
+        tok0, rows_b = int(cu[s]) + I * B, min(n, I * B + B) - I * B
+        lo, hi = host["block_ptr"][b], host["block_ptr"][b + 1]
+        want = host["probs"][lo:hi, :, :rows_b, :].sum(axis=(0, 3))
+        assert np.allclose(host["row_kept_mass"][:, tok0:tok0 + rows_b], want, rtol=1e-6, atol=1e-7)
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], case["dtype"])
+    O = mf.retrieve(store, W, V, x["kv_head_map"])
+    torch.cuda.synchronize()
+    assert_out_close(O.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], x["kv_head_map"]), "O_r (variant)")
