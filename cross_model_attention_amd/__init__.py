@@ -20,6 +20,7 @@ from .mapflow import (  # noqa: F401
     prefix_hashes,
     probs_store_to_canonical,
     retrieve,
+    retrieve_layers,
     retrieve_multi,
     retrieve_prepared,
     v_prepare,

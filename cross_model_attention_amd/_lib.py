@@ -64,6 +64,8 @@ _SIGNATURES = {
     "mf_vfrag_free": (c_int, [c_void_p, POINTER(MfVfrag)]),
     "mf_retrieve_prepared": (c_int, [c_void_p, POINTER(MfBsr), c_void_p, c_int32, POINTER(MfVfrag),
                                      _P_I32, c_void_p, c_void_p]),
+    "mf_retrieve_layers": (c_int, [c_void_p, c_int32, POINTER(MfBsr), POINTER(c_void_p), c_int32, POINTER(MfVfrag),
+                                   _P_I32, c_void_p, c_void_p]),
     "mf_retrieve_multi": (c_int, [c_void_p, POINTER(MfBsr), c_int32, POINTER(c_void_p), _P_I32,
                                   POINTER(POINTER(MfVfrag)), POINTER(_P_I32), POINTER(c_void_p), c_void_p]),
     "mf_retrieve": (c_int, [c_void_p, POINTER(MfBsr), c_void_p, c_int32, c_void_p, c_int, c_int32,

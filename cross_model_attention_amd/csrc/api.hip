@@ -168,7 +168,7 @@ struct VfragOwner {
 
 struct mf_ctx {
   int device = 0;
-  Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile, hflags, lse2n;
+  Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile, hflags, lse2n, den;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
   mf_vfrag vf_prefill{};    // context-owned prepared sender V (mf_compress_prefill_into)
@@ -485,7 +485,7 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
   (void)hipSetDevice(ctx->device);
   (void)hipDeviceSynchronize();
   for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf, &ctx->ktile,
-                     &ctx->hflags, &ctx->lse2n, &ctx->dense_tables})
+                     &ctx->hflags, &ctx->lse2n, &ctx->den, &ctx->dense_tables})
     if (s->p) (void)hipFree(s->p);
   vfrag_release(&ctx->vf_retrieve);
   vfrag_release(&ctx->vf_dense);
@@ -831,7 +831,8 @@ MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {
 // one row-tile work item, so each stored probability tile is read from HBM once for all of them.
 static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, const float* const* W,
                                  const int32_t* H_r, const mf_vfrag* const* vf,
-                                 const int32_t* const* kvmap, float* const* O, void* stream) {
+                                 const int32_t* const* kvmap, float* const* O, void* stream,
+                                 int accumulate = 0, float* den = nullptr) {
   if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
   if (n_recv < 1 || n_recv > mf::kMaxRecv)
     return fail(MF_ERR_INVALID, "n_recv = %d outside [1, %d]", n_recv, mf::kMaxRecv);
@@ -865,6 +866,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
     rv.O = O[r];
     rv.H_r = H_r[r];
     rv.H_kv = v->H_kv;
+    rv.den = den;
   }
   // Head splits.  Each receiver's heads (in KV order) form one part, or two equal parts above 24
   // heads.  Parts are packed first-fit, largest first, into splits of at most 24 heads (a split
@@ -909,6 +911,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   a.T = bsr->T;
   a.rkm = bsr->row_kept_mass;
   a.n_recv = n_recv;
+  a.accumulate = accumulate;
   for (int HP = 1; HP <= 3; ++HP) {
     a.HP = HP;
     a.n_split = 0;
@@ -952,6 +955,32 @@ MF_EXPORT mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_
                                       const mf_vfrag* const* vf, const int32_t* const* kvmap,
                                       float* const* O, void* stream) {
   return retrieve_launch(ctx, bsr, n_recv, W, H_r, vf, kvmap, O, stream);
+}
+
+MF_EXPORT mf_status mf_retrieve_layers(mf_ctx* ctx, int32_t n_layers, const mf_bsr* stores,
+                                       const float* const* W, int32_t H_r, const mf_vfrag* vf,
+                                       const int32_t* kvmap, float* O, void* stream) {
+  if (n_layers < 1 || !stores || !W) return fail(MF_ERR_INVALID, "need n_layers >= 1 stores and weights");
+  if (n_layers == 1) return mf_retrieve_prepared(ctx, &stores[0], W[0], H_r, vf, kvmap, O, stream);
+  for (int l = 0; l < n_layers; ++l) {
+    const mf_bsr& b = stores[l];
+    if (!b._owner || !W[l]) return fail(MF_ERR_INVALID, "store or W of layer %d is NULL", l);
+    const BsrOwner* o0 = static_cast<const BsrOwner*>(stores[0]._owner);
+    const BsrOwner* ol = static_cast<const BsrOwner*>(b._owner);
+    if (b.B != stores[0].B || ol->geom.cu != o0->geom.cu || ol->geom.active != o0->geom.active)
+      return fail(MF_ERR_INVALID, "store of layer %d has another geometry (B, cu_seqlens or row range)", l);
+  }
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  if ((st = ensure(ctx->den, (size_t)stores[0].T * H_r * 4 + 256, "denominators")) != MF_OK) return st;
+  float* den = static_cast<float*>(ctx->den.p);
+  for (int l = 0; l < n_layers; ++l) {
+    const int mode = l == 0 ? 1 : (l + 1 < n_layers ? 2 : 3);
+    const float* Wl = W[l];
+    st = retrieve_launch(ctx, &stores[l], 1, &Wl, &H_r, &vf, &kvmap, &O, stream, mode, den);
+    if (st != MF_OK) return st;
+  }
+  return MF_OK;
 }
 
 MF_EXPORT mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,

@@ -83,6 +83,7 @@ struct RecvArgs {
   const uint16_t* vfrag; // prepared V tiles
   const int32_t* vexps;  // per-KV-head scale exponents
   float* O;              // [T][H_r][d]
+  float* den;            // [T][H_r] running denominators (cross-layer accumulation), else NULL
   int H_r, H_kv;
 };
 
@@ -102,6 +103,8 @@ struct RetrieveArgs {
   int64_t T;
   const float* rkm;
   int n_recv, n_split;
+  int accumulate;        // 0: normalised output; across sender layers 1: write the unnormalised
+                         // output and denominator, 2: add to them, 3: add and normalise
   int HP;                                  // heads per wave: a split holds up to 8*HP heads
   int8_t split_nslots[kMaxSplit];          // heads in each split; they fill its leading slots
   int8_t slot_recv[kMaxSplit][kMaxSlots];  // receiver of each slot

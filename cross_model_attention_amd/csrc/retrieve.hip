@@ -199,6 +199,7 @@ struct SlotInfo {
   const MF_GLOBAL float* w;
   const MF_GLOBAL uint16_t* v;
   MF_GLOBAL float* o;
+  MF_GLOBAL float* dn;   // running denominator of the head (cross-layer accumulation), row stride H_r
   int ostride;
   int vexp;
 };
@@ -269,10 +270,11 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     const RecvArgs& rv = args.recv[args.slot_recv[split][j]];
     const int kv = args.slot_kv[split][j];
     SlotInfo si{nullptr, (const MF_GLOBAL uint16_t*)(rv.vfrag + (size_t)kv * n_brow * (NCH * NDT * 512)),
-                nullptr, 0, 0};
+                nullptr, nullptr, 0, 0};
     if (g >= 0) {
       si.w = (const MF_GLOBAL float*)(rv.W + (size_t)g * H_s);
       si.o = (MF_GLOBAL float*)(rv.O + (size_t)g * D);
+      si.dn = rv.den ? (MF_GLOBAL float*)(rv.den + g) : nullptr;
       si.ostride = rv.H_r * D;
       si.vexp = rv.vexps[kv];
     }
@@ -485,14 +487,40 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     // den carries the same 2^s_g as the mixed map, so only V's scale is undone here
     const SlotInfo& si = s_slot[w * HP + j];
     const float unscale = ldexpf(1.f, -si.vexp);
+    if (args.accumulate == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ii = 4 * a + i;
-      if (ii >= rows) continue;
-      const float inv = unscale / s_den[w * HP + j][ii];
-      MF_GLOBAL float* orow = si.o + (size_t)(bi.tok0 + row0 + ii) * si.ostride;
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 4 * a + i;
+        if (ii >= rows) continue;
+        const float inv = unscale / s_den[w * HP + j][ii];
+        MF_GLOBAL float* orow = si.o + (size_t)(bi.tok0 + row0 + ii) * si.ostride;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
+        for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
+      }
+    } else {
+      // cross-layer mix: this layer's unnormalised output and denominator in true units (the
+      // head's weight scale 2^s_g undone), summed over the layers, divided by the last one
+      const float wun = ldexpf(1.f, -s_sexp[w * HP + j]);
+      const int mode = args.accumulate;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ii = 4 * a + i;
+        if (ii >= rows) continue;
+        const size_t tok = (size_t)(bi.tok0 + row0 + ii);
+        MF_GLOBAL float* orow = si.o + tok * si.ostride;
+        MF_GLOBAL float* dp = si.dn + tok * (si.ostride / D);
+        float den = s_den[w * HP + j][ii] * wun;
+        if (mode >= 2) den += *dp;
+        const float num = unscale * wun;
+        const float inv = mode == 3 ? 1.f / den : 1.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          float v = acc[j][dt][i] * num;
+          if (mode >= 2) v += orow[16 * dt + c];
+          orow[16 * dt + c] = v * inv;
+        }
+        if (mode != 3 && c == 0) *dp = den;
+      }
     }
   }
 }

@@ -429,6 +429,24 @@ def retrieve_multi(store: BlockStore, receivers, outs=None, stream=None) -> list
     return tensors
 
 
+def retrieve_layers(stores, Ws, pv: PreparedV, kv_head_map, out=None, stream=None) -> torch.Tensor:
+    """mf_retrieve_layers: one receiver layer from several sender layers' stores; Ws[l] is fp32
+    [H_r, stores[l].H_s]."""
+    stores, Ws = list(stores), list(Ws)
+    if len(stores) != len(Ws) or not stores:
+        raise ValueError("one W per store")
+    H_r = int(Ws[0].shape[0])
+    for st, W in zip(stores, Ws):
+        if W.dtype != torch.float32 or W.dim() != 2 or W.shape != (H_r, st.raw.H_s):
+            raise ValueError("each W must be float32 [H_r, H_s of its store]")
+    out = _out(out, stores[0].raw.T, H_r, pv.raw.d, Ws[0])
+    arr = (MfBsr * len(stores))(*[st.raw for st in stores])
+    w_arr = (ctypes.c_void_p * len(Ws))(*[_dev(W, "W") for W in Ws])
+    check(_L.mf_retrieve_layers(stores[0].ctx.handle, len(stores), arr, w_arr, H_r, ctypes.byref(pv.raw),
+                                i32_array(kv_head_map), _dev(out, "out"), _stream(stream)))
+    return out
+
+
 def retrieve(store: BlockStore, W: torch.Tensor, V: torch.Tensor, kv_head_map, page_table=None,
              page_size: int = 16, out=None, stream=None) -> torch.Tensor:
     """mf_retrieve: V preparation into context scratch + the fused retrieve kernel."""

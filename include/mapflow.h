@@ -317,6 +317,21 @@ mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_recv, cons
                             const int32_t* const* kv_head_map_host, float* const* O,
                             void* stream);
 
+/*
+ * One receiver layer from the stores of several sender layers (a variant the wording allows:
+ * [MapFlow 方案, 二] names a linear mapping across layers as well as heads).  For receiver head
+ * g and token i, with P_l zero outside layer l's kept blocks:
+ *     Ahat[g,i,j] = sum_l sum_h W_l[g,h] P_l[h,i,j],   O[i,g,:] = sum_j Ahat V / sum_j Ahat,
+ * i.e. mf_retrieve_prepared over the union of the layers' blocks.  stores: n_layers stores with
+ * the same B, cu_seqlens and row range (H_s may differ); W[l]: fp32 [H_r][stores[l].H_s] device;
+ * vf, kv_head_map_host, O as for mf_retrieve_prepared.  One launch per layer; O holds the running
+ * unnormalised sum in between and the context keeps the running denominators [T][H_r].
+ * n_layers = 1 is mf_retrieve_prepared.
+ */
+mf_status mf_retrieve_layers(mf_ctx* ctx, int32_t n_layers, const mf_bsr* stores, const float* const* W,
+                             int32_t H_r, const mf_vfrag* vf, const int32_t* kv_head_map_host, float* O,
+                             void* stream);
+
 /* mf_v_prepare into context scratch followed by mf_retrieve_prepared. */
 mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r, const void* V,
                       mf_dtype vdtype, int32_t H_kv, int32_t d, const int32_t* page_table,

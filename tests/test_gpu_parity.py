@@ -467,3 +467,33 @@ def test_compress_variants(mf, case):
     O = mf.retrieve(store, W, V, x["kv_head_map"])
     torch.cuda.synchronize()
     assert_out_close(O.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], x["kv_head_map"]), "O_r (variant)")
+
+
+@pytest.mark.parametrize("case", [
+    dict(wl="pair_8b3b_8k", seed=17, lengths=[230, 40], heads=[8, 16], H_r=12, H_kv=4, d=128),
+    dict(wl="tiny", seed=18, lengths=[120, 1, 60], heads=[4, 4, 2], H_r=5, H_kv=5, d=64),
+])
+def test_retrieve_layers(mf, case):
+    """One receiver layer from several sender layers' stores against the oracle's cross-layer
+    retrieve (mix over the union of the layers' blocks, then renormalise)."""
+    wl = synth.WORKLOADS[case["wl"]]
+    tau = _f32(wl.tau if case["wl"] != "tiny" else 0.6)
+    say(f"case: retrieve_layers {case}")
+    refs, stores, Ws, Wn = [], [], [], []
+    for l, H_s in enumerate(case["heads"]):
+        x = synth.make_layer_inputs(wl, case["seed"], layer=l, lengths=case["lengths"], H_s=H_s, H_r=case["H_r"],
+                                    H_kv=case["H_kv"], d=case["d"])
+        ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B)
+        refs.append(ref)
+        stores.append(_upload_oracle_store(mf, ref, x))
+        Wn.append(x["w"])
+        Ws.append(to_dev(x["w"]))
+    v, kv = x["v_r"], x["kv_head_map"]
+    pv = mf.v_prepare(to_dev(v, wl.dtype), wl.B, cu_seqlens=x["cu_seqlens"])
+    O = mf.retrieve_layers(stores, Ws, pv, kv)
+    torch.cuda.synchronize()
+    assert_out_close(O.cpu().numpy(), oracle.retrieve_layers(refs, Wn, v, kv), "O_r (cross-layer)")
+    # one layer is the plain retrieve
+    O1 = mf.retrieve_layers(stores[:1], Ws[:1], pv, kv)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, mf.retrieve_prepared(stores[0], Ws[0], pv, kv))
