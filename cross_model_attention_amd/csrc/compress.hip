@@ -316,12 +316,12 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 //     k_ktile, already in MFMA fragment layout: each load instruction reads 1 KiB of contiguous
 //     memory (loading the fragments from the plain key rows would touch 16 rows per instruction
 //     and make the vector L1 the bottleneck);
-//   * scores are formed on MFMA and turned into bf16 probabilities exp(s - lse); a lane's values
-//     for two adjacent rows are converted as one packed pair, and each stored value is added to
-//     its row's sum with a bf16 dot2 against a unit vector (no unpacking);
-//   * the pair is written into an LDS tile laid out like the stored 16-byte records of 8 heads
-//     per (row, column), head slots rotated by 2*((row / 4) mod 4) so that one wave's 2-byte
-//     writes hit distinct banks;
+//   * scores are formed transposed on MFMA (lane (a, c): keys 16 nt + 4 a + i of row c) and
+//     turned into bf16 probabilities exp(s - lse); the stored values of two slices, packed, are
+//     summed per row on MFMA against an all-ones operand (the row sums of the stored values);
+//   * the values are written into an LDS tile laid out like the stored 16-byte records of 8
+//     heads per (row, column), with key positions and head slots permuted by the row so that one
+//     wave's 2-byte writes hit distinct banks;
 // once all 8 waves have written their head, the tile is streamed to HBM with the rotation undone,
 // with non-temporal stores spread over the next block's slices, each part issued right after
 // that slice's key loads (LDS double buffered where it fits: one barrier per block).
@@ -375,9 +375,20 @@ __device__ __forceinline__ void ktile_load(Frag<float, D>& f, const unsigned cha
   for (int k = 0; k < Frag<float, D>::N; ++k) f.v[k] = *reinterpret_cast<const float*>(slice + (k * 64 + lane) * 4);
 }
 
-// Stream part q of NQ of a finished 8-head record tile (B x B records of 16 bytes) to HBM with the
-// head-slot rotation undone.  Each thread handles contiguous 16-byte pieces; the rotation of a
-// piece depends only on its row, which is uniform over a wave.
+// LDS record tile of one kept block: for every (row r, key k) a 16-byte record of the 8 heads of
+// the group, bf16.  Wave w (head 8 hg + w) forms its scores transposed, so lane (a, c) holds keys
+// 16 nt + 4 a + i of row 16 mt + c; its 2-byte writes would all hit the same four banks (the 16
+// rows are 1 KiB apart), so two functions of c = r mod 16 spread them:
+//   * the record of key k sits at position k ^ kv(c) of its row (kv flips the key's low 2 bits),
+//   * the head slots of the record are rotated by kg(c) dwords (head w at halfword (w + 2 kg) mod 8);
+// (kv, kg) takes all 16 values as c does, so one wave's writes of one i hit 64 distinct banks.
+// On the way out a wave reads one row (B = 64) or two rows whose kg agrees (B = 32), so the
+// rotation is uniform there and the reads are 16-byte, conflict-free.
+__device__ __forceinline__ int rec_xor(int c) { return (c & 1) | ((c >> 3) << 1); }
+__device__ __forceinline__ int rec_rot(int c) { return (c >> 1) & 3; }
+
+// Stream part q of NQ of a finished record tile (B x B records of 16 bytes) to HBM in (row, key)
+// order with the head-slot rotation undone.  Each thread handles contiguous 16-byte pieces.
 template <int B>
 __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned char* dst, int q, int NQ,
                                             int w, int lane) {
@@ -387,8 +398,9 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
   for (int u0 = 0; u0 < PIECES; ++u0) {
     if (u0 / per != q) continue;
     const int piece = 64 * w + lane + u0 * 512;
-    const int rot = (((64 * w + u0 * 512) / B) >> 2) & 3;   // uniform: a wave covers 1 or 2 rows of one group of 4
-    const v4u x = *reinterpret_cast<const v4u*>(tile + piece * 16);
+    const int r = piece / B, k = piece % B;
+    const int rot = rec_rot((64 * w + u0 * 512) / B % 16);   // uniform over the wave
+    const v4u x = *reinterpret_cast<const v4u*>(tile + (r * B + (k ^ rec_xor(r % 16))) * 16);
     v4u y;
     if (rot == 0) y = x;
     else if (rot == 1) y = v4u{x[1], x[2], x[3], x[0]};
@@ -398,22 +410,26 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
   }
 }
 
+// One kept block for one wave: scores of the block transposed (keys x rows) on MFMA, bf16
+// probabilities 2^(s c - lse2) written into the record tile, and the row sums of the stored
+// values accumulated on MFMA: the packed probabilities of two key slices form the B operand
+// (8 keys of row c per lane) against an all-ones A operand, so each product adds 32 keys of 16
+// rows.  rsum[mt] ends with the row total of row 16 mt + c in every element.
 template <typename T, int B, int D>
-__device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16][4],
+__device__ __forceinline__ void gather_block(bool MASKED, const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16],
                                              Frag<T, D> (&kb)[B / 16], const unsigned char* ktj,
                                              const unsigned char* ktn, bool has_next, int J, int rows,
-                                             int qdiag, float scale2, unsigned char* tile, int w, int lane,
-                                             int a, int c, float (&rs)[B / 16][4], const unsigned char* prev,
-                                             unsigned char* prev_dst) {
+                                             int qdiag, float scale2, unsigned char* tile, const int (&woff)[4],
+                                             int w, int lane, int a, int c, v4f (&rsum)[B / 16],
+                                             const unsigned char* prev, unsigned char* prev_dst) {
   constexpr int MT = B / 16;   // 16-row tiles
   constexpr int NT = B / 16;   // 16-key slices; slice nt lives in kb[nt]
   constexpr int SB = KTile<T, D>::kSliceBytes;
-  // unit vectors (1, 0) and (0, 1) in bf16, kept in registers: as inline constants the compiler
-  // would encode 1.0, which the dot2 reads as the pair (0, 1)
-  uint32_t u0 = 0x00003F80u, u1 = 0x3F800000u;
-  asm volatile("" : "+v"(u0), "+v"(u1));
-  const b2 e0 = __builtin_bit_cast(b2, u0), e1 = __builtin_bit_cast(b2, u1);
-  const int slot = ((w + 2 * a) & 7) * 2;
+  static_assert(NT % 2 == 0, "row sums pair the key slices");
+  uint32_t one2 = 0x3F803F80u;                     // (1, 1) in bf16
+  asm volatile("" : "+v"(one2));
+  const v8s ones = as_v8s(v4u{one2, one2, one2, one2});
+  uint32_t pend[MT][2];                            // packed probabilities of the even slice
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     // the slice NT-1 ahead (the last of this block, or one of the next block's) into the
@@ -425,31 +441,31 @@ __device__ __forceinline__ void gather_block(bool masked, const Frag<T, D> (&qf)
     if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT, w, lane);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v4f sc = dot_tile<D>(qf[mt], kb[nt], zero4());
-      if (masked) {
+      v4f sc = dot_tile<D>(kb[nt], qf[mt], zero4());   // keys 16 nt + 4 a + i, row 16 mt + c
+      if (MASKED) {
         // diagonal / partial blocks only: invisible keys and padding rows get -inf scores
-        int kq = J * B + 16 * nt + c - qdiag - 4 * a;  // key - (first row of the lane's rows)
-        int rl = rows - 4 * a;
-        asm volatile("" : "+v"(kq), "+v"(rl));
+        int kq = J * B + 16 * nt + 4 * a - qdiag - 16 * mt - c;   // key (i = 0) minus query
+        int rv = rows - 16 * mt - c;                               // > 0: the row exists
+        asm volatile("" : "+v"(kq), "+v"(rv));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (!(16 * mt + i < rl && kq <= 16 * mt + i)) sc[i] = -__builtin_inff();
+          if (!(rv > 0 && kq + i <= 0)) sc[i] = -__builtin_inff();
       }
       float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale2, -l2[mt][i]));
-      // rows 4a+i and 4a+i+1 of key 16nt+c: one packed conversion, each row's stored value
-      // added to its sum with a bf16 dot2 against a unit vector
-#pragma unroll
-      for (int i = 0; i < 4; i += 2) {
-        const f2 v2 = {p[i], p[i + 1]};
-        const b2 pk = __builtin_convertvector(v2, b2);
-        rs[mt][i] = __builtin_amdgcn_fdot2_f32_bf16(pk, e0, rs[mt][i], false);
-        rs[mt][i + 1] = __builtin_amdgcn_fdot2_f32_bf16(pk, e1, rs[mt][i + 1], false);
-        const int r = 16 * mt + 4 * a + i;
-        unsigned char* rec = tile + (r * B + 16 * nt + c) * 16 + slot;
-        *reinterpret_cast<__bf16*>(rec) = pk[0];
-        *reinterpret_cast<__bf16*>(rec + B * 16) = pk[1];
+      for (int i = 0; i < 4; ++i) p[i] = fast_exp2(fmaf(sc[i], scale2, -l2[mt]));
+      const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{p[0], p[1]}), b2));
+      const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{p[2], p[3]}), b2));
+      unsigned char* rec = tile + (16 * mt * B + 16 * nt) * 16;
+      *reinterpret_cast<uint16_t*>(rec + woff[0]) = (uint16_t)lo;
+      *reinterpret_cast<uint16_t*>(rec + woff[1]) = (uint16_t)(lo >> 16);
+      *reinterpret_cast<uint16_t*>(rec + woff[2]) = (uint16_t)hi;
+      *reinterpret_cast<uint16_t*>(rec + woff[3]) = (uint16_t)(hi >> 16);
+      if (nt & 1)
+        rsum[mt] = mfma_bf16(ones, as_v8s(v4u{pend[mt][0], pend[mt][1], lo, hi}), rsum[mt]);
+      else {
+        pend[mt][0] = lo;
+        pend[mt][1] = hi;
       }
     }
   }
@@ -521,18 +537,21 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
   if (t0 >= t1) return;
 
   const int hq = active ? h : 0;
+  // lane (a, c) handles row 16 mt + c of every 16-row tile
   Frag<T, D> qf[MT];
-  float l2[MT][4];
+  float l2[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = 16 * mt + c;
     qf[mt].load(Q + (size_t)hq * T_tot * D + (size_t)(bi.tok0 + r) * D, active && r < rows, a);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rr = 16 * mt + 4 * a + i;
-      l2[mt][i] = (active && rr < rows) ? lse2[(size_t)hq * T_tot + bi.tok0 + rr] : 0.f;
-    }
+    l2[mt] = (active && r < rows) ? lse2[(size_t)hq * T_tot + bi.tok0 + r] : 0.f;
   }
+  // byte offsets in the record tile of this lane's keys 4 a + i of row c (tile (0, 0)), head slot
+  // of head w rotated by rec_rot(c)
+  int woff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    woff[i] = (c * B + 4 * a + (i ^ rec_xor(c))) * 16 + ((w + 2 * rec_rot(c)) & 7) * 2;
   // this head's key operand tiles; key block J of the sequence is block row kbrow0 + J
   const int kbrow0 = brow - bi.I;
   const unsigned char* kth = ktile + (size_t)hq * n_brow * NT * SB;
@@ -551,28 +570,23 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     const bool has_next = t + 1 < t1;
     const int Jn = has_next ? block_idx[t + 1] : J;
     unsigned char* tile = s_out[(t - t0) % NBUF];
-    float rs[MT][4];
+    v4f rsum[MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rs[mt][i] = 0.f;
+    for (int mt = 0; mt < MT; ++mt) rsum[mt] = zero4();
     // with two tile buffers the previous block's tile is streamed during this block
     const bool overlap = NBUF == 2 && t > t0;
     const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
     // a head that did not select this block (per-head selection) stores zeros
     const bool keep = active && (hflags == nullptr || hflags[((size_t)h * n_brow + brow) * nb_max + J]);
-    gather_block<T, B, D>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next,
-                          J, keep ? rows : 0, qdiag, scale2, tile, w, lane, a, c, rs, prev, prev_dst);
+    gather_block<T, B, D>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next, J,
+                          keep ? rows : 0, qdiag, scale2, tile, woff, w, lane, a, c, rsum, prev, prev_dst);
     {
-      // per-row sums over the block's 64 keys: lane c of group a ends with row 16 (c/4) + 4a + c%4
-      float flat[MT * 4];
+      // row sums of the stored values: lane (a, c) writes row 16 a + c
+      float v = rsum[0][0];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) flat[4 * mt + i] = rs[mt][i];
-      const float v = row16_reduce_scatter<MT * 4>(flat, c);
-      if (active && c < MT * 4) part[((size_t)t * H_s + h) * B + 16 * (c >> 2) + 4 * a + (c & 3)] = v;
+      for (int mt = 1; mt < MT; ++mt) v = a == mt ? rsum[mt][0] : v;
+      if (active && a < MT) part[((size_t)t * H_s + h) * B + 16 * a + c] = v;
     }
     __syncthreads();
     if (NBUF == 1) {                               // single buffer: stream now, then reuse

@@ -58,6 +58,24 @@ __device__ __forceinline__ void load_lds_frag(Frag<uint16_t, D>& f, const unsign
   for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
     f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(row + (32 * k + 8 * a) * 2));
 }
+// bf16 key tiles staged by LDS DMA: rows of D bf16 values without padding, 16-byte chunk j of row
+// r stored at chunk position j ^ kswz(r); kswz takes 16 distinct values over any 16 consecutive
+// rows' bank offsets, so the 16 lanes reading one chunk index of 16 rows hit distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  constexpr int RPB = 256 / (D * 2);                      // rows per 256 bytes (all 64 banks)
+  constexpr int NCH = D * 2 / 16;                         // chunks per row
+  return (r / RPB) % NCH;
+}
+template <int D>
+__device__ __forceinline__ void load_lds_frag_swz(Frag<uint16_t, D>& f, const unsigned char* tile, int r, int a) {
+  const unsigned char* row = tile + r * D * 2;
+  const int x = kswz<D>(r);
+#pragma unroll
+  for (int k = 0; k < Frag<uint16_t, D>::N; ++k)
+    f.v[k] = as_v8s(*reinterpret_cast<const v4u*>(row + ((4 * k + a) ^ x) * 16));
+}
+
 template <int D>
 __device__ __forceinline__ void load_lds_frag(Frag<float, D>& f, const unsigned char* row, int a) {
 #pragma unroll
@@ -147,9 +165,13 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   constexpr int MT = B / 16;                               // 16-key tiles per block
   constexpr int QT = 2;                                    // 16-query tiles per wave
   constexpr int NTHR = B * 4;
-  constexpr int ROWB = D * (int)sizeof(T) + 32;            // row stride = 32 mod 128: no conflicts
+  // bf16 keys: staged by LDS DMA in the swizzled layout (no registers on the way); fp32 keys:
+  // through registers into rows padded to 32 mod 128 bytes
+  constexpr bool DMA = sizeof(T) == 2;
+  constexpr int ROWB = DMA ? D * 2 : D * (int)sizeof(T) + 32;
   constexpr int CPR = D * (int)sizeof(T) / 16;
-  constexpr int CPT = B * CPR / NTHR;
+  constexpr int CPT = DMA ? 1 : B * CPR / NTHR;
+  constexpr int NDMA = B * D * 2 / 1024 / (NTHR / 64);     // 1 KiB DMA loads per wave and tile
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
   __shared__ float s_lse[2][B];
 
@@ -174,7 +196,27 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   }
 
   // key tiles: registers -> LDS, fetched two blocks ahead (LDS double buffered)
+  // DMA load of key block J into LDS buffer buf: each wave fills NDMA consecutive KiB; lane l of
+  // a load writes bytes 16 l .. 16 l + 15 of its KiB, i.e. chunk position p of row r, and so
+  // fetches chunk p ^ kswz(r) of key J B + r (clamped into the sequence: keys past its end are
+  // masked wherever they are read)
+  auto dma_k = [&](int J, int buf) {
+    if constexpr (DMA) {
+#pragma unroll
+      for (int u = 0; u < NDMA; ++u) {
+        const int kib = w * NDMA + u;
+        const int byte = kib * 1024 + lane * 16;
+        const int r = byte / (D * 2), p = (byte % (D * 2)) / 16;
+        const int key = min(J * B + r, b0.n - 1);
+        const MF_GLOBAL unsigned char* src = (const MF_GLOBAL unsigned char*)Kh +
+                                             (size_t)key * hd.k_stride * 2 + (p ^ kswz<D>(r)) * 16;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&s_k[buf][kib * 1024], 16, 0, 0);
+      }
+    }
+  };
+  auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0): the DMA has landed
   auto fetch_k = [&](v4u (&kst)[CPT], int J) {
+    if constexpr (DMA) return;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int piece = threadIdx.x + u * NTHR;
@@ -184,6 +226,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
     }
   };
   auto stage_k = [&](const v4u (&kst)[CPT], int buf) {
+    if constexpr (DMA) return;
 #pragma unroll
     for (int u = 0; u < CPT; ++u) {
       const int piece = threadIdx.x + u * NTHR;
@@ -212,14 +255,18 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   const int kbrow0 = pairs[2 * pr] - b0.I;                // block row holding key block 0
   v4u kst[CPT];
   auto block = [&](int J) {
-    if (J + 1 <= Jend) fetch_k(kst, J + 1);
+    if (J + 1 <= Jend) {
+      fetch_k(kst, J + 1);
+      dma_k(J + 1, (J + 1) & 1);                            // that buffer was last read in block J - 1
+    }
     if (mine && J <= bi.I) {
       const unsigned char* kt = s_k[J & 1];
       v4f s[QT][MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         Frag<T, D> kf;
-        load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
+        if constexpr (DMA) load_lds_frag_swz<D>(kf, kt, 16 * mt + c, a);
+        else load_lds_frag<D>(kf, kt + (16 * mt + c) * ROWB, a);
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[qt][mt] = dot_tile<D>(kf, qf[qt], zero4());
       }
@@ -230,11 +277,35 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
       for (int qt = 0; qt < QT; ++qt) {
         const int qr = q0 + 16 * qt + c;
         const int qloc = bi.I * B + qr;
-        const float2 zr = masked ? block_stats<MT, true, ATTN>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
-                                 : block_stats<MT, false, ATTN>(s[qt], 0, true, scale2);
+        float2 zr;
+        bool done = false;
+        if constexpr (!ATTN) {
+          // past the first block, an unmasked block is summed against the running maximum
+          // instead of its own: z = sum_j 2^(s_j c - m_run), stored with reference m_run, and the
+          // running sum just adds it.  Should the block's scores rise far above m_run (z reaching
+          // 2^64 in some row), the whole wave redoes it with the block maximum below.  A finite
+          // m_run is guaranteed here: block 0 of a row always holds a visible key.
+          if (!masked && J > 0) {
+            float z = 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) z += fast_exp2(fmaf(s[qt][mt][i], scale2, -m_run[qt]));
+            z = xrow_sum(z);
+            done = __builtin_amdgcn_ballot_w64(!(z < 0x1p64f)) == 0;
+            if (done) {
+              zr = make_float2(z, m_run[qt]);
+              l_run[qt] += (double)z;
+            }
+          }
+        }
+        if (!done) {
+          zr = masked ? block_stats<MT, true, ATTN>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
+                      : block_stats<MT, false, ATTN>(s[qt], 0, true, scale2);
+        }
         if (STATS && a == 0) zrow[(size_t)J * B + qr] = zr;
         const float mprev = m_run[qt];
-        if (zr.x > 0.f) {
+        if (!done && zr.x > 0.f) {
           const float mn = __builtin_fmaxf(m_run[qt], zr.y);
           l_run[qt] = l_run[qt] * (double)fast_exp2(m_run[qt] - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
           m_run[qt] = mn;
@@ -274,10 +345,13 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
       }
     }
     if (J + 1 <= Jend) stage_k(kst, (J + 1) & 1);
+    if (DMA) dma_wait();
     __syncthreads();
   };
   fetch_k(kst, 0);
   stage_k(kst, 0);
+  dma_k(0, 0);
+  if (DMA) dma_wait();
   __syncthreads();
   for (int J = 0; J <= Jend; ++J) block(J);
   // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
