@@ -289,7 +289,9 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   if ((st = ensure(ctx->M, nbn * 8 + 256, "head-summed mass")) != MF_OK) return st;
   if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
   if ((st = ensure(ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts")) != MF_OK) return st;
-  if ((st = ensure(ctx->part, (size_t)capacity * bsr->H_s * bsr->B * 4 + 256, "row sums")) != MF_OK) return st;
+  if ((st = ensure(ctx->part, (size_t)bsr->n_brow * ((bsr->nb_max + 15) / 16) * bsr->H_s * bsr->B * 8 + 256,
+                   "row sums")) != MF_OK)
+    return st;
   const size_t elem = dtype == MF_BF16 ? 2 : 4;
   if ((st = ensure(ctx->ktile, (size_t)bsr->H_s * bsr->n_brow * bsr->B * d * elem + 256, "key operand tiles")) != MF_OK)
     return st;
@@ -319,7 +321,7 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.M = static_cast<double*>(ctx->M.p);
   a.flags = static_cast<uint8_t*>(ctx->flags.p);
   a.counts = static_cast<int32_t*>(ctx->counts.p);
-  a.part = static_cast<float*>(ctx->part.p);
+  a.part = static_cast<double*>(ctx->part.p);
   a.ktile = ctx->ktile.p;
   a.block_ptr = bsr->block_ptr;
   a.block_idx = bsr->block_idx;

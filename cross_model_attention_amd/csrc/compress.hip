@@ -14,8 +14,8 @@
 //                  column) until the kept mass reaches tau * H_s * rows
 //   k_scan         counts -> block_ptr, kept-block total
 //   k_emit         ascending kept columns per block row
-//   k_gather       recompute kept tiles for 8 sender heads, store bf16 probs and per-block row sums
-//   k_rowmass      kept row mass = sum over a row's kept blocks, in column order
+//   k_gather       recompute kept tiles for 8 sender heads, store bf16 probs and per-chunk row sums
+//   k_rowmass      kept row mass = sum of the gather's per-chunk row sums, in column order
 // Scores s = q.k / sqrt(d) are formed by MFMA (bf16 inputs: 16x16x32 bf16; fp32 inputs:
 // 16x16x4 f32) with fp32 accumulation; exponentials use base 2 with log2(e) folded into the
 // scale.
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
                                                 int64_t capacity, const float* __restrict__ lse2,
                                                 float scale2, const unsigned char* __restrict__ ktile,
                                                 const uint8_t* __restrict__ hflags, int nb_max,
-                                                uint16_t* __restrict__ probs, float* __restrict__ part) {
+                                                uint16_t* __restrict__ probs, double* __restrict__ part) {
   constexpr int MT = B / 16;
   constexpr int NT = B / 16;
   using L = GatherLds<T, B, D>;
@@ -565,6 +565,7 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
 #pragma unroll
     for (int nt = 0; nt + 1 < NT; ++nt) ktile_load<D>(kb[nt], k0 + nt * SB, lane);
   }
+  double rsum_chunk = 0.0;
   for (int t = t0; t < t1; ++t) {
     const int J = block_idx[t];
     const bool has_next = t + 1 < t1;
@@ -582,11 +583,12 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     gather_block<T, B, D>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next, J,
                           keep ? rows : 0, qdiag, scale2, tile, woff, w, lane, a, c, rsum, prev, prev_dst);
     {
-      // row sums of the stored values: lane (a, c) writes row 16 a + c
+      // row sums of the stored values, summed over the chunk in column order: lane (a, c) holds
+      // row 16 a + c
       float v = rsum[0][0];
 #pragma unroll
       for (int mt = 1; mt < MT; ++mt) v = a == mt ? rsum[mt][0] : v;
-      if (active && a < MT) part[((size_t)t * H_s + h) * B + 16 * a + c] = v;
+      rsum_chunk += (double)v;
     }
     __syncthreads();
     if (NBUF == 1) {                               // single buffer: stream now, then reuse
@@ -599,20 +601,27 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     stream_tile<B>(s_out[(t1 - 1 - t0) % NBUF],
                    reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1, w,
                    lane);
+  // the chunk's row sums, one slot per (block row, chunk)
+  const int n_chunk = (nb_max + kGatherChunk - 1) / kGatherChunk;
+  if (active && a < MT) part[(((size_t)brow * n_chunk + chunk) * H_s + h) * B + 16 * a + c] = rsum_chunk;
 }
 
 // ------------------------------------------------------------------------------------------
-__global__ void k_rowmass(const float* __restrict__ part, const int32_t* __restrict__ block_ptr,
+// kept row mass: the row's chunk sums (each over up to 16 kept blocks, in column order) added in
+// chunk order, fp64 throughout
+__global__ void k_rowmass(const double* __restrict__ part, const int32_t* __restrict__ block_ptr,
                           const int32_t* __restrict__ info, const int32_t* __restrict__ counters,
-                          int H_s, int B, int64_t T_tot, int64_t capacity, float* __restrict__ rkm) {
+                          int H_s, int B, int nb_max, int64_t T_tot, int64_t capacity, float* __restrict__ rkm) {
   const int brow = blockIdx.x, h = blockIdx.y, r = threadIdx.x;
   const BrowInfo bi = load_info(info, brow);
   const int rows = min(B, bi.n - bi.I * B);
   if (r >= rows) return;
   const int64_t nnzb = min((int64_t)counters[0], capacity);
   const int64_t lo = min((int64_t)block_ptr[brow], nnzb), hi = min((int64_t)block_ptr[brow + 1], nnzb);
+  const int n_chunk = (nb_max + kGatherChunk - 1) / kGatherChunk;
+  const int nk = (int)((hi - lo + kGatherChunk - 1) / kGatherChunk);   // chunks the gather wrote
   double s = 0.0;
-  for (int64_t t = lo; t < hi; ++t) s += (double)part[((size_t)t * H_s + h) * B + r];
+  for (int k = 0; k < nk; ++k) s += part[(((size_t)brow * n_chunk + k) * H_s + h) * B + r];
   rkm[(size_t)h * T_tot + bi.tok0 + r] = (float)s;
 }
 
@@ -722,7 +731,7 @@ hipError_t compress_fill(const CompressArgs& a, hipStream_t s) {
   }
   if ((e = gather_dispatch(a, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_rowmass, dim3(a.n_brow, a.H_s), dim3(a.B), 0, s, a.part, a.block_ptr,
-                     a.info, a.counters, a.H_s, a.B, a.T, a.capacity, a.rkm);
+                     a.info, a.counters, a.H_s, a.B, a.nb_max, a.T, a.capacity, a.rkm);
   return hipGetLastError();
 }
 

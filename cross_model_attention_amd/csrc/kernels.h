@@ -34,7 +34,7 @@ struct CompressArgs {
   double* M;             // [n_brow][nb_max] head-summed block masses
   uint8_t* flags;        // [n_brow][nb_max] kept flags
   int32_t* counts;       // [n_brow]
-  float* part;           // [capacity][H_s][B] per-block row sums of stored probs
+  double* part;          // [n_brow][ceil(nb_max / 16)][H_s][B] row sums of stored probs per gather chunk
   void* ktile;           // [H_s][n_brow][B/16][fragment elements][64 lanes] key operands
   // fused prefill (attn_out != NULL): the statistics pass also writes the sender's own causal
   // attention output [T][H_s][d] fp32, from V prepared per sender head (fp16 tiles, exponents)
