@@ -105,6 +105,34 @@ def test_compress_bf16_shapes(mf, lengths, H_s, d, B, tau, seed):
         assert host["nnzb"] == n_causal
 
 
+def test_compress_scores_far_above_the_running_maximum(mf):
+    """Block statistics past a row's first block are summed against the row's running maximum;
+    when a later block's scores sit far above it (z would reach 2^64) the wave redoes the block
+    with the block maximum.  Keys of block 1 are copies of queries of block rows 2 and 3 scaled by
+    4 (exact in bf16), so those rows' scores in block 1 exceed everything before them by ~2^65."""
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 5, lengths=[256], H_s=8, H_r=8, H_kv=2, d=128)
+    q, k = x["q_s"].copy(), x["k_s"].copy()
+    k[:, 64:128] = 4.0 * q[:, 128:192]
+    x["k_s"] = k
+    tau = _f32(0.95)
+    store, host = _compress_case(mf, x, tau, 64, "bf16")
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, 64)
+    _check_compress(x, host, ref, tau, 64)
+
+
+@pytest.mark.parametrize("lengths,H_s,d,B,seed", [
+    ([300], 8, 64, 64, 6),                   # d = 64 with 64-token blocks
+])
+def test_compress_bf16_d64_b64(mf, lengths, H_s, d, B, seed):
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, seed, lengths=lengths, H_s=H_s, H_r=8, H_kv=2, d=d)
+    tau = _f32(0.9)
+    store, host = _compress_case(mf, x, tau, B, "bf16")
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    _check_compress(x, host, ref, tau, B)
+
+
 def _upload_oracle_store(mf, ref, x):
     store = mf.BlockStore.create(ref.H_s, ref.B, x["cu_seqlens"], capacity=len(ref.block_idx))
     store.upload(ref.block_ptr, ref.block_idx, ref.probs, ref.row_kept_mass)
