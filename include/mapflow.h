@@ -214,8 +214,10 @@ mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, mf_dtype d
  * [MapFlow开源, section 只存重要的:块稀疏压缩]: the map is compressed without first assembling the
  * dense matrix; here the score tiles that the sender's causal attention forms anyway also give
  * the block statistics, so no separate statistics pass runs.
- * Fills *bsr exactly as mf_compress_into(ctx, Q, K, dtype, d, tau, bsr, stream) does, bit for bit
- * (the statistics come from the same code), and also writes
+ * Fills *bsr as mf_compress_into(ctx, Q, K, dtype, d, tau, bsr, stream) does, up to rounding
+ * (mf_compress_into sums most blocks' statistics against the row's running maximum, this call
+ * against each block's own maximum; block choices can differ only at near-ties of the masses),
+ * and also writes
  *     O[i, h, :] = sum_j softmax_j(q_i . k_j / sqrt(d), j <= i within i's sequence) V[j, h, :]
  *   Q, K   [H_s][T][d] as for mf_compress_into
  *   V      sender values, [T][H_s][d] (one value head per sender head), dtype as Q
