@@ -344,7 +344,8 @@ def _rows_of(host, r):
 
 def test_chunked_prefill_rows_equal_the_full_store(mf):
     """A row-range store compresses exactly the rows of the full store it covers (bit for bit),
-    keeps nothing elsewhere, and its retrieve and fused prefill touch only its rows."""
+    keeps nothing elsewhere, and its retrieve and fused prefill touch only its rows (the fused
+    prefill's range rows equal those of a full fused prefill, bit for bit)."""
     wl = synth.WORKLOADS["pair_8b3b_8k"]
     lengths = [300, 129, 64]
     x = synth.make_layer_inputs(wl, 11, lengths=lengths, H_s=8, H_r=12, H_kv=4, d=128)
@@ -388,11 +389,20 @@ def test_chunked_prefill_rows_equal_the_full_store(mf):
     O_pre = torch.full((int(cu[-1]), 8, 128), float("nan"), device="cuda")
     mf.compress_prefill_into(pre, Q, K, Vs, tau, out=O_pre)
     pre.sync()
-    O_pre_full = mf.compress_prefill_into(mf.BlockStore.create(8, wl.B, x["cu_seqlens"]), Q, K, Vs, tau)
+    pre_full = mf.BlockStore.create(8, wl.B, x["cu_seqlens"])
+    O_pre_full = mf.compress_prefill_into(pre_full, Q, K, Vs, tau)
+    pre_full.sync()
     torch.cuda.synchronize()
-    hq = pre.to_host()
-    for key in ["block_ptr", "block_idx", "probs_bits", "row_kept_mass"]:
-        assert np.array_equal(hq[key], hp[key]), key
+    hq, hqf = pre.to_host(), pre_full.to_host()
+    assert np.array_equal(hq["block_ptr"], hp["block_ptr"])
+    r = 0
+    for s, n in enumerate(lengths):
+        for I in range((n + wl.B - 1) // wl.B):
+            if I >= row_begin[s]:
+                for a_, b_ in zip(_rows_of(hqf, r), _rows_of(hq, r)):
+                    assert np.array_equal(a_, b_), f"prefill row {r}"
+            r += 1
+    assert np.array_equal(hqf["row_kept_mass"][:, active_tok], hq["row_kept_mass"][:, active_tok])
     assert torch.equal(O_pre[act], O_pre_full[act]) and torch.isnan(O_pre[~act]).all()
 
 
