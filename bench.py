@@ -52,6 +52,8 @@ def parse():
                         "the step's launches")
     p.add_argument("--probe-bytes", type=int, default=1 << 30,
                    help="size of the HBM copy probe run after the timed steps (0 = skip)")
+    p.add_argument("--read-probe-bytes", type=int, default=4 << 30,
+                   help="size of the HBM read probe run after the timed steps (0 = skip)")
     return p.parse_args()
 
 
@@ -461,6 +463,26 @@ def main():
         ms = e0.elapsed_time(e1) / reps
         out["hbm_copy_probe"] = {"bytes_moved": 2 * n * 4, "GB_per_s": 2 * n * 4 / (ms * 1e-3) / 1e9}
         del src, dst
+
+    if args.read_probe_bytes > 0:
+        # read ceiling: a buffer streamed through non-temporal loads only
+        n = args.read_probe_bytes // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        mf.read_probe(src, sink)
+        torch.cuda.synchronize()
+        e0, e1 = ev(), ev()
+        e0.record()
+        reps = 10
+        for _ in range(reps):
+            mf.read_probe(src, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        read_gbs = n * 4 / (ms * 1e-3) / 1e9
+        out["hbm_read_probe"] = {"bytes_read": n * 4, "GB_per_s": read_gbs}
+        out["roofline"]["frac_of_read_ceiling"] = achieved / read_gbs if read_gbs > 0 else None
+        del src, sink
 
     if args.extras and n_map >= 1:
         out["prefill"] = prefill(mf, torch, wl, args, send[mapped[-1]], slots[(n_map - 1) % k], tau, ctx, dev)

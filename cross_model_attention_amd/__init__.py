@@ -14,6 +14,7 @@ from .mapflow import (  # noqa: F401
     compress_into,
     compress_prefill_into,
     copy_probe,
+    read_probe,
     dense_attention,
     map_layers,
     probs_canonical_to_store,

@@ -1291,4 +1291,14 @@ MF_EXPORT mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_read_probe(mf_ctx* ctx, const void* src, size_t bytes, void* sink, void* stream) {
+  if (!src || !sink) return fail(MF_ERR_INVALID, "src or sink is NULL");
+  if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))
+    return fail(MF_ERR_INVALID, "read probe needs a 16-byte aligned source, a multiple of 16 bytes and a 4-byte aligned sink");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(mf::read_probe(src, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream)), "read probe launch");
+  return MF_OK;
+}
+
 }  // extern "C"

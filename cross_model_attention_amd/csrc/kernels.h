@@ -134,5 +134,6 @@ hipError_t dense_attention(const DenseArgs& a, hipStream_t s);
 bool dense_supported(int dtype, int d);
 
 hipError_t copy_probe(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 
 }  // namespace mf

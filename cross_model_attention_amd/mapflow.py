@@ -482,3 +482,13 @@ def copy_probe(dst: torch.Tensor, src: torch.Tensor, ctx=None, stream=None) -> N
     ctx = _ctx(ctx)
     nbytes = src.numel() * src.element_size()
     check(_L.mf_copy_probe(ctx.handle, _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))
+
+
+def read_probe(src: torch.Tensor, sink: torch.Tensor, ctx=None, stream=None) -> None:
+    """mf_read_probe: stream src through non-temporal loads (HBM read ceiling); sink is a device
+    tensor of at least 4 bytes that the probe leaves untouched."""
+    ctx = _ctx(ctx)
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink needs 4 bytes")
+    check(_L.mf_read_probe(ctx.handle, _dev(src, "src"), nbytes, _dev(sink, "sink"), _stream(stream)))

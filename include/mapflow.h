@@ -406,6 +406,15 @@ mf_status mf_cache_lookup(mf_cache* cache, int32_t layer, const int32_t* tokens_
  */
 mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_t bytes, void* stream);
 
+/*
+ * HBM read probe: read `bytes` (a multiple of 16, src 16-byte aligned) with non-temporal 16-byte
+ * loads and fold them by XOR; `sink` (4 bytes of device memory, 4-byte aligned) is written only
+ * if a thread's fold equals one fixed 128-bit value (so the loads cannot be optimised away), and
+ * nothing else is written.  Gives the read ceiling that a read-dominated kernel such as the
+ * fused retrieve is compared with.
+ */
+mf_status mf_read_probe(mf_ctx* ctx, const void* src, size_t bytes, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

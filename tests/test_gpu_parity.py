@@ -337,6 +337,14 @@ def test_copy_probe(mf):
     assert torch.equal(src, dst)
 
 
+def test_read_probe_reads_without_writing(mf):
+    src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    mf.read_probe(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(sink.cpu(), torch.full((4,), 7, dtype=torch.int32))
+
+
 def _rows_of(host, r):
     a, b = int(host["block_ptr"][r]), int(host["block_ptr"][r + 1])
     return host["block_idx"][a:b], host["probs_bits"][a:b]
