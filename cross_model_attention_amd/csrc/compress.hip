@@ -439,9 +439,23 @@ __device__ __forceinline__ void gather_block(bool MASKED, const Frag<T, D> (&qf)
     // a part of the previous block's tile goes out after the key loads, so no wait on a key
     // slice ever covers these stores (one counter, completed in issue order)
     if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT, w, lane);
+    // the slice's score tiles, the MT accumulation chains interleaved step by step over the head
+    // dimension so that no product waits on the one just issued
+    v4f scs[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) scs[mt] = zero4();
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int k = 0; k < Frag<T, D>::N; ++k)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) scs[mt] = mfma_bf16(kb[nt].v[k], qf[mt].v[k], scs[mt]);
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) scs[mt] = dot_tile<D>(kb[nt], qf[mt], zero4());
+    }
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      v4f sc = dot_tile<D>(kb[nt], qf[mt], zero4());   // keys 16 nt + 4 a + i, row 16 mt + c
+      v4f sc = scs[mt];   // keys 16 nt + 4 a + i, row 16 mt + c
       if (MASKED) {
         // diagonal / partial blocks only: invisible keys and padding rows get -inf scores
         int kq = J * B + 16 * nt + 4 * a - qdiag - 16 * mt - c;   // key (i = 0) minus query
