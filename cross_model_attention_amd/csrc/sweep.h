@@ -175,7 +175,8 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   __shared__ __attribute__((aligned(16))) unsigned char s_k[2][B * ROWB];
   __shared__ float s_lse[2][B];
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, a = lane >> 4, c = lane & 15;
+  const int lane = threadIdx.x & 63, a = lane >> 4, c = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: LDS bases, row side
   const int side = w / WR;                                 // 0: row I, 1: row I+1
   const int brow = pairs[2 * pr + side];                   // -1: the pair has one row
   const BrowInfo b0 = load_info(info, pairs[2 * pr]);
@@ -200,17 +201,32 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   // a load writes bytes 16 l .. 16 l + 15 of its KiB, i.e. chunk position p of row r, and so
   // fetches chunk p ^ kswz(r) of key J B + r (clamped into the sequence: keys past its end are
   // masked wherever they are read)
+  // Each lane's source offset within a block of keys is the same for every block; only the
+  // block base (uniform) changes, except in a block that runs past the sequence's end.
+  int dma_row[DMA ? NDMA : 1];
+  uint32_t dma_off[DMA ? NDMA : 1];
+  if constexpr (DMA) {
+#pragma unroll
+    for (int u = 0; u < NDMA; ++u) {
+      const int byte = (w * NDMA + u) * 1024 + lane * 16;
+      const int r = byte / (D * 2), p = (byte % (D * 2)) / 16;
+      dma_row[u] = r;
+      dma_off[u] = (uint32_t)(r * hd.k_stride * 2 + (p ^ kswz<D>(r)) * 16);
+    }
+  }
   auto dma_k = [&](int J, int buf) {
     if constexpr (DMA) {
+      const MF_GLOBAL unsigned char* kb = (const MF_GLOBAL unsigned char*)Kh + (size_t)J * B * hd.k_stride * 2;
+      const bool full = J * B + B <= b0.n;
 #pragma unroll
       for (int u = 0; u < NDMA; ++u) {
         const int kib = w * NDMA + u;
-        const int byte = kib * 1024 + lane * 16;
-        const int r = byte / (D * 2), p = (byte % (D * 2)) / 16;
-        const int key = min(J * B + r, b0.n - 1);
-        const MF_GLOBAL unsigned char* src = (const MF_GLOBAL unsigned char*)Kh +
-                                             (size_t)key * hd.k_stride * 2 + (p ^ kswz<D>(r)) * 16;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&s_k[buf][kib * 1024], 16, 0, 0);
+        uint32_t off = dma_off[u];
+        if (!full) {
+          const int r = dma_row[u], over = J * B + r - (b0.n - 1);
+          if (over > 0) off -= (uint32_t)over * (uint32_t)(hd.k_stride * 2);   // clamp onto the sequence's last key
+        }
+        __builtin_amdgcn_global_load_lds(kb + off, (__attribute__((address_space(3))) void*)&s_k[buf][kib * 1024], 16, 0, 0);
       }
     }
   };
