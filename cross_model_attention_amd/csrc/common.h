@@ -8,7 +8,6 @@
 // v_mfma_f32_16x16x4_f32: A lane holds A[c][a], B lane holds B[a][c], same C layout.
 #pragma once
 
-#include <type_traits>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -82,58 +81,6 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// Sum over the 16 lanes of each DPP row (row_ror 8, 4, 2, 1); every lane gets its row's sum.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
-  return v;
-}
-// Sums NV values per lane (NV = 8 or 16) over the 16 lanes of each row of the wave, scattering the
-// results: afterwards lane c of a row holds the row total of value (c mod NV).  Each step pairs
-// lanes that differ in one bit of c (mirror, half mirror, xor 2, xor 1); a lane keeps the half of
-// its values selected by that bit and adds its partner's copy of the same half.  NV - 1 adds per
-// lane instead of 4 NV for a full reduction of every value; the order is fixed.
-template <int NV>
-__device__ __forceinline__ float row16_reduce_scatter(float (&x)[NV], int c) {
-  static_assert(NV == 8 || NV == 16, "8 or 16 values per lane");
-  constexpr int kCtrl[4] = {0x140, 0x141, 0x4E, 0xB1};   // row_mirror, row_half_mirror, xor 2, xor 1
-  auto dpp = [](float v, auto ctrl) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, false));
-  };
-  if constexpr (NV == 8) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] += dpp(x[j], std::integral_constant<int, kCtrl[0]>{});
-  }
-  auto step = [&](auto sc, auto nc) {
-    constexpr int S = decltype(sc)::value, H = decltype(nc)::value / 2;
-    const bool hi = (c >> (3 - S)) & 1;
-#pragma unroll
-    for (int j = 0; j < H; ++j) {
-      const float keep = hi ? x[j + H] : x[j];
-      const float send = hi ? x[j] : x[j + H];
-      x[j] = keep + dpp(send, std::integral_constant<int, kCtrl[S]>{});
-    }
-  };
-  using std::integral_constant;
-  if constexpr (NV == 16) step(integral_constant<int, 0>{}, integral_constant<int, 16>{});
-  step(integral_constant<int, 1>{}, integral_constant<int, 8>{});
-  step(integral_constant<int, 2>{}, integral_constant<int, 4>{});
-  step(integral_constant<int, 3>{}, integral_constant<int, 2>{});
-  return x[0];
-}
-
-// Sum over the wave in a fixed order (rows summed by DPP, then rows 0..3 added); uniform result.
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = row16_sum(v);
-  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (r0 + r1) + (r2 + r3);
 }
 
 // max / sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), result in every
