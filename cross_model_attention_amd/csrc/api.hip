@@ -263,10 +263,15 @@ mf_status alloc_bsr_data(int64_t capacity, int H_s, int B, mf_bsr* out, BsrOwner
   return MF_OK;
 }
 
+// Q, K and V are read with 16-byte loads (and key tiles by 16-byte DMA), so their base pointers
+// must be 16-byte aligned (every row of a contiguous layout then is, since d * size >= 128).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 mf_status validate_compress(const void* Q, const void* K, mf_dtype dtype, int32_t d, float tau,
                             const mf_bsr* bsr) {
   if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL or not created by mf_bsr_create");
   if (!Q || !K) return fail(MF_ERR_INVALID, "Q or K is NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(MF_ERR_INVALID, "Q and K must be 16-byte aligned");
   mf_status st = check_dtype(dtype);
   if (st != MF_OK) return st;
   if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
@@ -355,6 +360,7 @@ mf_status vfrag_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B
                         hipStream_t stream) {
   if (!out) return fail(MF_ERR_INVALID, "output vfrag is NULL");
   if (!V) return fail(MF_ERR_INVALID, "V is NULL");
+  if (!aligned16(V)) return fail(MF_ERR_INVALID, "V must be 16-byte aligned");
   mf_status st = check_dtype(dtype);
   if (st != MF_OK) return st;
   if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
@@ -721,6 +727,7 @@ MF_EXPORT mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const v
   mf_status st = validate_compress(Q, K, dtype, d, tau, bsr);
   if (st != MF_OK) return st;
   if (!V || !O) return fail(MF_ERR_INVALID, "V or O is NULL");
+  if (!aligned16(V)) return fail(MF_ERR_INVALID, "V must be 16-byte aligned");
   if ((st = set_device(ctx)) != MF_OK) return st;
   if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1009,6 +1016,8 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
                                        const int32_t* cu, int32_t n_seq, const int32_t* kvmap,
                                        float* O, void* stream) {
   if (!Q || !K || !V || !O) return fail(MF_ERR_INVALID, "Q, K, V or O is NULL");
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V))
+    return fail(MF_ERR_INVALID, "Q, K and V must be 16-byte aligned");
   mf_status st = check_dtype(dtype);
   if (st != MF_OK) return st;
   if (!mf::dense_supported(dtype_code(dtype), d))

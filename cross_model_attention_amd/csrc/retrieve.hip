@@ -62,12 +62,25 @@ __global__ __launch_bounds__(256) void k_vmax(const T* __restrict__ V, int H_kv,
   const int brow = blockIdx.x, kv = blockIdx.y;
   const BrowInfo bi = load_info(info, brow);
   const int seq = brow_seq[brow];
+  // 16-byte loads: a token's D values of one KV head are contiguous in either layout
+  constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
+  const int CH = D / EPC;                          // chunks per token row
   float m = 0.f;
-  for (int e = threadIdx.x; e < B * D; e += blockDim.x) {
-    const int kloc = bi.I * B + e / D;
-    if (kloc < bi.n)
-      m = fmaxf(m, fabsf(load_v<T>(V, v_offset(bi, seq, kloc, kv, e % D, H_kv, D, page_table,
-                                                   page_size, pages_per_seq))));
+  for (int e = threadIdx.x; e < B * CH; e += blockDim.x) {
+    const int kloc = bi.I * B + e / CH;
+    if (kloc < bi.n) {
+      const v4u x = ld16(V + v_offset(bi, seq, kloc, kv, (e % CH) * EPC, H_kv, D, page_table, page_size,
+                                      pages_per_seq));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(T) == 2) {
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(x[j] & 0xFFFFu))));
+          m = fmaxf(m, fabsf(bf16_to_f32((uint16_t)(x[j] >> 16))));
+        } else {
+          m = fmaxf(m, fabsf(__uint_as_float(x[j])));
+        }
+      }
+    }
   }
   // NaN must win the maximum so that the scale falls back to 1
   if (m != m) m = __uint_as_float(0x7FC00000u);

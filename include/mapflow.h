@@ -197,7 +197,8 @@ mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr);
  * [MapFlow开源, section 只存重要的:块稀疏压缩] and [Reuses Attention, first component]: block
  * statistics first, then the kept blocks; the dense L x L map is never formed.
  *
- *   Q, K   sender queries and keys, [H_s][T][d] (head-major, post-RoPE), dtype MF_BF16 or MF_F32
+ *   Q, K   sender queries and keys, [H_s][T][d] (head-major, post-RoPE), dtype MF_BF16 or MF_F32;
+ *          device pointers, 16-byte aligned (MF_ERR_INVALID otherwise)
  *   d      64 or 128
  *   tau    in (0, 1]: per block row, keep the sink block (column 0) and the diagonal block, then
  *          blocks by descending mass (ties: lower column) until the kept mass reaches
@@ -220,7 +221,7 @@ mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, mf_dtype d
  * and also writes
  *     O[i, h, :] = sum_j softmax_j(q_i . k_j / sqrt(d), j <= i within i's sequence) V[j, h, :]
  *   Q, K   [H_s][T][d] as for mf_compress_into
- *   V      sender values, [T][H_s][d] (one value head per sender head), dtype as Q
+ *   V      sender values, [T][H_s][d] (one value head per sender head), dtype as Q; 16-byte aligned
  *   O      fp32 [T][H_s][d] device; must not alias any input
  * Probabilities enter the P.V product as fp16 scaled by 2^15 and V as fp16 with a power-of-two
  * scale per head (as in mf_dense_attention); sums are fp32.  The prepared V lives in context
@@ -263,7 +264,8 @@ mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
  * Prepare the receiver's V for retrieval (and for mf_dense_attention).
  *   V            contiguous [T][H_kv][d] when page_table is NULL; otherwise a page pool
  *                [n_pages][page_size][H_kv][d] with page_table int32 [n_seq][pages_per_seq]
- *                (device) mapping each sequence's logical pages to pool pages
+ *                (device) mapping each sequence's logical pages to pool pages; V is a device
+ *                pointer, 16-byte aligned (MF_ERR_INVALID otherwise)
  *   dtype        MF_BF16 or MF_F32
  * If out->frag is NULL the library allocates frag and exps (free with mf_vfrag_free); otherwise
  * the caller provides frag with room for H_kv * n_brow * B * d fp16 values.  Calling again with an
@@ -345,6 +347,7 @@ mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_
  * the receiver computes its first layers normally).  O[i,g,:] = softmax_j<=i(q.k / sqrt(d)) V
  * per sequence, query head g reading KV head kv_head_map_host[g].
  *   Q [T][H_q][d], K, V [T][H_kv][d] (MF_BF16 or MF_F32), O fp32 [T][H_q][d]; d in {64, 128}.
+ *   Q, K and V must be 16-byte aligned (MF_ERR_INVALID otherwise).
  */
 mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K, const void* V,
                              mf_dtype dtype, int32_t H_q, int32_t H_kv, int32_t d,

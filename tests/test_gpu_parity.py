@@ -337,6 +337,28 @@ def test_copy_probe(mf):
     assert torch.equal(src, dst)
 
 
+def test_misaligned_inputs_are_rejected(mf):
+    """Q, K and V are read with 16-byte loads: a base pointer off 16-byte alignment is an
+    argument error, raised before any launch."""
+    from cross_model_attention_amd import MapflowError
+    H, T, d = 2, 128, 64
+    flat = torch.zeros(H * T * d + 8, dtype=torch.bfloat16, device="cuda")
+    good = flat[:H * T * d].view(H, T, d)
+    bad = flat[1:1 + H * T * d].view(H, T, d)              # 2 bytes off
+    store = mf.BlockStore.create(H, 32, [0, T])
+    with pytest.raises(MapflowError):
+        mf.compress_into(store, bad, good, 0.9)
+    with pytest.raises(MapflowError):
+        mf.compress_into(store, good, bad, 0.9)
+    V = flat[1:1 + T * H * d].view(T, H, d)
+    with pytest.raises(MapflowError):
+        mf.v_prepare(V, 32, [0, T])
+    with pytest.raises(MapflowError):
+        mf.dense_attention(V, V, V, [0, 1])
+    mf.compress_into(store, good, good, 0.9)               # the aligned call still works
+    torch.cuda.synchronize()
+
+
 def test_read_probe_reads_without_writing(mf):
     src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
     sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
