@@ -51,21 +51,23 @@ __global__ void k_fill_u32(uint32_t* p, int n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
+// One workgroup per (group of block rows, KV head): block rows brow = blockIdx.x + k gridDim.x.
 template <typename T>
-__global__ __launch_bounds__(256) void k_vmax(const T* __restrict__ V, int H_kv, int D, int B,
+__global__ __launch_bounds__(256) void k_vmax(const T* __restrict__ V, int H_kv, int D, int B, int n_brow,
                                               const int32_t* __restrict__ info,
                                               const int32_t* __restrict__ brow_seq,
                                               const int32_t* __restrict__ page_table,
                                               int page_size, int pages_per_seq,
                                               uint32_t* __restrict__ vmax_bits) {
   __shared__ float red[4];
-  const int brow = blockIdx.x, kv = blockIdx.y;
-  const BrowInfo bi = load_info(info, brow);
-  const int seq = brow_seq[brow];
+  const int kv = blockIdx.y;
   // 16-byte loads: a token's D values of one KV head are contiguous in either layout
   constexpr int EPC = 16 / (int)sizeof(T);         // elements per 16-byte chunk
   const int CH = D / EPC;                          // chunks per token row
   float m = 0.f;
+  for (int brow = blockIdx.x; brow < n_brow; brow += gridDim.x) {
+  const BrowInfo bi = load_info(info, brow);
+  const int seq = brow_seq[brow];
   for (int e = threadIdx.x; e < B * CH; e += blockDim.x) {
     const int kloc = bi.I * B + e / CH;
     if (kloc < bi.n) {
@@ -81,6 +83,7 @@ __global__ __launch_bounds__(256) void k_vmax(const T* __restrict__ V, int H_kv,
         }
       }
     }
+  }
   }
   // NaN must win the maximum so that the scale falls back to 1
   if (m != m) m = __uint_as_float(0x7FC00000u);
@@ -172,13 +175,17 @@ hipError_t v_prepare(const VprepArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, a.vmax_bits, a.H_kv, 0u);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.n_brow < 1) {                              // no tokens: scale exponents only
+    hipLaunchKernelGGL(k_vexps, dim3(1), dim3(64), 0, s, a.vmax_bits, a.H_kv, a.exps);
+    return hipGetLastError();
+  }
   if (a.dtype == DT_BF16)
-    hipLaunchKernelGGL((k_vmax<uint16_t>), dim3(a.n_brow, a.H_kv), dim3(256), 0, s,
-                       (const uint16_t*)a.V, a.H_kv, a.d, a.B, a.info, a.brow_seq, a.page_table,
+    hipLaunchKernelGGL((k_vmax<uint16_t>), dim3(min(a.n_brow, 64), a.H_kv), dim3(256), 0, s,
+                       (const uint16_t*)a.V, a.H_kv, a.d, a.B, a.n_brow, a.info, a.brow_seq, a.page_table,
                        a.page_size, a.pages_per_seq, a.vmax_bits);
   else
-    hipLaunchKernelGGL((k_vmax<float>), dim3(a.n_brow, a.H_kv), dim3(256), 0, s,
-                       (const float*)a.V, a.H_kv, a.d, a.B, a.info, a.brow_seq, a.page_table,
+    hipLaunchKernelGGL((k_vmax<float>), dim3(min(a.n_brow, 64), a.H_kv), dim3(256), 0, s,
+                       (const float*)a.V, a.H_kv, a.d, a.B, a.n_brow, a.info, a.brow_seq, a.page_table,
                        a.page_size, a.pages_per_seq, a.vmax_bits);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_vexps, dim3(1), dim3(64), 0, s, a.vmax_bits, a.H_kv, a.exps);
