@@ -111,11 +111,13 @@ __global__ void k_vexps(const uint32_t* __restrict__ vmax_bits, int H_kv, int32_
   exps[kv] = e;
 }
 
-// One thread per 16-byte operand record: lane (a, dd) of tile (kv, block row, 32-key chunk,
-// 16-column slice) holds V[key(e)][kv][16 dt + dd] for e = 0..7, where within the chunk
-// key(e) = 4a + e for e < 4 and 16 + 4a + (e - 4) otherwise.  That key order matches the
-// accumulator layout of two stacked 16x16 score tiles, so attention probabilities computed in
-// registers can be used as the other MFMA operand without a transpose.
+// One workgroup per (block row, KV head).  The block's V rows are staged in LDS with 16-byte
+// loads (zero past the sequence's end), then each thread writes 16-byte operand records: lane
+// (a, dd) of tile (kv, block row, 32-key chunk, 16-column slice) holds V[key(e)][kv][16 dt + dd]
+// for e = 0..7, where within the chunk key(e) = 4a + e for e < 4 and 16 + 4a + (e - 4) otherwise.
+// That key order matches the accumulator layout of two stacked 16x16 score tiles, so attention
+// probabilities computed in registers can be used as the other MFMA operand without a
+// transpose.  The records of one (KV head, block row) are contiguous.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_vconvert(const T* __restrict__ V, int H_kv, int B,
                                                   int n_brow, const int32_t* __restrict__ info,
@@ -125,47 +127,52 @@ __global__ __launch_bounds__(256) void k_vconvert(const T* __restrict__ V, int H
                                                   const int32_t* __restrict__ exps,
                                                   uint16_t* __restrict__ frag) {
   constexpr int NDT = D / 16;
-  const int NCH = B / 32;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)H_kv * n_brow * NCH * NDT * 64;
-  if (gid >= total) return;
-  const int lane = (int)(gid & 63);
-  int64_t rec = gid >> 6;
-  const int dt = (int)(rec % NDT);
-  rec /= NDT;
-  const int ch = (int)(rec % NCH);
-  rec /= NCH;
-  const int brow = (int)(rec % n_brow);
-  const int kv = (int)(rec / n_brow);
+  constexpr int ROW = D * (int)sizeof(T) + 16;    // staged row stride: keys 4 a + e fall on distinct banks
+  constexpr int CH = D * (int)sizeof(T) / 16;     // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[64 * ROW];
+  const int brow = blockIdx.x, kv = blockIdx.y;
   const BrowInfo bi = load_info(info, brow);
   const int seq = brow_seq[brow];
-  const int a = lane >> 4, dd = lane & 15;
-  const float scale = ldexpf(1.f, exps[kv]);
-  uint32_t packed[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    uint32_t two = 0;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int e = 2 * p + q;
-      const int koff = 32 * ch + (e < 4 ? 4 * a + e : 16 + 4 * a + (e - 4));
-      const int kloc = bi.I * B + koff;
-      float v = 0.f;
-      if (kloc < bi.n)
-        v = load_v<T>(V, v_offset(bi, seq, kloc, kv, 16 * dt + dd, H_kv, D, page_table, page_size,
-                                   pages_per_seq));
-      two |= (uint32_t)f32_to_f16_bits(v * scale) << (16 * q);
-    }
-    packed[p] = two;
+  for (int e = threadIdx.x; e < B * CH; e += blockDim.x) {
+    const int key = e / CH, chunk = e % CH;
+    const int kloc = bi.I * B + key;
+    v4u x = zero_u4();
+    if (kloc < bi.n)
+      x = ld16(V + v_offset(bi, seq, kloc, kv, chunk * (16 / (int)sizeof(T)), H_kv, D, page_table, page_size,
+                            pages_per_seq));
+    *reinterpret_cast<v4u*>(s_v + key * ROW + chunk * 16) = x;
   }
-  st16(frag + gid * 8, v4u{packed[0], packed[1], packed[2], packed[3]});
+  __syncthreads();
+  const float scale = ldexpf(1.f, exps[kv]);
+  const int NCH = B / 32;
+  const int n_rec = NCH * NDT * 64;
+  uint16_t* out = frag + ((size_t)kv * n_brow + brow) * (size_t)n_rec * 8;
+  for (int r = threadIdx.x; r < n_rec; r += blockDim.x) {
+    const int lane = r & 63, dt = (r >> 6) % NDT, ch = (r >> 6) / NDT;
+    const int a = lane >> 4, dd = lane & 15;
+    const int col = 16 * dt + dd;
+    uint32_t packed[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t two = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int e = 2 * p + q;
+        const int koff = 32 * ch + (e < 4 ? 4 * a + e : 16 + 4 * a + (e - 4));
+        float v;
+        if constexpr (sizeof(T) == 2) v = bf16_to_f32(*reinterpret_cast<const uint16_t*>(s_v + koff * ROW + col * 2));
+        else v = *reinterpret_cast<const float*>(s_v + koff * ROW + col * 4);
+        two |= (uint32_t)f32_to_f16_bits(v * scale) << (16 * q);
+      }
+      packed[p] = two;
+    }
+    st16(out + (size_t)r * 8, v4u{packed[0], packed[1], packed[2], packed[3]});
+  }
 }
 
 template <typename T, int D>
 static hipError_t vconvert_t(const VprepArgs& a, hipStream_t s) {
-  const int64_t total = (int64_t)a.H_kv * a.n_brow * (a.B / 32) * (D / 16) * 64;
-  const unsigned grid = (unsigned)((total + 255) / 256);
-  hipLaunchKernelGGL((k_vconvert<T, D>), dim3(grid), dim3(256), 0, s, (const T*)a.V, a.H_kv, a.B,
+  hipLaunchKernelGGL((k_vconvert<T, D>), dim3(a.n_brow, a.H_kv), dim3(256), 0, s, (const T*)a.V, a.H_kv, a.B,
                      a.n_brow, a.info, a.brow_seq, a.page_table, a.page_size, a.pages_per_seq,
                      a.exps, a.frag);
   return hipGetLastError();
