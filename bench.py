@@ -411,6 +411,7 @@ def main():
     traffic = traffic_from_profile(os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip"))
     cp_ms = total_ms(rec["compress"]) / max(len(rec["compress"]), 1)
     # compress work: two score passes over every causal block plus one over the kept blocks
+    store_gb = float(np.mean([nnzb[l] * wl.H_s * B * B * 2 for l in mapped])) / 1e9
     cp_flops = np.mean([(2 * n_causal + nnzb[l]) * 2 * wl.H_s * B * B * wl.d for l in mapped])
     dense_ms = total_ms(rec["dense"]) / max(len(rec["dense"]), 1)
     dense_flops = 4 * wl.H_r * wl.d * sum(min(B, L - I * B) * (I * B + (min(B, L - I * B) + 1) / 2)
@@ -441,6 +442,8 @@ def main():
                      "algorithmic": kr_bytes / max(n_kr, 1) / 1e9,
                      "algorithmic_unit": "GB per launch"},
         "retrieve": {"ms_per_layer": kr_avg_ms, "tokens_per_s_per_layer": L / (kr_avg_ms * 1e-3),
+                     "ms_per_launch_median": float(np.median([a.elapsed_time(b) for a, b in rec["retrieve"]])),
+                     "launches_timed": n_kr,
                      "algorithmic_GB_per_layer": kr_bytes / max(n_kr, 1) / 1e9,
                      "mfma_TFLOPs": kr_flops / (kr_ms * 1e-3) / 1e12 if kr_ms > 0 else 0.0,
                      "kept_blocks_mean": float(np.mean(list(nnzb.values()))),
@@ -448,7 +451,10 @@ def main():
                      "full_stack_tokens_per_s": L / (kr_avg_ms * 1e-3 * max(n_map, 1))},
         "compress": {"ms_per_layer": cp_ms, "tokens_per_s_per_layer": L / (cp_ms * 1e-3),
                      "mfma_TFLOPs": cp_flops / (cp_ms * 1e-3) / 1e12,
-                     "frac_bf16_peak": cp_flops / (cp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+                     "frac_bf16_peak": cp_flops / (cp_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                     # kept probabilities written per layer (bf16), over the whole compress call
+                     "store_GB_per_layer": store_gb,
+                     "store_write_GB_per_s": store_gb / (cp_ms * 1e-3)},
         "v_prepare": {"ms_per_layer": total_ms(rec["vprep"]) / max(len(rec["vprep"]), 1)},
         "dense_recompute": {"ms_per_layer": dense_ms,
                             "TFLOPs": dense_flops / (dense_ms * 1e-3) / 1e12 if dense_ms > 0 else 0.0},
