@@ -294,7 +294,7 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   if ((st = ensure(ctx->M, nbn * 8 + 256, "head-summed mass")) != MF_OK) return st;
   if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
   if ((st = ensure(ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts")) != MF_OK) return st;
-  if ((st = ensure(ctx->part, (size_t)bsr->n_brow * ((bsr->nb_max + 15) / 16) * bsr->H_s * bsr->B * 8 + 256,
+  if ((st = ensure(ctx->part, (size_t)bsr->n_brow * ((bsr->nb_max + mf::kGatherChunk - 1) / mf::kGatherChunk) * bsr->H_s * bsr->B * 8 + 256,
                    "row sums")) != MF_OK)
     return st;
   const size_t elem = dtype == MF_BF16 ? 2 : 4;

@@ -308,7 +308,8 @@ __global__ __launch_bounds__(256) void k_emit(const uint8_t* __restrict__ flags,
 }
 
 // ------------------------------------------------------------------------------------------
-// k_gather: one workgroup per (chunk of 16 kept blocks of a block row, group of 8 sender heads),
+// k_gather: one workgroup per (chunk of kGatherChunk kept blocks of a block row, group of 8 sender
+// heads),
 // 8 waves; wave w owns sender head 8*hg + w and keeps that head's query rows of the block row in
 // registers.  Work items are ordered chunk-major, so the workgroups in flight share one range of
 // key blocks in L2.  Per kept block of the chunk, in column order, and 16-key slice:
@@ -485,9 +486,6 @@ __device__ __forceinline__ void gather_block(bool MASKED, const Frag<T, D> (&qf)
   }
 }
 
-// kept blocks per gather work item
-constexpr int kGatherChunk = 16;
-
 template <typename T, int B, int D>
 struct GatherLds {
   static constexpr int kTile = B * B * 16;                               // 8-head records of a block
@@ -621,7 +619,7 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
 }
 
 // ------------------------------------------------------------------------------------------
-// kept row mass: the row's chunk sums (each over up to 16 kept blocks, in column order) added in
+// kept row mass: the row's chunk sums (each over up to kGatherChunk kept blocks, in column order) added in
 // chunk order, fp64 throughout
 __global__ void k_rowmass(const double* __restrict__ part, const int32_t* __restrict__ block_ptr,
                           const int32_t* __restrict__ info, const int32_t* __restrict__ counters,
