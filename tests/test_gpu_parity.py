@@ -105,6 +105,21 @@ def test_compress_bf16_shapes(mf, lengths, H_s, d, B, tau, seed):
         assert host["nnzb"] == n_causal
 
 
+def test_compress_rows_spanning_several_gather_items(mf):
+    # tau = 1 keeps every causal block, so the last block rows of a 4200-token sequence at B = 32
+    # hold up to 132 kept blocks: more than one gather work item (128 kept blocks), with a short
+    # remainder.  Their probabilities and kept row mass are compared with the oracle.
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 5, lengths=[4200], H_s=4, H_r=4, H_kv=2, d=64)
+    tau = _f32(1.0)
+    B = 32
+    store, host = _compress_case(mf, x, tau, B, "bf16")
+    counts = np.diff(host["block_ptr"])
+    assert counts.max() == 132 and (counts > 128).sum() == 4
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    _check_compress(x, host, ref, tau, B)
+
+
 def test_compress_scores_far_above_the_running_maximum(mf):
     """Block statistics past a row's first block are summed against the row's running maximum;
     when a later block's scores sit far above it (z would reach 2^64) the wave redoes the block
