@@ -132,7 +132,19 @@ def cpu_baseline(wl, args, mapped_layers, n_mapped, recompute_layers):
                        f"{I} of one recomputed layer ({t_dense:.1f} s), extrapolated by per-row work to "
                        f"{n_mapped} mapped + {len(recompute_layers)} recomputed layers "
                        f"(est. {est:.0f} s per step)"),
-            "extrapolated": True}
+            "extrapolated": True, "cpu_model": _cpu_model(),
+            "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def fanout(mf, torch, wl, args, store, recvs, pvs, kv_map, B, cu, ctx, dev):
