@@ -10,6 +10,8 @@ One step = one pass of the whole path over one batch (all inputs resident in HBM
     the slot holding its sender layer's blocks; stream B refills that slot with a later layer once
     the retrieve is done.  HIP events order the two streams so that a retrieve never shares the
     GPU with a compress: its event-timed duration is the kernel's own.
+The whole schedule is one library call per step (mf_prefill_layers); its stage times come from
+the library's own HIP events, recorded on the stream each kernel runs on.
 The JSON line reports whole-step throughput (tokens through the full receiver depth per second),
 the fused-retrieve kernel's own timing, bytes and roofline fraction from HIP events recorded on its
 stream, and the fp64 oracle timed on a bounded sample of the same workload on the host cores.
@@ -300,99 +302,70 @@ def main():
     dev = torch.device("cuda:0")
     ctx = mf.Context.default(0)
     L, B, tau = wl.seq_len, wl.B, float(np.float32(wl.tau))
-    pi = mf.map_layers(wl.n_recv_layers, wl.n_send_layers, wl.R)
+    pi = mf.layer_map_uniform(wl.n_recv_layers, wl.n_send_layers, wl.R)
+    recompute = [l for l in range(wl.n_recv_layers) if pi[l] < 0]
     mapped = [l for l in range(wl.n_recv_layers) if pi[l] >= 0]
     if args.layers is not None:
+        # a shorter stack: the first `layers` mapped layers only
+        n_recv = len(recompute) + args.layers
+        pi = pi[:n_recv]
         mapped = mapped[: args.layers]
-    recompute = [l for l in range(wl.n_recv_layers) if pi[l] < 0]
     n_map = len(mapped)
+    n_recv = len(pi)
     k = max(1, min(args.slots, n_map))
     cu = synth.cu_seqlens_of([L])
+    mf.map_layers(pi, wl.n_send_layers, len(recompute), ctx=ctx)
     log(f"workload {wl.name}: {n_map} mapped layers (pi={[pi[l] for l in mapped]}), recompute {recompute}, "
         f"{k} slots")
 
     # ---- inputs, resident in HBM ------------------------------------------------------------
     t_gen = time.time()
-    send, recv = {}, {}
-    for l in mapped:
-        x = synth.make_layer_inputs_torch(wl, args.seed, layer=l, device=dev)
-        send[l] = (x["q_s"], x["k_s"])
-        recv[l] = (x["w"], x["v_r"])
-        kv_map = x["kv_head_map"]
-    dense_in = {l: synth.make_dense_inputs_torch(wl, args.seed, layer=l, device=dev) for l in recompute}
-    if not mapped:
-        kv_map = [g // (wl.H_r // wl.H_kv) for g in range(wl.H_r)]
-    O = {l: torch.empty((L, wl.H_r, wl.d), dtype=torch.float32, device=dev) for l in mapped + recompute}
+    send = [None] * wl.n_send_layers
+    for j in sorted({pi[l] for l in mapped}):
+        x = synth.make_sender_inputs_torch(wl, args.seed, layer=j, device=dev)
+        send[j] = (x["q_s"], x["k_s"])
+    recv = []
+    kv_map = [g // (wl.H_r // wl.H_kv) for g in range(wl.H_r)]
+    for l in range(n_recv):
+        if pi[l] < 0:
+            di = synth.make_dense_inputs_torch(wl, args.seed, layer=l, device=dev)
+            recv.append({"q": di["q"], "k": di["k"], "v": di["v"]})
+        else:
+            x = synth.make_receiver_inputs_torch(wl, args.seed, layer=100 + l, device=dev)
+            recv.append({"w": x["w"], "v": x["v_r"]})
+        recv[-1]["o"] = torch.empty((L, wl.H_r, wl.d), dtype=torch.float32, device=dev)
     slots = [mf.BlockStore.create(wl.H_s, B, cu, capacity=-1, ctx=ctx) for _ in range(k)]
-    pv = {l: mf.v_prepare(recv[l][1], B, cu, ctx=ctx) for l in mapped}
     torch.cuda.synchronize()
     log(f"inputs generated in {time.time() - t_gen:.1f} s; slot capacity {slots[0].capacity} blocks")
 
     # ---- census: kept blocks per mapped layer (deterministic, same in every step) ------------
     nnzb = {}
     for l in mapped:
-        mf.compress_into(slots[0], *send[l], tau)
+        mf.compress_into(slots[0], *send[pi[l]], tau)
         nnzb[l] = slots[0].sync()
     n_causal = slots[0].n_causal
     n_brow = slots[0].n_brow
     log(f"kept blocks per layer: min {min(nnzb.values())} max {max(nnzb.values())} of {n_causal} "
         f"(density {np.mean([nnzb[l] / n_causal for l in mapped]):.3f})")
 
-    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
-    b_done = torch.cuda.Event()      # last compress enqueued on stream B
-    a_done = torch.cuda.Event()      # last retrieve enqueued on stream A
-    state = {"a_recorded": False}
+    s_main, s_pre = torch.cuda.Stream(), torch.cuda.Stream()
 
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    c_done = [torch.cuda.Event() for _ in range(n_map)]   # compress i finished (overlapped schedule)
-
-    def step(rec, overlap=False):
-        # Slots filled by the previous step's retrieves must be consumed before refilling.
-        if state["a_recorded"]:
-            sB.wait_event(a_done)
-
-        def enqueue_compress(i):
-            e0, e1 = ev(), ev()
-            e0.record(sB)
-            mf.compress_into(slots[i % k], *send[mapped[i]], tau, stream=sB)
-            e1.record(sB)
-            b_done.record(sB)
-            c_done[i].record(sB)
-            rec["compress"].append((e0, e1))
-
-        # stream B prefetches the first k slots while stream A recomputes layers 0..R-1
-        for i in range(min(k, n_map)):
-            enqueue_compress(i)
-        for l in recompute:
-            di = dense_in[l]
-            e0, e1 = ev(), ev()
-            e0.record(sA)
-            mf.dense_attention(di["q"], di["k"], di["v"], di["kv_head_map"], out=O[l], ctx=ctx, stream=sA)
-            e1.record(sA)
-            rec["dense"].append((e0, e1))
-        for i, l in enumerate(mapped):
-            # slot i is filled and stream B is idle: the retrieve has the GPU to itself.  In the
-            # overlapped schedule it waits only for slot i and shares the GPU with later compresses.
-            sA.wait_event(c_done[i] if overlap else b_done)
-            e0, e1, e2 = ev(), ev(), ev()
-            e0.record(sA)
-            mf.v_prepare(recv[l][1], B, cu, out=pv[l], ctx=ctx, stream=sA)
-            e1.record(sA)
-            mf.retrieve_prepared(slots[i % k], recv[l][0], pv[l], kv_map, out=O[l], stream=sA)
-            e2.record(sA)
-            a_done.record(sA)
-            state["a_recorded"] = True
-            rec["vprep"].append((e0, e1))
-            rec["retrieve"].append((e1, e2))
-            if i + k < n_map:
-                sB.wait_event(a_done)      # slot (i + k) % k == i % k is free again
-                enqueue_compress(i + k)
+    def step(rec, isolate=True):
+        """One receiver prefill through the native pipeline (mf_prefill_layers), then its stage
+        times from the library's events (the host waits for the step to read them)."""
+        mf.prefill_layers(slots, send, recv, kv_map, tau, isolate=isolate, timing=True, ctx=ctx,
+                          stream_main=s_main, stream_prefetch=s_pre)
+        t = mf.prefill_timings(len(recompute), n_map, ctx=ctx)
+        for key in rec:
+            rec[key] += t[key]
 
     def new_rec():
         return {"dense": [], "compress": [], "vprep": [], "retrieve": []}
 
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(new_rec())
     torch.cuda.synchronize()
@@ -406,26 +379,23 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    def total_ms(pairs):
-        return sum(a.elapsed_time(b) for a, b in pairs)
-
     # sanity: the last layers' stores still hold the census counts
-    for i in range(max(0, n_map - k), n_map):
-        got = slots[i % k].sync()
-        assert got == nnzb[mapped[i]], f"kept-block count changed for layer {mapped[i]}: {got} vs {nnzb[mapped[i]]}"
+    for m in range(max(0, n_map - k), n_map):
+        got = slots[m % k].sync()
+        assert got == nnzb[mapped[m]], f"kept-block count changed for layer {mapped[m]}: {got} vs {nnzb[mapped[m]]}"
 
-    kr_ms = total_ms(rec["retrieve"])
+    kr_ms = sum(rec["retrieve"])
     n_kr = len(rec["retrieve"])
     kr_bytes = args.steps * sum(retrieve_bytes(nnzb[l], wl.H_s, B, n_brow, L, wl.H_kv, wl.H_r, wl.d) for l in mapped)
     kr_flops = args.steps * sum(retrieve_flops(nnzb[l], wl.H_s, wl.H_r, B, wl.d) for l in mapped)
     kr_avg_ms = kr_ms / max(n_kr, 1)
     achieved = kr_bytes / (kr_ms * 1e-3) / 1e9 if kr_ms > 0 else 0.0
     traffic = traffic_from_profile(os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip"))
-    cp_ms = total_ms(rec["compress"]) / max(len(rec["compress"]), 1)
+    cp_ms = sum(rec["compress"]) / max(len(rec["compress"]), 1)
     # compress work: two score passes over every causal block plus one over the kept blocks
     store_gb = float(np.mean([nnzb[l] * wl.H_s * B * B * 2 for l in mapped])) / 1e9
     cp_flops = np.mean([(2 * n_causal + nnzb[l]) * 2 * wl.H_s * B * B * wl.d for l in mapped])
-    dense_ms = total_ms(rec["dense"]) / max(len(rec["dense"]), 1)
+    dense_ms = sum(rec["dense"]) / max(len(rec["dense"]), 1)
     dense_flops = 4 * wl.H_r * wl.d * sum(min(B, L - I * B) * (I * B + (min(B, L - I * B) + 1) / 2)
                                           for I in range((L + B - 1) // B))
 
@@ -454,7 +424,7 @@ def main():
                      "algorithmic": kr_bytes / max(n_kr, 1) / 1e9,
                      "algorithmic_unit": "GB per launch"},
         "retrieve": {"ms_per_layer": kr_avg_ms, "tokens_per_s_per_layer": L / (kr_avg_ms * 1e-3),
-                     "ms_per_launch_median": float(np.median([a.elapsed_time(b) for a, b in rec["retrieve"]])),
+                     "ms_per_launch_median": float(np.median(rec["retrieve"])),
                      "launches_timed": n_kr,
                      "algorithmic_GB_per_layer": kr_bytes / max(n_kr, 1) / 1e9,
                      "mfma_TFLOPs": kr_flops / (kr_ms * 1e-3) / 1e12 if kr_ms > 0 else 0.0,
@@ -467,31 +437,32 @@ def main():
                      # kept probabilities written per layer (bf16), over the whole compress call
                      "store_GB_per_layer": store_gb,
                      "store_write_GB_per_s": store_gb / (cp_ms * 1e-3)},
-        "v_prepare": {"ms_per_layer": total_ms(rec["vprep"]) / max(len(rec["vprep"]), 1)},
+        "v_prepare": {"ms_per_layer": sum(rec["vprep"]) / max(len(rec["vprep"]), 1)},
         "dense_recompute": {"ms_per_layer": dense_ms,
                             "TFLOPs": dense_flops / (dense_ms * 1e-3) / 1e12 if dense_ms > 0 else 0.0},
     }
 
     if args.overlap:
         # same work, retrieves beside the compresses of later layers; outputs must not change
-        ref = {l: O[l].double().sum().item() for l in mapped}
+        ref = {l: recv[l]["o"].clone() for l in range(n_recv)}
         for _ in range(args.warmup):
-            step(new_rec(), overlap=True)
+            step(new_rec(), isolate=False)
         torch.cuda.synchronize()
         orec = new_rec()
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            step(orec, overlap=True)
+            step(orec, isolate=False)
         torch.cuda.synchronize()
         o_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        same = all(O[l].double().sum().item() == ref[l] for l in mapped)
-        for i in range(max(0, n_map - k), n_map):
-            assert slots[i % k].sync() == nnzb[mapped[i]], "kept-block count changed in the overlapped schedule"
-        assert same, "overlapped schedule changed a retrieve output"
+        same = all(torch.equal(recv[l]["o"], ref[l]) for l in range(n_recv))
+        del ref
+        for m in range(max(0, n_map - k), n_map):
+            assert slots[m % k].sync() == nnzb[mapped[m]], "kept-block count changed in the overlapped schedule"
+        assert same, "overlapped schedule changed an output"
         out["overlap"] = {"ms_per_step": o_ms, "tokens_per_s": L / (o_ms * 1e-3),
-                          "retrieve_ms_per_layer_shared": total_ms(orec["retrieve"]) / max(len(orec["retrieve"]), 1),
-                          "compress_ms_per_layer_shared": total_ms(orec["compress"]) / max(len(orec["compress"]), 1),
-                          "outputs_unchanged": same}
+                          "retrieve_ms_per_layer_shared": sum(orec["retrieve"]) / max(len(orec["retrieve"]), 1),
+                          "compress_ms_per_layer_shared": sum(orec["compress"]) / max(len(orec["compress"]), 1),
+                          "outputs_bit_identical": same}
 
     if args.probe_bytes > 0:
         n = args.probe_bytes // 4
@@ -531,15 +502,18 @@ def main():
         del src, sink
 
     if args.extras and n_map >= 1:
-        out["prefill"] = prefill(mf, torch, wl, args, send[mapped[-1]], slots[(n_map - 1) % k], tau, ctx, dev)
+        out["prefill"] = prefill(mf, torch, wl, args, send[pi[mapped[-1]]], slots[(n_map - 1) % k], tau, ctx, dev)
 
     if args.extras and n_map >= 1:
-        out["prefix_reuse"] = prefix_reuse(mf, torch, wl, args, send[mapped[-1]], recv[mapped[-1]], kv_map, tau,
-                                           ctx, dev)
+        last = recv[mapped[-1]]
+        out["prefix_reuse"] = prefix_reuse(mf, torch, wl, args, send[pi[mapped[-1]]], (last["w"], last["v"]), kv_map,
+                                           tau, ctx, dev)
 
     if args.extras and n_map >= 2:
-        out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [recv[l] for l in mapped[-2:]],
-                               [pv[l] for l in mapped[-2:]], kv_map, B, cu, ctx, dev)
+        two = mapped[-2:]
+        pvs = [mf.v_prepare(recv[l]["v"], B, cu, ctx=ctx) for l in two]
+        out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [(recv[l]["w"], recv[l]["v"]) for l in two],
+                               pvs, kv_map, B, cu, ctx, dev)
 
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample (CPU)")

@@ -16,7 +16,10 @@ from .mapflow import (  # noqa: F401
     copy_probe,
     read_probe,
     dense_attention,
+    layer_map_uniform,
     map_layers,
+    prefill_layers,
+    prefill_timings,
     probs_canonical_to_store,
     prefix_hashes,
     probs_store_to_canonical,

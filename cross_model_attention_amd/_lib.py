@@ -34,13 +34,28 @@ class MfVfrag(ctypes.Structure):
     ]
 
 
+class MfRecvLayer(ctypes.Structure):
+    _fields_ = [("Q", c_void_p), ("K", c_void_p), ("V", c_void_p), ("W", c_void_p), ("O", c_void_p)]
+
+
+class MfSendLayer(ctypes.Structure):
+    _fields_ = [("Q", c_void_p), ("K", c_void_p)]
+
+
+# mf_alloc_fn / mf_free_fn
+ALLOC_FN = ctypes.CFUNCTYPE(c_void_p, c_size_t, c_void_p, c_void_p)
+FREE_FN = ctypes.CFUNCTYPE(None, c_void_p, c_size_t, c_void_p, c_void_p)
+MF_PREFILL_ISOLATE, MF_PREFILL_TIMING = 1, 2
+
 _P_I32 = POINTER(c_int32)
+_P_F32 = POINTER(c_float)
 _SIGNATURES = {
     "mf_version": (c_char_p, []),
     "mf_last_error": (c_char_p, []),
-    "mf_create": (c_int, [c_int, POINTER(c_void_p)]),
+    "mf_create": (c_int, [c_int, ALLOC_FN, FREE_FN, c_void_p, POINTER(c_void_p)]),
     "mf_destroy": (c_int, [c_void_p]),
-    "mf_map_layers": (c_int, [c_int32, c_int32, c_int32, _P_I32]),
+    "mf_map_layers": (c_int, [c_void_p, _P_I32, c_int32, c_int32, c_int32]),
+    "mf_layer_map_uniform": (c_int, [c_int32, c_int32, c_int32, _P_I32]),
     "mf_check_layer_map": (c_int, [_P_I32, c_int32, c_int32, c_int32]),
     "mf_bsr_create": (c_int, [c_void_p, c_int32, c_int32, _P_I32, c_int32, c_int64, POINTER(MfBsr)]),
     "mf_bsr_create_range": (c_int, [c_void_p, c_int32, c_int32, _P_I32, c_int32, _P_I32, c_int64, POINTER(MfBsr)]),
@@ -72,6 +87,10 @@ _SIGNATURES = {
                             c_int32, c_void_p, c_int32, c_int32, _P_I32, c_void_p, c_void_p]),
     "mf_dense_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32,
                                    c_int32, _P_I32, c_int32, _P_I32, c_void_p, c_void_p]),
+    "mf_prefill_layers": (c_int, [c_void_p, POINTER(MfRecvLayer), POINTER(MfSendLayer), c_int, c_int32, c_int32,
+                                  c_int32, _P_I32, c_float, c_int32, POINTER(MfBsr), ctypes.c_uint32, c_void_p,
+                                  c_void_p]),
+    "mf_prefill_timings": (c_int, [c_void_p, _P_F32, _P_F32, _P_F32, _P_F32]),
     "mf_copy_probe": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mf_read_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     "mf_prefix_hashes": (c_int, [_P_I32, c_int64, c_int32, POINTER(c_uint64)]),

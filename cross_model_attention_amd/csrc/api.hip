@@ -120,62 +120,113 @@ mf_status build_geometry(const int32_t* cu, int32_t n_seq, int32_t B, Geometry& 
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Where device memory comes from: the caller's allocator, or hipMalloc / hipFree.  Stores and
+// prepared V keep a copy, so they can be released after their context is gone.
+struct Allocator {
+  mf_alloc_fn alloc = nullptr;
+  mf_free_fn release = nullptr;
+  void* user = nullptr;
+
+  void* take(size_t bytes, hipStream_t s) const {
+    if (alloc) return alloc(bytes, s, user);
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return p;
+  }
+  // Callers have made sure no enqueued work still reads or writes p.
+  void give(void* p, size_t bytes, hipStream_t s) const {
+    if (!p) return;
+    if (release) release(p, bytes, s, user);
+    else (void)hipFree(p);
+  }
+};
+
 // One device buffer that only grows.
 struct Scratch {
   void* p = nullptr;
   size_t bytes = 0;
 };
 
-mf_status ensure(Scratch& s, size_t bytes, const char* what) {
+// Grow a context buffer.  Every user of one buffer is ordered on the calling stream (the
+// context's contract), so once that stream is idle the old buffer is unused.
+mf_status ensure(const Allocator& al, Scratch& s, size_t bytes, const char* what, hipStream_t stream) {
   if (bytes <= s.bytes) return MF_OK;
   if (s.p) {
-    MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize before scratch growth");
-    MF_HIP(hipFree(s.p), "hipFree(scratch)");
+    MF_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize before scratch growth");
+    al.give(s.p, s.bytes, stream);
     s.p = nullptr;
     s.bytes = 0;
   }
   const size_t want = align_up(bytes, 1 << 20);
-  if (hipMalloc(&s.p, want) != hipSuccess) {
-    (void)hipGetLastError();
-    s.p = nullptr;
-    return fail(MF_ERR_OOM, "out of device memory growing %s scratch to %zu bytes", what, want);
-  }
+  s.p = al.take(want, stream);
+  if (!s.p) return fail(MF_ERR_OOM, "out of device memory growing %s scratch to %zu bytes", what, want);
   s.bytes = want;
   return MF_OK;
 }
 
+void release_scratch(const Allocator& al, Scratch& s) {
+  al.give(s.p, s.bytes, nullptr);
+  s = Scratch();
+}
+
 // Bookkeeping behind mf_bsr::_owner.
 struct BsrOwner {
+  Allocator al;
   void* meta = nullptr;
+  size_t meta_bytes = 0;
   void* data = nullptr;
+  size_t data_bytes = 0;
   int32_t* pairs = nullptr;       // device copy of geom.pairs (inside meta)
   uint8_t* active = nullptr;      // device copy of geom.active when the store is ranged (inside meta)
+  int32_t* brow_seq = nullptr;    // device copy of geom.brow_seq (inside meta)
   bool cache_owned = false;       // an entry of an mf_cache: freed by the cache only
   Geometry geom;
 };
 
 // Bookkeeping behind mf_vfrag::_owner.
 struct VfragOwner {
+  Allocator al;
   void* tables = nullptr;   // info, brow_seq, exps, vmax scratch
+  size_t tables_bytes = 0;
   void* frag = nullptr;     // only when the library allocated it
+  size_t frag_bytes = 0;
   int32_t* info = nullptr;
   int32_t* brow_seq = nullptr;
   uint32_t* vmax = nullptr;
   Geometry geom;
 };
 
+// Events and timings of mf_prefill_layers.
+struct PrefillState {
+  std::vector<hipEvent_t> ev;   // created on demand, destroyed with the context
+  int n_map = 0, R = 0;
+  bool timed = false;           // the last call recorded timing events
+  // event indices of the last call
+  int e_start = 0, e_end = 0;
+  std::vector<int> d0, d1, c0, c1, v0, r0, r1;
+};
+
 }  // namespace
 
 struct mf_ctx {
   int device = 0;
+  Allocator al;
   Scratch lse2, Mh, M, flags, counts, part, zbuf, ktile, hflags, lse2n, den;
   mf_vfrag vf_retrieve{};   // context-owned prepared V (mf_retrieve)
   mf_vfrag vf_dense{};      // context-owned prepared V (mf_dense_attention)
   mf_vfrag vf_prefill{};    // context-owned prepared sender V (mf_compress_prefill_into)
+  mf_vfrag vf_pipe{};       // context-owned prepared receiver V (mf_prefill_layers)
   // cached device copies of the dense-attention geometry
   Scratch dense_tables;
   std::vector<int32_t> dense_cu;
   int dense_nbrow = 0;
+  // layer map installed by mf_map_layers
+  std::vector<int32_t> pi;
+  int n_recv = 0, n_send = 0, R = 0;
+  PrefillState pre;
 };
 
 namespace {
@@ -198,17 +249,16 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   const size_t o_info = 0;
   const size_t o_order = align_up(o_info + n_info, 256);
   const size_t o_coff = align_up(o_order + (size_t)g.n_brow * 4, 256);
-  const size_t o_ptr = align_up(o_coff + (size_t)g.n_brow * 4, 256);
+  const size_t o_seq = align_up(o_coff + (size_t)g.n_brow * 4, 256);
+  const size_t o_ptr = align_up(o_seq + (size_t)g.n_brow * 4, 256);
   const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
   const size_t o_cnt = align_up(o_rkm + (size_t)H_s * g.T * 4, 256);
   const size_t o_pairs = o_cnt + 256;
   const size_t o_active = align_up(o_pairs + (size_t)g.n_pair * 8, 256);
   const size_t total = align_up(o_active + (size_t)g.n_brow, 256) + 256;
-  if (hipMalloc(&own->meta, total) != hipSuccess) {
-    (void)hipGetLastError();
-    own->meta = nullptr;
-    return fail(MF_ERR_OOM, "out of device memory for block-store metadata (%zu bytes)", total);
-  }
+  own->meta = own->al.take(total, nullptr);
+  if (!own->meta) return fail(MF_ERR_OOM, "out of device memory for block-store metadata (%zu bytes)", total);
+  own->meta_bytes = total;
   char* base = static_cast<char*>(own->meta);
   out->brow_info = reinterpret_cast<int32_t*>(base + o_info);
   out->brow_order = reinterpret_cast<int32_t*>(base + o_order);
@@ -216,6 +266,7 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   out->block_ptr = reinterpret_cast<int32_t*>(base + o_ptr);
   out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
   out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
+  own->brow_seq = reinterpret_cast<int32_t*>(base + o_seq);
   own->pairs = reinterpret_cast<int32_t*>(base + o_pairs);
   own->active = g.ranged ? reinterpret_cast<uint8_t*>(base + o_active) : nullptr;
   out->n_order = g.n_order;
@@ -226,6 +277,8 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
       e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
       e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(own->brow_seq, g.brow_seq.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess && g.n_pair > 0)
       e = hipMemcpy(own->pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice);
     if (e == hipSuccess && own->active)
@@ -234,8 +287,12 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   if (e == hipSuccess) e = hipMemset(out->block_ptr, 0, (size_t)(g.n_brow + 1) * 4);
   if (e == hipSuccess) e = hipMemset(out->counters, 0, 256);
   if (e == hipSuccess && g.T > 0) e = hipMemset(out->row_kept_mass, 0, (size_t)H_s * g.T * 4);
+  // the initialisation is complete before any stream can use the store, and before a failed
+  // creation hands the memory back
+  if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    (void)hipFree(own->meta);
+    (void)hipDeviceSynchronize();
+    own->al.give(own->meta, own->meta_bytes, nullptr);
     own->meta = nullptr;
     return hip_fail(e, "initialising block-store metadata");
   }
@@ -249,18 +306,24 @@ mf_status alloc_bsr_data(int64_t capacity, int H_s, int B, mf_bsr* out, BsrOwner
   const size_t o_row = align_up((size_t)capacity * 4, 256);
   const size_t o_probs = align_up(o_row + (size_t)capacity * 4, 256);
   const size_t total = o_probs + (size_t)capacity * probs_block_bytes(H_s, B) + 256;
-  if (hipMalloc(&own->data, total) != hipSuccess) {
-    (void)hipGetLastError();
-    own->data = nullptr;
-    return fail(MF_ERR_OOM, "out of device memory for %lld kept blocks (%zu bytes)",
-                (long long)capacity, total);
-  }
+  own->data = own->al.take(total, nullptr);
+  if (!own->data)
+    return fail(MF_ERR_OOM, "out of device memory for %lld kept blocks (%zu bytes)", (long long)capacity, total);
+  own->data_bytes = total;
   char* base = static_cast<char*>(own->data);
   out->block_idx = reinterpret_cast<int32_t*>(base + o_idx);
   out->block_row = reinterpret_cast<int32_t*>(base + o_row);
   out->probs = reinterpret_cast<uint16_t*>(base + o_probs);
   out->capacity = capacity;
   return MF_OK;
+}
+
+// Hand back a store's device arrays (the device must be idle for them).
+void bsr_release_arrays(BsrOwner* own) {
+  own->al.give(own->meta, own->meta_bytes, nullptr);
+  own->al.give(own->data, own->data_bytes, nullptr);
+  own->meta = own->data = nullptr;
+  own->meta_bytes = own->data_bytes = 0;
 }
 
 // Q, K and V are read with 16-byte loads (and key tiles by 16-byte DMA), so their base pointers
@@ -285,20 +348,20 @@ mf_status validate_compress(const void* Q, const void* K, mf_dtype dtype, int32_
 
 mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dtype dtype,
                                 int32_t d, float tau, mf_bsr* bsr, int64_t capacity,
-                                mf::CompressArgs& a) {
+                                mf::CompressArgs& a, hipStream_t stream) {
   const size_t nbn = (size_t)bsr->n_brow * bsr->nb_max;
   mf_status st;
-  if ((st = ensure(ctx->lse2, (size_t)bsr->H_s * bsr->T * 4 + 256, "lse")) != MF_OK) return st;
-  if ((st = ensure(ctx->zbuf, (size_t)bsr->H_s * bsr->n_causal * bsr->B * 8 + 256, "block statistics")) != MF_OK) return st;
-  if ((st = ensure(ctx->Mh, (size_t)bsr->H_s * nbn * 4 + 256, "block mass")) != MF_OK) return st;
-  if ((st = ensure(ctx->M, nbn * 8 + 256, "head-summed mass")) != MF_OK) return st;
-  if ((st = ensure(ctx->flags, nbn + 256, "flags")) != MF_OK) return st;
-  if ((st = ensure(ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts")) != MF_OK) return st;
-  if ((st = ensure(ctx->part, (size_t)bsr->n_brow * ((bsr->nb_max + mf::kGatherChunk - 1) / mf::kGatherChunk) * bsr->H_s * bsr->B * 8 + 256,
-                   "row sums")) != MF_OK)
+  if ((st = ensure(ctx->al, ctx->lse2, (size_t)bsr->H_s * bsr->T * 4 + 256, "lse", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->zbuf, (size_t)bsr->H_s * bsr->n_causal * bsr->B * 8 + 256, "block statistics", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->Mh, (size_t)bsr->H_s * nbn * 4 + 256, "block mass", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->M, nbn * 8 + 256, "head-summed mass", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->flags, nbn + 256, "flags", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->counts, (size_t)bsr->n_brow * 4 + 256, "counts", stream)) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->part, (size_t)bsr->n_brow * ((bsr->nb_max + mf::kGatherChunk - 1) / mf::kGatherChunk) * bsr->H_s * bsr->B * 8 + 256,
+                   "row sums", stream)) != MF_OK)
     return st;
   const size_t elem = dtype == MF_BF16 ? 2 : 4;
-  if ((st = ensure(ctx->ktile, (size_t)bsr->H_s * bsr->n_brow * bsr->B * d * elem + 256, "key operand tiles")) != MF_OK)
+  if ((st = ensure(ctx->al, ctx->ktile, (size_t)bsr->H_s * bsr->n_brow * bsr->B * d * elem + 256, "key operand tiles", stream)) != MF_OK)
     return st;
   a = mf::CompressArgs{};
   a.Q = Q;
@@ -379,31 +442,31 @@ mf_status vfrag_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B
   const bool same_geom = own && own->geom.cu == g.cu && own->geom.B == B && out->H_kv == H_kv && out->d == d;
   if (!(reuse && same_geom)) {
     if (own) {
-      if (reuse) {
-        MF_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize before V scratch growth");
-      }
-      if (own->tables) (void)hipFree(own->tables);
-      if (own->frag) (void)hipFree(own->frag);
+      // a context-owned buffer of another geometry: its users are ordered on this stream
+      if (reuse) MF_HIP(hipStreamSynchronize(stream), "hipStreamSynchronize before V scratch growth");
+      own->al.give(own->tables, own->tables_bytes, stream);
+      own->al.give(own->frag, own->frag_bytes, stream);
       delete own;
       out->_owner = nullptr;
       if (reuse) out->frag = nullptr;
     }
     own = new (std::nothrow) VfragOwner();
     if (!own) return fail(MF_ERR_OOM, "host allocation failed");
+    own->al = ctx->al;
     const size_t o_info = 0;
     const size_t o_seq = align_up((size_t)g.n_brow * 16, 256);
     const size_t o_exp = align_up(o_seq + (size_t)g.n_brow * 4, 256);
     const size_t o_max = align_up(o_exp + (size_t)H_kv * 4, 256);
     const size_t tb = o_max + 256;
-    if (hipMalloc(&own->tables, tb) != hipSuccess) {
-      (void)hipGetLastError();
+    own->tables = own->al.take(tb, stream);
+    if (!own->tables) {
       delete own;
       return fail(MF_ERR_OOM, "out of device memory for V tables");
     }
+    own->tables_bytes = tb;
     char* base = static_cast<char*>(own->tables);
     own->info = reinterpret_cast<int32_t*>(base + o_info);
     own->brow_seq = reinterpret_cast<int32_t*>(base + o_seq);
-    out->exps = reinterpret_cast<int32_t*>(base + o_exp);
     own->vmax = reinterpret_cast<uint32_t*>(base + o_max);
     hipError_t e = hipSuccess;
     if (g.n_brow > 0) {
@@ -412,20 +475,23 @@ mf_status vfrag_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B
         e = hipMemcpy(own->brow_seq, g.brow_seq.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     }
     if (e != hipSuccess) {
-      (void)hipFree(own->tables);
+      (void)hipDeviceSynchronize();
+      own->al.give(own->tables, own->tables_bytes, stream);
       delete own;
       return hip_fail(e, "uploading V tables");
     }
     if (out->frag == nullptr) {
       const size_t fb = (size_t)H_kv * g.n_brow * B * d * 2 + 256;
-      if (hipMalloc(&own->frag, fb) != hipSuccess) {
-        (void)hipGetLastError();
-        (void)hipFree(own->tables);
+      own->frag = own->al.take(fb, stream);
+      if (!own->frag) {
+        own->al.give(own->tables, own->tables_bytes, stream);
         delete own;
         return fail(MF_ERR_OOM, "out of device memory for prepared V (%zu bytes)", fb);
       }
+      own->frag_bytes = fb;
       out->frag = static_cast<uint16_t*>(own->frag);
     }
+    out->exps = reinterpret_cast<int32_t*>(base + o_exp);
     own->geom = g;
     out->_owner = own;
   }
@@ -455,12 +521,13 @@ mf_status vfrag_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, int32_t B
   return MF_OK;
 }
 
+// Release a prepared V (the device must be idle for it).
 void vfrag_release(mf_vfrag* vf) {
   if (!vf) return;
   VfragOwner* own = static_cast<VfragOwner*>(vf->_owner);
   if (own) {
-    if (own->tables) (void)hipFree(own->tables);
-    if (own->frag) (void)hipFree(own->frag);
+    own->al.give(own->tables, own->tables_bytes, nullptr);
+    own->al.give(own->frag, own->frag_bytes, nullptr);
     delete own;
   }
   std::memset(vf, 0, sizeof(*vf));
@@ -474,9 +541,11 @@ MF_EXPORT const char* mf_version(void) { return "libmapflow 0.1.0 (gfx950)"; }
 
 MF_EXPORT const char* mf_last_error(void) { return g_err.c_str(); }
 
-MF_EXPORT mf_status mf_create(int device, mf_ctx** out) {
+MF_EXPORT mf_status mf_create(int device, mf_alloc_fn alloc, mf_free_fn release, void* user, mf_ctx** out) {
   if (!out) return fail(MF_ERR_INVALID, "out is NULL");
   *out = nullptr;
+  if ((alloc == nullptr) != (release == nullptr))
+    return fail(MF_ERR_INVALID, "give both allocator callbacks or neither");
   int n = 0;
   MF_HIP(hipGetDeviceCount(&n), "hipGetDeviceCount");
   if (device < 0 || device >= n) return fail(MF_ERR_INVALID, "device %d out of range [0, %d)", device, n);
@@ -484,6 +553,9 @@ MF_EXPORT mf_status mf_create(int device, mf_ctx** out) {
   mf_ctx* ctx = new (std::nothrow) mf_ctx();
   if (!ctx) return fail(MF_ERR_OOM, "host allocation failed");
   ctx->device = device;
+  ctx->al.alloc = alloc;
+  ctx->al.release = release;
+  ctx->al.user = user;
   *out = ctx;
   return MF_OK;
 }
@@ -494,15 +566,17 @@ MF_EXPORT mf_status mf_destroy(mf_ctx* ctx) {
   (void)hipDeviceSynchronize();
   for (Scratch* s : {&ctx->lse2, &ctx->Mh, &ctx->M, &ctx->flags, &ctx->counts, &ctx->part, &ctx->zbuf, &ctx->ktile,
                      &ctx->hflags, &ctx->lse2n, &ctx->den, &ctx->dense_tables})
-    if (s->p) (void)hipFree(s->p);
+    release_scratch(ctx->al, *s);
   vfrag_release(&ctx->vf_retrieve);
   vfrag_release(&ctx->vf_dense);
   vfrag_release(&ctx->vf_prefill);
+  vfrag_release(&ctx->vf_pipe);
+  for (hipEvent_t e : ctx->pre.ev) (void)hipEventDestroy(e);
   delete ctx;
   return MF_OK;
 }
 
-MF_EXPORT mf_status mf_map_layers(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out) {
+MF_EXPORT mf_status mf_layer_map_uniform(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out) {
   if (!pi_out) return fail(MF_ERR_INVALID, "pi_out_host is NULL");
   if (n_recv < 1 || n_send < 1) return fail(MF_ERR_INVALID, "layer counts must be >= 1");
   if (R < 0 || R > n_recv) return fail(MF_ERR_INVALID, "R must be in [0, n_recv]");
@@ -531,6 +605,17 @@ MF_EXPORT mf_status mf_check_layer_map(const int32_t* pi, int32_t n_recv, int32_
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_map_layers(mf_ctx* ctx, const int32_t* pi, int32_t n_recv, int32_t n_send, int32_t R) {
+  if (!ctx) return fail(MF_ERR_INVALID, "context is NULL");
+  mf_status st = mf_check_layer_map(pi, n_recv, n_send, R);
+  if (st != MF_OK) return st;
+  ctx->pi.assign(pi, pi + n_recv);
+  ctx->n_recv = n_recv;
+  ctx->n_send = n_send;
+  ctx->R = R;
+  return MF_OK;
+}
+
 static mf_status bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* cu, int32_t n_seq,
                             const int32_t* row_begin, int64_t capacity, mf_bsr* out) {
   if (!out) return fail(MF_ERR_INVALID, "out is NULL");
@@ -541,6 +626,7 @@ static mf_status bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* 
   if ((st = set_device(ctx)) != MF_OK) return st;
   BsrOwner* own = new (std::nothrow) BsrOwner();
   if (!own) return fail(MF_ERR_OOM, "host allocation failed");
+  own->al = ctx->al;
   mf_bsr b{};
   b.B = B;
   b.H_s = H_s;
@@ -559,7 +645,7 @@ static mf_status bsr_create(mf_ctx* ctx, int32_t H_s, int32_t B, const int32_t* 
     return st;
   }
   if ((st = alloc_bsr_data(capacity, H_s, B, &b, own)) != MF_OK) {
-    (void)hipFree(own->meta);
+    bsr_release_arrays(own);          // the metadata initialisation finished inside alloc_bsr_meta
     delete own;
     return st;
   }
@@ -587,8 +673,8 @@ MF_EXPORT mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr) {
   if (own && own->cache_owned) return fail(MF_ERR_INVALID, "this store belongs to a prefix cache");
   if (own) {
     if (ctx) (void)hipSetDevice(ctx->device);
-    if (own->meta) (void)hipFree(own->meta);
-    if (own->data) (void)hipFree(own->data);
+    (void)hipDeviceSynchronize();       // no enqueued work may still use the arrays
+    bsr_release_arrays(own);
     delete own;
   }
   std::memset(bsr, 0, sizeof(*bsr));
@@ -687,9 +773,9 @@ MF_EXPORT mf_status mf_compress_into(mf_ctx* ctx, const void* Q, const void* K, 
   if (st != MF_OK) return st;
   if ((st = set_device(ctx)) != MF_OK) return st;
   if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress / retrieve
-  mf::CompressArgs a;
-  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  mf::CompressArgs a;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a, s)) != MF_OK) return st;
   MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
   MF_HIP(mf::compress_fill(a, s), "compress gather launch");
   return MF_OK;
@@ -703,19 +789,19 @@ MF_EXPORT mf_status mf_compress_into_ex(mf_ctx* ctx, const void* Q, const void* 
   if (st != MF_OK) return st;
   if ((st = set_device(ctx)) != MF_OK) return st;
   if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;   // nothing to compress
+  hipStream_t s = static_cast<hipStream_t>(stream);
   mf::CompressArgs a;
-  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a, s)) != MF_OK) return st;
   a.options = (int)options;
   if (options & MF_SELECT_PER_HEAD) {
-    if ((st = ensure(ctx->hflags, (size_t)bsr->H_s * bsr->n_brow * bsr->nb_max + 256, "per-head flags")) != MF_OK)
+    if ((st = ensure(ctx->al, ctx->hflags, (size_t)bsr->H_s * bsr->n_brow * bsr->nb_max + 256, "per-head flags", s)) != MF_OK)
       return st;
     a.hflags = static_cast<uint8_t*>(ctx->hflags.p);
   }
   if (options & MF_NORM_PER_HEAD) {
-    if ((st = ensure(ctx->lse2n, (size_t)bsr->H_s * bsr->T * 4 + 256, "per-head logsumexp")) != MF_OK) return st;
+    if ((st = ensure(ctx->al, ctx->lse2n, (size_t)bsr->H_s * bsr->T * 4 + 256, "per-head logsumexp", s)) != MF_OK) return st;
     a.lse2n = static_cast<float*>(ctx->lse2n.p);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   MF_HIP(mf::compress_plan(a, s), "compress statistics / selection launch");
   MF_HIP(mf::compress_fill(a, s), "compress gather launch");
   return MF_OK;
@@ -736,7 +822,7 @@ MF_EXPORT mf_status mf_compress_prefill_into(mf_ctx* ctx, const void* Q, const v
                      &ctx->vf_prefill, true, s);
   if (st != MF_OK) return st;
   mf::CompressArgs a;
-  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a)) != MF_OK) return st;
+  if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, bsr, bsr->capacity, a, s)) != MF_OK) return st;
   a.attn_vfrag = ctx->vf_prefill.frag;
   a.attn_vexps = ctx->vf_prefill.exps;
   a.attn_out = O;
@@ -774,7 +860,7 @@ MF_EXPORT mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   if (b.n_brow > 0) {
     mf::CompressArgs a;
     // selection first with room for every causal block, then exact allocation
-    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, 0, a)) != MF_OK) {
+    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, 0, a, s)) != MF_OK) {
       mf_bsr_free(ctx, &b);
       return st;
     }
@@ -791,13 +877,14 @@ MF_EXPORT mf_status mf_compress(mf_ctx* ctx, const void* Q, const void* K, mf_dt
       mf_bsr_free(ctx, &b);
       return hip_fail(e, "reading kept-block count");
     }
-    (void)hipFree(own->data);
+    own->al.give(own->data, own->data_bytes, s);   // the stream is idle: nothing used the empty arrays
     own->data = nullptr;
+    own->data_bytes = 0;
     if ((st = alloc_bsr_data(cnt[0], H_s, B, &b, own)) != MF_OK) {
       mf_bsr_free(ctx, &b);
       return st;
     }
-    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, b.capacity, a)) != MF_OK) {
+    if ((st = prepare_compress_args(ctx, Q, K, dtype, d, tau, &b, b.capacity, a, s)) != MF_OK) {
       mf_bsr_free(ctx, &b);
       return st;
     }
@@ -832,6 +919,7 @@ MF_EXPORT mf_status mf_v_prepare(mf_ctx* ctx, const int32_t* cu, int32_t n_seq, 
 
 MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {
   if (ctx) (void)hipSetDevice(ctx->device);
+  if (vf && vf->_owner) (void)hipDeviceSynchronize();   // no enqueued work may still use it
   vfrag_release(vf);
   return MF_OK;
 }
@@ -981,7 +1069,7 @@ MF_EXPORT mf_status mf_retrieve_layers(mf_ctx* ctx, int32_t n_layers, const mf_b
   }
   mf_status st = set_device(ctx);
   if (st != MF_OK) return st;
-  if ((st = ensure(ctx->den, (size_t)stores[0].T * H_r * 4 + 256, "denominators")) != MF_OK) return st;
+  if ((st = ensure(ctx->al, ctx->den, (size_t)stores[0].T * H_r * 4 + 256, "denominators", static_cast<hipStream_t>(stream))) != MF_OK) return st;
   float* den = static_cast<float*>(ctx->den.p);
   for (int l = 0; l < n_layers; ++l) {
     const int mode = l == 0 ? 1 : (l + 1 < n_layers ? 2 : 3);
@@ -1034,7 +1122,7 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
   if (ctx->dense_cu != g.cu) {
     const size_t o_order = align_up((size_t)g.n_brow * 16, 256);
     const size_t o_pairs = align_up(o_order + (size_t)g.n_brow * 4, 256);
-    if ((st = ensure(ctx->dense_tables, o_pairs + (size_t)g.n_pair * 8 + 256, "dense geometry")) != MF_OK) return st;
+    if ((st = ensure(ctx->al, ctx->dense_tables, o_pairs + (size_t)g.n_pair * 8 + 256, "dense geometry", s)) != MF_OK) return st;
     char* base = static_cast<char*>(ctx->dense_tables.p);
     MF_HIP(hipMemcpy(base, g.info.data(), (size_t)g.n_brow * 16, hipMemcpyHostToDevice), "uploading geometry");
     MF_HIP(hipMemcpy(base + o_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice),
@@ -1066,6 +1154,176 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
   a.hm = hm;
   a.O = O;
   MF_HIP(mf::dense_attention(a, s), "dense attention launch");
+  return MF_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Receiver prefill over every layer: dense recompute of the first R layers and the fused retrieve
+// of the mapped ones, with the compress of later layers' sender maps on a second stream.
+// ------------------------------------------------------------------------------------------
+
+MF_EXPORT mf_status mf_prefill_layers(mf_ctx* ctx, const mf_recv_layer* recv, const mf_send_layer* send,
+                                      mf_dtype dtype, int32_t H_r, int32_t H_kv, int32_t d,
+                                      const int32_t* kvmap, float tau, int32_t n_slots, mf_bsr* slots,
+                                      uint32_t flags, void* stream_main, void* stream_prefetch) {
+  if (!ctx) return fail(MF_ERR_INVALID, "context is NULL");
+  if (ctx->pi.empty()) return fail(MF_ERR_INVALID, "no layer map installed: call mf_map_layers first");
+  if (!recv || !send) return fail(MF_ERR_INVALID, "recv or send is NULL");
+  if (flags & ~(uint32_t)(MF_PREFILL_ISOLATE | MF_PREFILL_TIMING))
+    return fail(MF_ERR_INVALID, "unknown flag bits 0x%x", flags);
+  if (n_slots < 1 || !slots) return fail(MF_ERR_INVALID, "need n_slots >= 1 stores (got %d)", n_slots);
+  mf_status st = check_dtype(dtype);
+  if (st != MF_OK) return st;
+  if (!(tau > 0.f && tau <= 1.f)) return fail(MF_ERR_INVALID, "tau must be in (0, 1] (got %g)", (double)tau);
+  if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+  if (H_kv < 1 || H_kv > 64) return fail(MF_ERR_INVALID, "H_kv must be in [1, 64] (got %d)", H_kv);
+  mf::HeadMap hm;
+  if ((st = build_headmap(kvmap, H_r, H_kv, hm)) != MF_OK) return st;
+
+  // the ring: stores of one geometry, each able to hold every causal block
+  const BsrOwner* o0 = static_cast<const BsrOwner*>(slots[0]._owner);
+  if (!o0) return fail(MF_ERR_INVALID, "slot 0 is not a block store");
+  for (int i = 0; i < n_slots; ++i) {
+    const mf_bsr& b = slots[i];
+    const BsrOwner* o = static_cast<const BsrOwner*>(b._owner);
+    if (!o) return fail(MF_ERR_INVALID, "slot %d is not a block store", i);
+    if (o->cache_owned) return fail(MF_ERR_INVALID, "slot %d is a prefix-cache view (read-only)", i);
+    if (o->geom.ranged) return fail(MF_ERR_INVALID, "slot %d is a row-range store", i);
+    if (b.B != slots[0].B || b.H_s != slots[0].H_s || o->geom.cu != o0->geom.cu)
+      return fail(MF_ERR_INVALID, "slot %d has another geometry than slot 0 (B, H_s or cu_seqlens)", i);
+    if (b.capacity < b.n_causal)
+      return fail(MF_ERR_INVALID, "slot %d holds %lld blocks, fewer than its %lld causal blocks", i,
+                  (long long)b.capacity, (long long)b.n_causal);
+    for (int j = 0; j < i; ++j)
+      if (slots[j].probs == b.probs) return fail(MF_ERR_INVALID, "slots %d and %d are the same store", j, i);
+  }
+  const int B = slots[0].B, H_s = slots[0].H_s;
+  if (!mf::retrieve_supported(B, d, H_r, H_s))
+    return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", B, d, H_r, H_s);
+  const int n_recv = ctx->n_recv, R = ctx->R;
+  const std::vector<int32_t> pi = ctx->pi;
+  std::vector<int> mapped;
+  for (int l = 0; l < n_recv; ++l)
+    if (pi[l] >= 0) mapped.push_back(l);
+  const int n_map = (int)mapped.size();
+  for (int l = 0; l < n_recv; ++l) {
+    const mf_recv_layer& r = recv[l];
+    if (!r.V || !r.O) return fail(MF_ERR_INVALID, "receiver layer %d: V or O is NULL", l);
+    if (!aligned16(r.V)) return fail(MF_ERR_INVALID, "receiver layer %d: V must be 16-byte aligned", l);
+    if (pi[l] < 0) {
+      if (!r.Q || !r.K) return fail(MF_ERR_INVALID, "recomputed receiver layer %d: Q or K is NULL", l);
+      if (!aligned16(r.Q) || !aligned16(r.K))
+        return fail(MF_ERR_INVALID, "recomputed receiver layer %d: Q and K must be 16-byte aligned", l);
+    } else {
+      if (!r.W) return fail(MF_ERR_INVALID, "mapped receiver layer %d: W is NULL", l);
+      if ((st = validate_compress(send[pi[l]].Q, send[pi[l]].K, dtype, d, tau, &slots[0])) != MF_OK) return st;
+    }
+  }
+  if (R > 0 && !mf::dense_supported(dtype_code(dtype), d))
+    return fail(MF_ERR_UNSUPPORTED, "dense attention supports d = 64 or 128 (got %d)", d);
+  if ((st = set_device(ctx)) != MF_OK) return st;
+
+  // events: start, end, then per layer
+  PrefillState& P = ctx->pre;
+  const bool timing = (flags & MF_PREFILL_TIMING) != 0, isolate = (flags & MF_PREFILL_ISOLATE) != 0;
+  int n_ev = 0;
+  auto take = [&n_ev](std::vector<int>& v, int n) {
+    v.resize(n);
+    for (int i = 0; i < n; ++i) v[i] = n_ev++;
+  };
+  P.e_start = n_ev++;
+  P.e_end = n_ev++;
+  take(P.d0, R);
+  take(P.d1, R);
+  take(P.c0, n_map);
+  take(P.c1, n_map);
+  take(P.v0, n_map);
+  take(P.r0, n_map);
+  take(P.r1, n_map);
+  while ((int)P.ev.size() < n_ev) {
+    hipEvent_t e;
+    MF_HIP(hipEventCreate(&e), "hipEventCreate");
+    P.ev.push_back(e);
+  }
+  P.timed = false;
+  P.n_map = n_map;
+  P.R = R;
+  auto E = [&P](int i) { return P.ev[i]; };
+  hipStream_t sa = static_cast<hipStream_t>(stream_main), sb = static_cast<hipStream_t>(stream_prefetch);
+  const int32_t* cu = o0->geom.cu.data();
+  const int n_seq = slots[0].n_seq;
+
+  // both streams start after the caller's earlier work on stream_main
+  MF_HIP(hipEventRecord(E(P.e_start), sa), "hipEventRecord");
+  MF_HIP(hipStreamWaitEvent(sb, E(P.e_start), 0), "hipStreamWaitEvent");
+
+  // compress of the m-th mapped layer into slot m % n_slots, once the retrieve that last read the
+  // slot has finished
+  auto compress = [&](int m) -> mf_status {
+    if (m >= n_slots) MF_HIP(hipStreamWaitEvent(sb, E(P.r1[m - n_slots]), 0), "hipStreamWaitEvent");
+    if (timing) MF_HIP(hipEventRecord(E(P.c0[m]), sb), "hipEventRecord");
+    const mf_send_layer& sl = send[pi[mapped[m]]];
+    const mf_status cs = mf_compress_into(ctx, sl.Q, sl.K, dtype, d, tau, &slots[m % n_slots], sb);
+    if (cs != MF_OK) return cs;
+    MF_HIP(hipEventRecord(E(P.c1[m]), sb), "hipEventRecord");
+    return MF_OK;
+  };
+  int enq = 0;   // compresses enqueued so far
+  for (; enq < std::min(n_slots, n_map); ++enq)
+    if ((st = compress(enq)) != MF_OK) return st;
+  // stream_main recomputes the first R layers meanwhile
+  for (int l = 0; l < R; ++l) {
+    const mf_recv_layer& r = recv[l];
+    if (timing) MF_HIP(hipEventRecord(E(P.d0[l]), sa), "hipEventRecord");
+    if ((st = mf_dense_attention(ctx, r.Q, r.K, r.V, dtype, H_r, H_kv, d, cu, n_seq, kvmap, r.O, sa)) != MF_OK)
+      return st;
+    if (timing) MF_HIP(hipEventRecord(E(P.d1[l]), sa), "hipEventRecord");
+  }
+  for (int m = 0; m < n_map; ++m) {
+    const mf_recv_layer& r = recv[mapped[m]];
+    // isolated: wait for the last compress enqueued so far (the prefetch stream is then idle);
+    // overlapped: wait for this slot's compress only
+    MF_HIP(hipStreamWaitEvent(sa, E(P.c1[isolate ? enq - 1 : m]), 0), "hipStreamWaitEvent");
+    if (timing) MF_HIP(hipEventRecord(E(P.v0[m]), sa), "hipEventRecord");
+    if ((st = vfrag_prepare(ctx, cu, n_seq, B, r.V, dtype, H_kv, d, nullptr, 0, 0, &ctx->vf_pipe, true, sa)) != MF_OK)
+      return st;
+    if (timing) MF_HIP(hipEventRecord(E(P.r0[m]), sa), "hipEventRecord");
+    const mf_vfrag* vfp = &ctx->vf_pipe;
+    const float* W = r.W;
+    float* O = r.O;
+    if ((st = retrieve_launch(ctx, &slots[m % n_slots], 1, &W, &H_r, &vfp, &kvmap, &O, sa)) != MF_OK) return st;
+    MF_HIP(hipEventRecord(E(P.r1[m]), sa), "hipEventRecord");
+    if (enq < n_map) {
+      if ((st = compress(enq)) != MF_OK) return st;
+      ++enq;
+    }
+  }
+  // stream_main's later work follows the last compress as well
+  MF_HIP(hipEventRecord(E(P.e_end), sb), "hipEventRecord");
+  MF_HIP(hipStreamWaitEvent(sa, E(P.e_end), 0), "hipStreamWaitEvent");
+  P.timed = timing;
+  return MF_OK;
+}
+
+MF_EXPORT mf_status mf_prefill_timings(mf_ctx* ctx, float* dense_ms, float* compress_ms, float* vprep_ms,
+                                       float* retrieve_ms) {
+  if (!ctx) return fail(MF_ERR_INVALID, "context is NULL");
+  const PrefillState& P = ctx->pre;
+  if (!P.timed) return fail(MF_ERR_INVALID, "the last mf_prefill_layers call recorded no timing events");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  auto span = [&P](int a, int b, float* out) -> mf_status {
+    MF_HIP(hipEventSynchronize(P.ev[b]), "hipEventSynchronize");
+    MF_HIP(hipEventElapsedTime(out, P.ev[a], P.ev[b]), "hipEventElapsedTime");
+    return MF_OK;
+  };
+  for (int l = 0; l < P.R && dense_ms; ++l)
+    if ((st = span(P.d0[l], P.d1[l], &dense_ms[l])) != MF_OK) return st;
+  for (int m = 0; m < P.n_map; ++m) {
+    if (compress_ms && (st = span(P.c0[m], P.c1[m], &compress_ms[m])) != MF_OK) return st;
+    if (vprep_ms && (st = span(P.v0[m], P.r0[m], &vprep_ms[m])) != MF_OK) return st;
+    if (retrieve_ms && (st = span(P.r0[m], P.r1[m], &retrieve_ms[m])) != MF_OK) return st;
+  }
   return MF_OK;
 }
 

@@ -54,14 +54,61 @@ def _cu(cu_seqlens, T: int):
     return i32_array(cu), len(cu) - 1, cu
 
 
+def _torch_allocator(device: int):
+    """PyTorch's caching allocator as the library's device memory: every buffer the library owns
+    (stores, prepared V, scratch) is taken from and returned to torch's pool."""
+
+    def alloc(nbytes, stream):
+        try:
+            return torch.cuda.caching_allocator_alloc(int(nbytes), device, int(stream or 0))
+        except torch.OutOfMemoryError:
+            return None
+
+    def free(ptr, nbytes, stream):
+        torch.cuda.caching_allocator_delete(int(ptr))
+
+    return alloc, free
+
+
 class Context:
-    """A libmapflow context on one device (owns scratch memory)."""
+    """A libmapflow context on one device (owns scratch memory).
+
+    ``allocator``: ``"torch"`` (the default: PyTorch's caching allocator provides all device
+    memory), ``"hip"`` (hipMalloc / hipFree inside the library), or a pair ``(alloc, free)`` of
+    callables ``alloc(nbytes, stream) -> device pointer or None`` and ``free(ptr, nbytes, stream)``.
+    """
 
     _defaults: dict = {}
 
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, allocator="torch"):
+        if allocator == "hip":
+            fns = None
+        elif allocator == "torch":
+            fns = _torch_allocator(int(device))
+        else:
+            fns = tuple(allocator)
+        if fns is None:
+            a, f = ctypes.cast(None, _lib.ALLOC_FN), ctypes.cast(None, _lib.FREE_FN)
+        else:
+            py_alloc, py_free = fns
+
+            def _a(nbytes, stream, user):
+                try:
+                    p = py_alloc(nbytes, stream)
+                    return int(p) if p else None
+                except Exception:              # an exception must not unwind through C
+                    return None
+
+            def _f(ptr, nbytes, stream, user):
+                try:
+                    py_free(ptr, nbytes, stream)
+                except Exception as e:         # noqa: BLE001 - reported, never propagated into C
+                    print(f"libmapflow free callback failed: {e!r}", flush=True)
+
+            a, f = _lib.ALLOC_FN(_a), _lib.FREE_FN(_f)
+        self._callbacks = (a, f)               # must outlive every store and prepared V
         h = ctypes.c_void_p()
-        check(_L.mf_create(int(device), ctypes.byref(h)))
+        check(_L.mf_create(int(device), a, f, None, ctypes.byref(h)))
         self.handle = h
         self.device = device
 
@@ -290,10 +337,17 @@ class PreparedV:
 # ----------------------------------------------------------------------------------------------
 # entry points
 # ----------------------------------------------------------------------------------------------
-def map_layers(n_recv: int, n_send: int, R: int) -> list[int]:
+def layer_map_uniform(n_recv: int, n_send: int, R: int) -> list[int]:
+    """mf_layer_map_uniform: -1 for the first R layers, then round(l (n_send-1) / (n_recv-1))."""
     out = (ctypes.c_int32 * n_recv)()
-    check(_L.mf_map_layers(int(n_recv), int(n_send), int(R), out))
+    check(_L.mf_layer_map_uniform(int(n_recv), int(n_send), int(R), out))
     return list(out)
+
+
+def map_layers(pi, n_send: int, R: int, ctx=None) -> None:
+    """mf_map_layers: install the layer map ``pi`` (one entry per receiver layer) on the context."""
+    ctx = _ctx(ctx)
+    check(_L.mf_map_layers(ctx.handle, i32_array(pi), len(pi), int(n_send), int(R)))
 
 
 def check_layer_map(pi, n_recv: int, n_send: int, R: int) -> None:
@@ -492,3 +546,48 @@ def read_probe(src: torch.Tensor, sink: torch.Tensor, ctx=None, stream=None) -> 
     if sink.numel() * sink.element_size() < 4:
         raise ValueError("sink needs 4 bytes")
     check(_L.mf_read_probe(ctx.handle, _dev(src, "src"), nbytes, _dev(sink, "sink"), _stream(stream)))
+
+
+def prefill_layers(slots, send, recv, kv_head_map, tau: float, isolate: bool = False, timing: bool = False,
+                   ctx=None, stream_main=None, stream_prefetch=None) -> None:
+    """mf_prefill_layers: one receiver prefill over every layer of the installed layer map.
+
+    ``slots``: list of BlockStore (the ring); ``send``: per sender layer a (Q, K) pair of
+    [H_s, T, d] tensors, or None for layers no receiver layer reuses; ``recv``: per receiver layer
+    a dict with ``v`` and ``o`` [T, H, d] plus ``q``, ``k`` (recomputed layers) or ``w`` [H_r, H_s]
+    (mapped layers).  Work goes on ``stream_main`` (default: the current stream) and
+    ``stream_prefetch`` (required)."""
+    ctx = _ctx(ctx)
+    if stream_prefetch is None:
+        raise ValueError("stream_prefetch is required")
+    rl = (_lib.MfRecvLayer * len(recv))()
+    v0 = None
+    for i, r in enumerate(recv):
+        def ptr(name):
+            t = r.get(name)
+            return None if t is None else _dev(t, f"recv[{i}].{name}")
+        rl[i] = _lib.MfRecvLayer(ptr("q"), ptr("k"), ptr("v"), ptr("w"), ptr("o"))
+        if v0 is None and r.get("v") is not None:
+            v0, o0 = r["v"], r["o"]
+    sl = (_lib.MfSendLayer * len(send))()
+    for i, pair in enumerate(send):
+        if pair is not None:
+            sl[i] = _lib.MfSendLayer(_dev(pair[0], f"send[{i}].Q"), _dev(pair[1], f"send[{i}].K"))
+    arr = (MfBsr * len(slots))(*[st.raw for st in slots])
+    H_kv, d = int(v0.shape[-2]), int(v0.shape[-1])
+    H_r = int(o0.shape[1])
+    flags = (_lib.MF_PREFILL_ISOLATE if isolate else 0) | (_lib.MF_PREFILL_TIMING if timing else 0)
+    check(_L.mf_prefill_layers(ctx.handle, rl, sl, _dtype(v0), H_r, H_kv, d, i32_array(kv_head_map), float(tau),
+                               len(slots), arr, flags, _stream(stream_main), _stream(stream_prefetch)))
+    for st, raw in zip(slots, arr):           # the library may update counts in the copies
+        st.raw.nnzb = raw.nnzb
+
+
+def prefill_timings(n_dense: int, n_map: int, ctx=None) -> dict:
+    """mf_prefill_timings: per-stage milliseconds of the last timed prefill_layers call."""
+    ctx = _ctx(ctx)
+    out = {k: (ctypes.c_float * max(n, 1))() for k, n in
+           (("dense", n_dense), ("compress", n_map), ("vprep", n_map), ("retrieve", n_map))}
+    check(_L.mf_prefill_timings(ctx.handle, out["dense"], out["compress"], out["vprep"], out["retrieve"]))
+    return {"dense": list(out["dense"])[:n_dense], "compress": list(out["compress"])[:n_map],
+            "vprep": list(out["vprep"])[:n_map], "retrieve": list(out["retrieve"])[:n_map]}

@@ -19,7 +19,12 @@
  *     leaves all outputs untouched.  No C++ exception crosses this boundary.
  *   - After a non-OK status, mf_last_error() returns a message for the calling thread.
  *   - A context holds scratch memory: calls on one context that use the same scratch (two
- *     compresses, or two retrieves through mf_retrieve) must be ordered on one stream.
+ *     compresses, or two retrieves through mf_retrieve) must be ordered on one stream.  When a
+ *     call needs more scratch than it holds, it waits for its own stream (only that stream) before
+ *     handing the old buffer back, then takes a larger one.
+ *   - Device memory comes from the allocator given to mf_create (for example PyTorch's caching
+ *     allocator), or from hipMalloc / hipFree when none is given.  Every library-owned device
+ *     buffer (stores, prepared V, context scratch, cache entries) is taken and returned through it.
  */
 #ifndef MAPFLOW_H
 #define MAPFLOW_H
@@ -114,24 +119,49 @@ const char* mf_version(void);
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* mf_last_error(void);
 
-/* Create a context on HIP device `device`; the context keeps per-device scratch memory. */
-mf_status mf_create(int device, mf_ctx** out);
+/*
+ * The caller's device allocator.  alloc returns `bytes` (> 0) of device memory on the context's
+ * device, aligned to at least 256 bytes, for work enqueued on `stream` (a hipStream_t; NULL = the
+ * default stream), or NULL when it cannot; the library then returns MF_ERR_OOM and hands back
+ * everything the failing call had taken.  release returns one pointer alloc gave, with the same
+ * `bytes`; the library calls it only when no work it enqueued still uses the memory (it has
+ * waited for the stream that used it, or for the device).  `user` is passed through unchanged.
+ * Both callbacks run on the thread that called into the library.
+ */
+typedef void* (*mf_alloc_fn)(size_t bytes, void* stream, void* user);
+typedef void (*mf_free_fn)(void* ptr, size_t bytes, void* stream, void* user);
 
-/* Destroy a context and free its scratch memory (after synchronising the device). */
+/*
+ * Create a context on HIP device `device`.  alloc and release are the caller's allocator (both or
+ * neither: NULL, NULL means hipMalloc / hipFree); `user` goes to both.  The context keeps scratch
+ * memory taken from that allocator.  Stores and prepared V created on the context keep a copy of
+ * the allocator, so they may be freed after the context is destroyed (with ctx = NULL).
+ */
+mf_status mf_create(int device, mf_alloc_fn alloc, mf_free_fn release, void* user, mf_ctx** out);
+
+/* Destroy a context and return its scratch memory (after synchronising the device). */
 mf_status mf_destroy(mf_ctx* ctx);
 
 /*
- * Layer map (host only, needs no GPU).  [MapFlow开源, section 不传 KV Cache,改传'注意力关系']:
- * a sender layer's map is assigned to a suitable receiver layer; [Reuses Attention] and
- * [Abstract]: the receiver computes its first layers itself (partial recomputation).
- * Writes pi_out[l] for l in [0, n_recv): -1 for l < R (recomputed densely), otherwise
- * round(l * (n_send - 1) / (n_recv - 1)) with halves rounded up, computed in integers.
- * Requires n_recv >= 1, n_send >= 1, 0 <= R <= n_recv.
+ * Install the layer map that mf_prefill_layers follows (host only: validates and copies).
+ * [MapFlow开源, section 不传 KV Cache,改传'注意力关系']: a sender layer's map is assigned to a
+ * suitable receiver layer; [Reuses Attention] and [Abstract]: the receiver computes its first
+ * layers itself (partial recomputation).  pi_host int32 [n_recv]: pi[l] = -1 exactly for l < R
+ * (receiver layer l is recomputed with dense causal attention), otherwise the sender layer in
+ * [0, n_send) whose compressed map receiver layer l reuses.  MF_ERR_INVALID otherwise (the
+ * context's previous map is kept).
  */
-mf_status mf_map_layers(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out_host);
+mf_status mf_map_layers(mf_ctx* ctx, const int32_t* pi_host, int32_t n_recv, int32_t n_send, int32_t R);
 
 /*
- * Check a caller-supplied layer map: pi[l] == -1 exactly for l < R and 0 <= pi[l] < n_send
+ * A uniform layer map (host only, needs no GPU): pi_out[l] = -1 for l < R, otherwise
+ * round(l * (n_send - 1) / (n_recv - 1)) with halves rounded up, computed in integers (0 when
+ * n_recv = 1).  Requires n_recv >= 1, n_send >= 1, 0 <= R <= n_recv.
+ */
+mf_status mf_layer_map_uniform(int32_t n_recv, int32_t n_send, int32_t R, int32_t* pi_out_host);
+
+/*
+ * Check a layer map without installing it: pi[l] == -1 exactly for l < R and 0 <= pi[l] < n_send
  * otherwise.  Host only.
  */
 mf_status mf_check_layer_map(const int32_t* pi_host, int32_t n_recv, int32_t n_send, int32_t R);
@@ -353,6 +383,80 @@ mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K, const vo
                              mf_dtype dtype, int32_t H_q, int32_t H_kv, int32_t d,
                              const int32_t* cu_seqlens_host, int32_t n_seq,
                              const int32_t* kv_head_map_host, float* O, void* stream);
+
+/*
+ * One receiver prefill over every layer: partial recomputation plus map reuse, with the prefetch
+ * of later layers' blocks overlapped with the recomputation of the first layers.
+ * [Reuses Attention]: the receiver computes its first few layers itself; [MapFlow开源, section
+ * 2. 找得快的:基于前缀哈希的缓存管理]: while those layers compute, the attention blocks that later
+ * layers need are already being loaded asynchronously in the background; [MapFlow开源, section
+ * 3. 算得省的:融合内核执行]: each reused layer runs the fused retrieve.
+ *
+ * The layer map is the one installed by mf_map_layers (n_recv receiver layers, n_send sender
+ * layers, the first R recomputed).  The m-th mapped receiver layer l (in layer order) reuses sender
+ * layer pi[l], compressed into ring slot m % n_slots.  Two streams:
+ *   stream_prefetch  compresses the sender layers of the first n_slots mapped layers, then each
+ *                    later one as soon as the retrieve that last read its slot has finished;
+ *   stream_main      runs dense causal attention for layers 0..R-1 (beside the first
+ *                    compresses), then for each mapped layer waits for its slot's compress,
+ *                    prepares its V (context scratch) and runs the fused retrieve into its O.
+ * HIP events order the two streams; nothing waits on the host.  Both streams start after the work
+ * enqueued on stream_main before the call, and stream_main's later work runs after every launch
+ * of the call (stream_main waits for stream_prefetch's last compress at the end).
+ * flags:
+ *   MF_PREFILL_ISOLATE  each retrieve also waits until stream_prefetch is idle, and each later
+ *                       compress waits for that retrieve, so a retrieve never shares the GPU with
+ *                       a compress (the retrieve's event time is then its kernel time)
+ *   MF_PREFILL_TIMING   record timing events; read them with mf_prefill_timings
+ *
+ *   recv            host array of n_recv entries, in receiver layer order:
+ *                     layers l < R: Q [T][H_r][d], K and V [T][H_kv][d], O fp32 [T][H_r][d];
+ *                     mapped layers: V [T][H_kv][d], W fp32 [H_r][H_s], O fp32 [T][H_r][d]
+ *                     (Q and K unused)
+ *   send            host array of n_send entries: sender queries and keys [H_s][T][d]; only the
+ *                   entries some pi[l] names are read
+ *   dtype           MF_BF16 or MF_F32, for every Q, K and V
+ *   kv_head_map_host int32 [H_r]: KV head of each receiver query head (all layers)
+ *   tau             in (0, 1], as for mf_compress_into
+ *   slots           n_slots >= 1 stores from mf_bsr_create with one geometry (cu_seqlens, B, H_s),
+ *                   not range stores or cache views, each with capacity for every causal block
+ *                   (capacity_blocks < 0), so no compress in the ring can overflow
+ * Every Q, K and V must be 16-byte aligned.  The limits of mf_compress_into, mf_retrieve_prepared
+ * and mf_dense_attention apply.  All arguments are validated before anything is launched.  After
+ * the call the slots hold the last n_slots mapped layers' stores.  Two calls on one context must
+ * not overlap (they share the prepared-V scratch and the events).
+ */
+typedef struct mf_recv_layer {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const float* W;
+  float* O;
+} mf_recv_layer;
+
+typedef struct mf_send_layer {
+  const void* Q;
+  const void* K;
+} mf_send_layer;
+
+enum { MF_PREFILL_ISOLATE = 1, MF_PREFILL_TIMING = 2 };
+mf_status mf_prefill_layers(mf_ctx* ctx, const mf_recv_layer* recv, const mf_send_layer* send,
+                            mf_dtype dtype, int32_t H_r, int32_t H_kv, int32_t d,
+                            const int32_t* kv_head_map_host, float tau, int32_t n_slots,
+                            mf_bsr* slots, uint32_t flags, void* stream_main,
+                            void* stream_prefetch);
+
+/*
+ * Stage times of the last mf_prefill_layers call made with MF_PREFILL_TIMING, in milliseconds
+ * (waits for that call to finish).  Each output may be NULL:
+ *   dense_ms     [R]      dense attention of receiver layers 0..R-1
+ *   compress_ms  [n_map]  compress of the m-th mapped layer's sender layer (stream_prefetch)
+ *   vprep_ms     [n_map]  V preparation of the m-th mapped layer (stream_main)
+ *   retrieve_ms  [n_map]  fused retrieve of the m-th mapped layer (stream_main)
+ * n_map = n_recv - R of the installed layer map.  MF_ERR_INVALID if no timed call was made.
+ */
+mf_status mf_prefill_timings(mf_ctx* ctx, float* dense_ms_host, float* compress_ms_host,
+                             float* vprep_ms_host, float* retrieve_ms_host);
 
 /*
  * Prefix-hash cache of compressed sender state.  [MapFlow开源, section 找得快的:基于前缀哈希的缓存管理]

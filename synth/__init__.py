@@ -16,6 +16,8 @@ from .workloads import (  # noqa: F401
     make_layer_inputs,
     make_layer_inputs_torch,
     make_page_table,
+    make_receiver_inputs_torch,
+    make_sender_inputs_torch,
     make_lengths,
     page_v,
     rng_for,

@@ -236,8 +236,8 @@ def _torch_gen(seed: int, layer: int, tensor: str, device):
     return g
 
 
-def make_layer_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
-    """Q_s, K_s [H_s, T, d], V_r [T, H_kv, d] (input dtype) and W [H_r, H_s] fp32 on ``device``."""
+def make_sender_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
+    """Q_s, K_s [H_s, T, d] (input dtype) of one sender layer on ``device``."""
     import torch
     lengths = make_lengths(wl, seed, lengths)
     cu = cu_seqlens_of(lengths)
@@ -262,12 +262,30 @@ def make_layer_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths
     k[:, hot, :] += boost
     k_out = k.to(dt)
     del k
-    v = torch.randn((T, wl.H_kv, d), generator=_torch_gen(seed, layer, "v_r", device), device=device).to(dt)
-    w = torch.from_numpy(rng_for(seed, layer, "w").dirichlet(np.full(H_s, 0.5), size=wl.H_r)
+    return {"q_s": q_out, "k_s": k_out, "cu_seqlens": cu, "lengths": lengths, "T": T}
+
+
+def make_receiver_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
+    """W [H_r, H_s] fp32 and V_r [T, H_kv, d] (input dtype) of one mapped receiver layer."""
+    import torch
+    lengths = make_lengths(wl, seed, lengths)
+    cu = cu_seqlens_of(lengths)
+    T = int(cu[-1])
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    v = torch.randn((T, wl.H_kv, wl.d), generator=_torch_gen(seed, layer, "v_r", device), device=device).to(dt)
+    w = torch.from_numpy(rng_for(seed, layer, "w").dirichlet(np.full(wl.H_s, 0.5), size=wl.H_r)
                          .astype(np.float32)).to(device)
     group = max(wl.H_r // wl.H_kv, 1)
-    return {"q_s": q_out, "k_s": k_out, "v_r": v, "w": w, "cu_seqlens": cu, "lengths": lengths,
-            "kv_head_map": [min(g // group, wl.H_kv - 1) for g in range(wl.H_r)], "T": T}
+    return {"w": w, "v_r": v, "cu_seqlens": cu, "lengths": lengths, "T": T,
+            "kv_head_map": [min(g // group, wl.H_kv - 1) for g in range(wl.H_r)]}
+
+
+def make_layer_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:
+    """Q_s, K_s [H_s, T, d], V_r [T, H_kv, d] (input dtype) and W [H_r, H_s] fp32 on ``device``:
+    one sender layer and its receiver layer drawn with the same layer index."""
+    out = make_sender_inputs_torch(wl, seed, layer, device, lengths)
+    out.update(make_receiver_inputs_torch(wl, seed, layer, device, lengths))
+    return out
 
 
 def make_dense_inputs_torch(wl: Workload, seed: int, layer: int, device, lengths=None) -> dict:

@@ -104,3 +104,25 @@ def brow_table(cu, B):
         n = int(cu[s + 1] - cu[s])
         rows += [(s, I) for I in range((n + B - 1) // B)]
     return rows
+
+
+def gpu_store_for_oracle(host: dict, cu, B: int, H_s: int):
+    """The GPU's downloaded store (``BlockStore.to_host()``) as an ``oracle.OracleBSR``, so that
+    ``oracle.retrieve`` runs on exactly the kept blocks and bf16 probabilities the GPU stored."""
+    table = brow_table(cu, B)
+    return oracle.OracleBSR(
+        B=B, H_s=H_s, cu_seqlens=np.asarray(cu), brow_seq=np.array([s for s, _ in table], dtype=np.int64),
+        brow_I=np.array([I for _, I in table], dtype=np.int64), block_ptr=host["block_ptr"],
+        block_idx=host["block_idx"], probs=host["probs"], row_kept_mass=host["row_kept_mass"],
+        lse=None, rows=[])
+
+
+def check_selection(host: dict, ref, tau: float, B: int) -> int:
+    """Every block row's kept set against the oracle's (tie rule); returns the excused rows."""
+    excused = 0
+    for b in range(len(host["block_ptr"]) - 1):
+        got = host["block_idx"][host["block_ptr"][b]:host["block_ptr"][b + 1]].tolist()
+        ok, why = sets_agree(got, ref.rows[b], tau)
+        assert ok, f"block row {b}: {why}; gpu {got} oracle {ref.rows[b]['kept']}"
+        excused += bool(why)
+    return excused

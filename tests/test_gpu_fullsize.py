@@ -35,10 +35,15 @@ def mf():
 
 
 def _golden(workload, seed):
+    """The oracle's stored selection for (workload, seed); every full-size workload has one, so a
+    missing file or seed fails the test instead of skipping the all-row check."""
     path = os.path.join(GOLDEN, f"{workload}_selection.json")
     if not os.path.exists(path):
-        return None
-    return json.load(open(path))["seeds"].get(str(seed))
+        pytest.fail(f"missing {path}: run tests/golden/make_selection_golden.py --workload {workload}")
+    gold = json.load(open(path))["seeds"].get(str(seed))
+    if gold is None:
+        pytest.fail(f"{path} has no entry for seed {seed}")
+    return gold
 
 
 def _check_all_rows(store, meta, gold):
@@ -135,8 +140,7 @@ def test_pair_8b3b_L8192(mf, seed):
     tau = float(np.float32(wl.tau))
     say(f"case: full-size {wl.name} seed {seed} T={x['T']}")
     store, meta, O = _layer(mf, x, tau, wl.B)
-    if gold is not None:
-        _check_all_rows(store, meta, gold)
+    _check_all_rows(store, meta, gold)
     _check_rows(store, meta, x, tau, wl.B, _sample_rows(x["cu_seqlens"], wl.B, [0]), O, x["v_r"])
 
 
@@ -148,8 +152,7 @@ def test_full_8b3b_L32768_layer(mf):
     say(f"case: full-size {wl.name} seed 0 T={x['T']}")
     store, meta, O = _layer(mf, x, tau, wl.B)
     say(f"  nnzb {meta['nnzb']}")
-    if gold is not None:
-        _check_all_rows(store, meta, gold)
+    _check_all_rows(store, meta, gold)
     _check_rows(store, meta, x, tau, wl.B, [0, 1, 300, 511], O, x["v_r"])
 
 
@@ -164,8 +167,7 @@ def test_varlen_14b8b_paged(mf):
     say(f"case: full-size {wl.name} seed 0 T={x['T']} lengths={lengths}")
     store, meta, O = _layer(mf, x, tau, wl.B, exact_alloc=True, page_table=table, pool=pool)
     say(f"  nnzb {meta['nnzb']}")
-    if gold is not None:
-        _check_all_rows(store, meta, gold)
+    _check_all_rows(store, meta, gold)
     order = np.argsort(lengths)
     seqs = [int(order[0]), int(order[-1])]
     sample = _sample_rows(x["cu_seqlens"], wl.B, seqs)
@@ -176,8 +178,6 @@ def test_varlen_14b8b_paged(mf):
 def test_long_L131072(mf, seed):
     wl = synth.WORKLOADS["long_131k"]
     gold = _golden(wl.name, seed)
-    if gold is None:
-        pytest.skip("no oracle-tuned tau for this seed under tests/golden/")
     x = synth.make_layer_inputs(wl, seed)
     tau = float(gold["tau"])
     say(f"case: full-size {wl.name} seed {seed} T={x['T']} tau={tau:.7g}")

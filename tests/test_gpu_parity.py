@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import synth
-from parity import (assert_out_close, brow_table, dense_maps, say, sets_agree, to_dev, ulp_bf16)
+from parity import (assert_out_close, brow_table, check_selection, dense_maps, gpu_store_for_oracle, say,
+                    sets_agree, to_dev, ulp_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -299,11 +300,13 @@ def test_end_to_end_and_determinism(mf):
     for key in ["block_ptr", "block_idx", "probs_bits", "row_kept_mass"]:
         assert np.array_equal(h1[key], h2[key]), key
     assert torch.equal(O1, O2)
+    # every row's kept set against the oracle's (tie rule), then the output against the oracle run
+    # on the GPU's own stored blocks, whether or not some row was a tie
     ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B)
-    if np.array_equal(h1["block_idx"], ref.block_idx):
-        assert_out_close(O1.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], x["kv_head_map"]), "end-to-end O_r")
-    else:
-        say("  kept sets differ at ties; end-to-end output not compared")
+    ex = check_selection(h1, ref, tau, wl.B)
+    gs = gpu_store_for_oracle(h1, x["cu_seqlens"], wl.B, x["H_s"])
+    assert_out_close(O1.cpu().numpy(), oracle.retrieve(gs, x["w"], x["v_r"], x["kv_head_map"]),
+                     f"end-to-end O_r ({ex} tie rows)")
 
 
 def test_compress_into_capacity(mf):

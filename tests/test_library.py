@@ -42,7 +42,7 @@ def test_version(lib):
                                              (36, 28, 0), (7, 2, 1), (4, 4, 4)])
 def test_map_layers_matches_oracle(lib, n_recv, n_send, R):
     out = (ctypes.c_int32 * n_recv)()
-    assert lib.mf_map_layers(n_recv, n_send, R, out) == _lib.MF_OK
+    assert lib.mf_layer_map_uniform(n_recv, n_send, R, out) == _lib.MF_OK
     assert list(out) == oracle.layer_map(n_recv, n_send, R)
     assert lib.mf_check_layer_map(out, n_recv, n_send, R) == _lib.MF_OK
 
@@ -53,8 +53,27 @@ def test_check_layer_map_rejects(lib):
     assert "outside" in lib.mf_last_error().decode()
     bad2 = _lib.i32_array([0, 1, 2])
     assert lib.mf_check_layer_map(bad2, 3, 5, 1) == _lib.MF_ERR_INVALID         # layer 0 < R
-    assert lib.mf_map_layers(3, 5, 4, (ctypes.c_int32 * 3)()) == _lib.MF_ERR_INVALID
-    assert lib.mf_map_layers(0, 5, 0, (ctypes.c_int32 * 1)()) == _lib.MF_ERR_INVALID
+    assert lib.mf_layer_map_uniform(3, 5, 4, (ctypes.c_int32 * 3)()) == _lib.MF_ERR_INVALID
+    assert lib.mf_layer_map_uniform(0, 5, 0, (ctypes.c_int32 * 1)()) == _lib.MF_ERR_INVALID
+    # installing a map needs a context, and the map is checked first
+    good = _lib.i32_array([-1, 0, 4])
+    assert lib.mf_map_layers(None, good, 3, 5, 1) == _lib.MF_ERR_INVALID
+    assert "context" in lib.mf_last_error().decode()
+
+
+def test_allocator_callbacks_come_in_pairs(lib):
+    # one callback without the other is an argument error, checked before any device query
+    h = ctypes.c_void_p()
+    a = _lib.ALLOC_FN(lambda n, s, u: None)
+    assert lib.mf_create(0, a, ctypes.cast(None, _lib.FREE_FN), None, ctypes.byref(h)) == _lib.MF_ERR_INVALID
+    assert "both" in lib.mf_last_error().decode()
+    assert not h.value
+
+
+def test_prefill_layers_rejects_before_any_gpu_work(lib):
+    assert lib.mf_prefill_layers(None, None, None, 1, 8, 8, 128, None, 0.9, 1, None, 0, None, None) == \
+        _lib.MF_ERR_INVALID
+    assert lib.mf_prefill_timings(None, None, None, None, None) == _lib.MF_ERR_INVALID
 
 
 def test_invalid_arguments_rejected_before_any_gpu_work(lib):
