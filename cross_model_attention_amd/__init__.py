@@ -26,6 +26,7 @@ from .mapflow import (  # noqa: F401
     retrieve,
     retrieve_layers,
     retrieve_multi,
+    retrieve_noalloc,
     retrieve_prepared,
     v_prepare,
     version,

@@ -85,6 +85,8 @@ _SIGNATURES = {
                                   POINTER(POINTER(MfVfrag)), POINTER(_P_I32), POINTER(c_void_p), c_void_p]),
     "mf_retrieve": (c_int, [c_void_p, POINTER(MfBsr), c_void_p, c_int32, c_void_p, c_int, c_int32,
                             c_int32, c_void_p, c_int32, c_int32, _P_I32, c_void_p, c_void_p]),
+    "mf_retrieve_noalloc": (c_int, [c_void_p, POINTER(MfBsr), c_void_p, c_int32, c_void_p, c_int, c_int32,
+                                    c_int32, c_void_p, c_int32, c_int32, _P_I32, c_void_p, c_void_p]),
     "mf_dense_attention": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int32, c_int32,
                                    c_int32, _P_I32, c_int32, _P_I32, c_void_p, c_void_p]),
     "mf_prefill_layers": (c_int, [c_void_p, POINTER(MfRecvLayer), POINTER(MfSendLayer), c_int, c_int32, c_int32,

@@ -9,6 +9,7 @@
 #include <cstring>
 #include <new>
 #include <memory>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -926,10 +927,11 @@ MF_EXPORT mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf) {
 
 // One launch for n_recv receivers of the same store: every receiver's head parts are splits of
 // one row-tile work item, so each stored probability tile is read from HBM once for all of them.
+// vf_from_store: the prepared V was laid out on the store's own geometry tables (it has no owner)
 static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, const float* const* W,
                                  const int32_t* H_r, const mf_vfrag* const* vf,
                                  const int32_t* const* kvmap, float* const* O, void* stream,
-                                 int accumulate = 0, float* den = nullptr) {
+                                 int accumulate = 0, float* den = nullptr, bool vf_from_store = false) {
   if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
   if (n_recv < 1 || n_recv > mf::kMaxRecv)
     return fail(MF_ERR_INVALID, "n_recv = %d outside [1, %d]", n_recv, mf::kMaxRecv);
@@ -939,7 +941,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   mf::HeadMap hm[mf::kMaxRecv];
   for (int r = 0; r < n_recv; ++r) {
     const mf_vfrag* v = vf[r];
-    if (!v || !v->_owner) return fail(MF_ERR_INVALID, "prepared V of receiver %d is NULL", r);
+    if (!v || !(v->_owner || vf_from_store)) return fail(MF_ERR_INVALID, "prepared V of receiver %d is NULL", r);
     if (!W[r] || !O[r]) return fail(MF_ERR_INVALID, "W or O of receiver %d is NULL", r);
     if (H_r[r] < 1) return fail(MF_ERR_INVALID, "H_r of receiver %d must be >= 1", r);
     if (v->B != bsr->B || v->n_brow != bsr->n_brow || v->T != bsr->T)
@@ -947,7 +949,7 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
                   "differs from the store's (B=%d, %d, T=%lld)", r, v->B, v->n_brow, (long long)v->T,
                   bsr->B, bsr->n_brow, (long long)bsr->T);
     const VfragOwner* vo = static_cast<const VfragOwner*>(v->_owner);
-    if (vo->geom.cu != bo->geom.cu)
+    if (!vf_from_store && vo->geom.cu != bo->geom.cu)
       return fail(MF_ERR_INVALID, "prepared V of receiver %d has different cu_seqlens", r);
     if (v->d != vf[0]->d)
       return fail(MF_ERR_INVALID, "receiver %d has head dim %d, receiver 0 has %d", r, v->d, vf[0]->d);
@@ -1546,6 +1548,105 @@ MF_EXPORT mf_status mf_cache_lookup(mf_cache* cache, int32_t layer, const int32_
     return MF_OK;
   }
   return MF_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// Retrieve without any device allocation: the prepared V lives in a fixed device array.
+// ------------------------------------------------------------------------------------------
+
+}  // extern "C"
+
+namespace {
+
+// Prepared-V tiles (up to kNoAllocFragBytes) followed by the per-KV-head exponents and maxima.
+constexpr size_t kNoAllocFragBytes = size_t(64) << 20;
+constexpr size_t kNoAllocBytes = kNoAllocFragBytes + 4096;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+// Device address of `scratch` on each device, looked up once per device.  In host code the
+// array's name is only a stand-in for the symbol; kernels get this address instead.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+mf_status scratch_address(int device, void** out) {
+  if (device < 0 || device >= kMaxDevices) return fail(MF_ERR_UNSUPPORTED, "device %d beyond %d", device, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[device]) {
+    void* p = nullptr;
+    MF_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    g_scratch_addr[device] = p;
+  }
+  *out = g_scratch_addr[device];
+  return MF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+MF_EXPORT mf_status mf_retrieve_noalloc(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r,
+                                        const void* V, mf_dtype vdtype, int32_t H_kv, int32_t d,
+                                        const int32_t* page_table, int32_t page_size, int32_t pages_per_seq,
+                                        const int32_t* kvmap, float* O, void* stream) {
+  if (!bsr || !bsr->_owner) return fail(MF_ERR_INVALID, "block store is NULL");
+  if (!W || !O) return fail(MF_ERR_INVALID, "W or O is NULL");
+  if (!V) return fail(MF_ERR_INVALID, "V is NULL");
+  if (!aligned16(V)) return fail(MF_ERR_INVALID, "V must be 16-byte aligned");
+  mf_status st = check_dtype(vdtype);
+  if (st != MF_OK) return st;
+  if (d != 64 && d != 128) return fail(MF_ERR_UNSUPPORTED, "head dim d must be 64 or 128 (got %d)", d);
+  if (H_kv < 1 || H_kv > 64) return fail(MF_ERR_INVALID, "H_kv must be in [1, 64] (got %d)", H_kv);
+  if (!mf::retrieve_supported(bsr->B, d, H_r, bsr->H_s))
+    return fail(MF_ERR_UNSUPPORTED, "no retrieve kernel for B=%d d=%d H_r=%d H_s=%d", bsr->B, d, H_r, bsr->H_s);
+  mf::HeadMap hm;
+  if ((st = build_headmap(kvmap, H_r, H_kv, hm)) != MF_OK) return st;
+  const BsrOwner* bo = static_cast<const BsrOwner*>(bsr->_owner);
+  const Geometry& g = bo->geom;
+  if (page_table) {
+    if (page_size < 1 || pages_per_seq < 1)
+      return fail(MF_ERR_INVALID, "paged V needs page_size >= 1 and pages_per_seq >= 1");
+    for (int s = 0; s < bsr->n_seq; ++s)
+      if ((int64_t)(g.cu[s + 1] - g.cu[s]) > (int64_t)page_size * pages_per_seq)
+        return fail(MF_ERR_INVALID, "sequence %d needs more than pages_per_seq pages", s);
+  }
+  const size_t frag_bytes = (size_t)H_kv * bsr->n_brow * bsr->B * d * 2;
+  if (frag_bytes > kNoAllocFragBytes)
+    return fail(MF_ERR_UNSUPPORTED, "prepared V needs %zu bytes, more than the %zu-byte fixed scratch "
+                "(H_kv x block rows x B x d fp16 values)", frag_bytes, kNoAllocFragBytes);
+  if ((st = set_device(ctx)) != MF_OK) return st;
+  if (bsr->n_brow == 0 || bsr->n_order == 0) return MF_OK;
+  void* base = nullptr;
+  if ((st = scratch_address(ctx->device, &base)) != MF_OK) return st;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mf_vfrag vf{};
+  vf.B = bsr->B;
+  vf.d = d;
+  vf.H_kv = H_kv;
+  vf.n_brow = bsr->n_brow;
+  vf.T = bsr->T;
+  vf.frag = reinterpret_cast<uint16_t*>(p);
+  vf.exps = reinterpret_cast<int32_t*>(p + kNoAllocFragBytes);
+  mf::VprepArgs va{};
+  va.V = V;
+  va.dtype = dtype_code(vdtype);
+  va.H_kv = H_kv;
+  va.d = d;
+  va.B = bsr->B;
+  va.T = bsr->T;
+  va.n_brow = bsr->n_brow;
+  va.info = bsr->brow_info;            // the store's geometry tables, already on the device
+  va.brow_seq = bo->brow_seq;
+  va.page_table = page_table;
+  va.page_size = page_size;
+  va.pages_per_seq = pages_per_seq;
+  va.vmax_bits = reinterpret_cast<uint32_t*>(p + kNoAllocFragBytes + 1024);   // cleared by a kernel first
+  va.frag = vf.frag;
+  va.exps = vf.exps;
+  MF_HIP(mf::v_prepare(va, s), "V preparation launch");
+  const mf_vfrag* vfp = &vf;
+  return retrieve_launch(ctx, bsr, 1, &W, &H_r, &vfp, &kvmap, &O, stream, 0, nullptr, true);
 }
 
 MF_EXPORT mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_t bytes, void* stream) {

@@ -516,6 +516,22 @@ def retrieve(store: BlockStore, W: torch.Tensor, V: torch.Tensor, kv_head_map, p
     return out
 
 
+def retrieve_noalloc(store: BlockStore, W: torch.Tensor, V: torch.Tensor, kv_head_map, page_table=None,
+                     page_size: int = 16, out=None, stream=None) -> torch.Tensor:
+    """mf_retrieve_noalloc: mf_retrieve with the prepared V in the library's fixed device array (no
+    device allocation inside the call).  ``out`` should be given by callers that must not allocate."""
+    H_r = int(W.shape[0])
+    if W.dtype != torch.float32 or W.shape[1] != store.raw.H_s:
+        raise ValueError("W must be float32 [H_r, H_s]")
+    H_kv, d = int(V.shape[-2]), int(V.shape[-1])
+    out = _out(out, store.raw.T, H_r, d, W)
+    pt, ps, pps = _paged(page_table, page_size)
+    check(_L.mf_retrieve_noalloc(store.ctx.handle, ctypes.byref(store.raw), _dev(W, "W"), H_r, _dev(V, "V"),
+                                 _dtype(V), H_kv, d, pt, ps, pps, i32_array(kv_head_map), _dev(out, "out"),
+                                 _stream(stream)))
+    return out
+
+
 def dense_attention(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, kv_head_map, cu_seqlens=None,
                     out=None, ctx=None, stream=None) -> torch.Tensor:
     """mf_dense_attention: causal softmax attention, Q [T, H_q, d], K/V [T, H_kv, d] -> fp32 O."""

@@ -373,6 +373,24 @@ mf_status mf_retrieve(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_
                       float* O, void* stream);
 
 /*
+ * mf_retrieve without any device allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, result and error codes as mf_retrieve, bit for bit.  The prepared V goes into
+ * a fixed device array of the library (64 MiB + 4 KiB per device, held until the process ends)
+ * instead of context scratch, and the geometry tables come from the store itself; no hipMalloc,
+ * hipFree or allocator callback is called.  Limit: H_kv * n_brow * B * d <= 2^25 fp16 values
+ * (e.g. 32768 tokens of one sequence with 8 KV heads at d = 128), else MF_ERR_UNSUPPORTED before
+ * anything is launched.  Every call on a device shares that device's array and overwrites what
+ * the previous call left there (the per-head maxima are cleared by a kernel at the start of each
+ * call): two calls that overlap on one device, on any streams or contexts, race and give wrong
+ * outputs.  Order them on one stream.
+ */
+mf_status mf_retrieve_noalloc(mf_ctx* ctx, const mf_bsr* bsr, const float* W, int32_t H_r, const void* V,
+                              mf_dtype vdtype, int32_t H_kv, int32_t d, const int32_t* page_table,
+                              int32_t page_size, int32_t pages_per_seq, const int32_t* kv_head_map_host,
+                              float* O, void* stream);
+
+/*
  * Dense causal attention for the receiver layers that are recomputed ([Reuses Attention]:
  * the receiver computes its first layers normally).  O[i,g,:] = softmax_j<=i(q.k / sqrt(d)) V
  * per sequence, query head g reading KV head kv_head_map_host[g].
