@@ -32,6 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+RETRIEVE_SRC = os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip")
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -59,6 +60,9 @@ def parse():
                         "share the GPU with later compresses (reported under 'overlap')")
     p.add_argument("--read-probe-bytes", type=int, default=4 << 30,
                    help="size of the HBM read probe run after the timed steps (0 = skip)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the single-layer measurements of the other workloads (8B->3B at L=8192, "
+                        "the 14B->8B varlen batch with paged V, L=131072 at ~5%% density)")
     return p.parse_args()
 
 
@@ -77,13 +81,15 @@ def retrieve_flops(nnzb, H_s, H_r, B, d):
     return nnzb * (2 * H_r * H_s * B * B + 2 * H_r * B * B * d)
 
 
-def traffic_from_profile(kernel_src):
-    """Measured HBM bytes per retrieve launch from the committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+def traffic_from_profile(kernel_src, workload):
+    """Measured HBM bytes per retrieve launch of ``workload`` from the committed counter summary,
+    if it was taken on the current kernel source (else None)."""
     path = os.path.join(ROOT, "profiles", "retrieve_traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = json.load(open(path)).get(workload)
+    if rec is None:
+        return None
     src = open(kernel_src, "rb").read()
     if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
         return None
@@ -283,6 +289,161 @@ def prefix_reuse(mf, torch, wl, args, send, recv, kv_map, tau, ctx, dev):
     return res
 
 
+def _paged_pool_torch(torch, V, lengths, table, page_size, n_pages):
+    """Scatter contiguous V [T, H_kv, d] into a page pool [n_pages, page_size, H_kv, d] on the device,
+    following the page table (the layout synth.page_v builds on the host)."""
+    idx = np.empty(V.shape[0], np.int64)
+    tok = 0
+    for s, n in enumerate(lengths):
+        loc = np.arange(n)
+        idx[tok:tok + n] = table[s, loc // page_size].astype(np.int64) * page_size + loc % page_size
+        tok += n
+    pool = torch.zeros((n_pages * page_size,) + tuple(V.shape[1:]), dtype=V.dtype, device=V.device)
+    pool[torch.from_numpy(idx).to(V.device)] = V
+    return pool.view(n_pages, page_size, *V.shape[1:])
+
+
+def oracle_rows(wl, seed, picks, tau):
+    """The oracle (compress + retrieve of one block row) on sampled block rows of a workload.
+
+    picks: list of (sequence length n, block row I).  The inputs of a row are drawn with the
+    workload's recipe (planted keys, Dirichlet W, N(0,1) V) at the row's own shape: its queries
+    and every key up to the end of the row, per head, so that the oracle's work equals that of
+    the same row of the full workload.  Returns (seconds, work units = sum of I + 1)."""
+    import oracle
+
+    H_s, d, B = wl.H_s, wl.d, wl.B
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7777]))
+    a = 0.75 * math.sqrt(d)
+    kv = np.array([g // (wl.H_r // wl.H_kv) for g in range(wl.H_r)], dtype=np.int32)
+    W = rng.dirichlet(np.full(H_s, 0.5), size=wl.H_r)
+    seconds, units = 0.0, 0
+    for n in sorted({n for n, _ in picks}):
+        rows_here = [I for m, I in picks if m == n]
+        r1max = min(n, (max(rows_here) + 1) * B)
+        u = rng.standard_normal((H_s, d))
+        u /= np.linalg.norm(u, axis=1, keepdims=True)
+        K = rng.standard_normal((H_s, r1max, d), dtype=np.float32)
+        hot = np.concatenate([[0], rng.choice(np.arange(1, max(r1max, 2)), size=int(round(wl.hot_frac * r1max)),
+                                              replace=False)])
+        K[:, hot, :] += (a * u[:, None, :]).astype(np.float32)
+        Q = np.zeros_like(K)
+        V = rng.standard_normal((r1max, wl.H_kv, d), dtype=np.float32)
+        for I in rows_here:
+            r0, r1 = I * B, min(n, (I + 1) * B)
+            Q[:, r0:r1] = rng.standard_normal((H_s, r1 - r0, d), dtype=np.float32) + (a * u[:, None, :])
+        t0 = time.perf_counter()
+        for I in rows_here:
+            r = oracle.block_row_compress(Q, K, 0, min(n, r1max), I, B, tau)
+            oracle.retrieve_block_row(r["probs"], B, r["rows"], r["tok0"], 0, 0, min(n, r1max), W, V, kv)
+            units += I + 1
+        seconds += time.perf_counter() - t0
+    return seconds, units
+
+
+def bench_single(mf, torch, wl, args, ctx, dev, read_gbs=None, reps=10):
+    """One sender layer mapped to one receiver layer of a single-layer workload, at its full size:
+    compress (exact-size store), V preparation (paged where the workload pages V) and the fused
+    retrieve, each timed per launch with HIP events on the stream it runs on; plus the oracle on
+    sampled block rows, extrapolated by per-row work."""
+    seed = args.seed
+    lengths = synth_mod().make_lengths(wl, seed)
+    cu = synth_mod().cu_seqlens_of(lengths)
+    T, B = int(cu[-1]), wl.B
+    if wl.tau is None:
+        gold = json.load(open(os.path.join(ROOT, "tests", "golden", f"{wl.name}_selection.json")))
+        tau = float(gold["seeds"][str(seed)]["tau"])       # tuned on the oracle's masses for this seed
+    else:
+        tau = float(np.float32(wl.tau))
+    x = synth_mod().make_sender_inputs_torch(wl, seed, 0, dev)
+    r = synth_mod().make_receiver_inputs_torch(wl, seed, 0, dev)
+    Q, K, W, V = x["q_s"], x["k_s"], r["w"], r["v_r"]
+    kv_map = r["kv_head_map"]
+    store = mf.compress(Q, K, tau, B, cu_seqlens=cu, ctx=ctx)
+    nnzb, n_causal, n_brow = int(store.raw.nnzb), int(store.raw.n_causal), int(store.raw.n_brow)
+    pt, Vin = None, V
+    if wl.paged:
+        table, n_pages = synth_mod().make_page_table(lengths, wl.page_size, seed=seed)
+        Vin = _paged_pool_torch(torch, V, lengths, table, wl.page_size, n_pages)
+        pt = torch.from_numpy(table).to(dev)
+        del V
+    pv = mf.v_prepare(Vin, B, cu, page_table=pt, page_size=wl.page_size, ctx=ctx)
+    O = torch.empty((T, wl.H_r, wl.d), dtype=torch.float32, device=dev)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    t_ret = timed(lambda: mf.retrieve_prepared(store, W, pv, kv_map, out=O), reps)
+    t_vp = timed(lambda: mf.v_prepare(Vin, B, cu, page_table=pt, page_size=wl.page_size, out=pv), 3)
+    t_cp = timed(lambda: mf.compress_into(store, Q, K, tau), 3)
+    assert store.sync() == nnzb, "kept-block count changed between compresses"
+    ms = float(np.mean(t_ret))
+    nbytes = retrieve_bytes(nnzb, wl.H_s, B, n_brow, T, wl.H_kv, wl.H_r, wl.d)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cp_ms = float(np.mean(t_cp))
+    cp_flops = (n_causal + nnzb) * 2 * wl.H_s * B * B * wl.d
+    res = {
+        "workload": wl.name, "tokens": T, "sequences": len(lengths), "tau": tau,
+        "heads": f"{wl.H_s} -> {wl.H_r}q/{wl.H_kv}kv", "paged_v": bool(wl.paged),
+        "kept_blocks": nnzb, "causal_blocks": n_causal, "density": nnzb / n_causal,
+        "retrieve": {"ms": ms, "ms_median": float(np.median(t_ret)), "launches": len(t_ret),
+                     "tokens_per_s": T / (ms * 1e-3), "algorithmic_GB": nbytes / 1e9, "GB_per_s": gbs,
+                     "frac_hbm_peak": gbs / HBM_PEAK_GBS,
+                     "frac_read_ceiling": gbs / read_gbs if read_gbs else None,
+                     "mfma_TFLOPs": retrieve_flops(nnzb, wl.H_s, wl.H_r, B, wl.d) / (ms * 1e-3) / 1e12,
+                     "traffic_GB": (lambda t: None if t is None else t / 1e9)(traffic_from_profile(RETRIEVE_SRC, wl.name))},
+        "compress": {"ms": cp_ms, "tokens_per_s": T / (cp_ms * 1e-3),
+                     "mfma_TFLOPs": cp_flops / (cp_ms * 1e-3) / 1e12,
+                     "store_GB": nnzb * wl.H_s * B * B * 2 / 1e9},
+        "v_prepare_ms": float(np.mean(t_vp)),
+    }
+    log(f"{wl.name}: T={T} nnzb={nnzb} density {nnzb / n_causal:.4f}; retrieve {ms:.3f} ms "
+        f"({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of peak); compress {cp_ms:.2f} ms; V prep {res['v_prepare_ms']:.3f} ms")
+    del store, pv, O, Q, K, Vin, x, r
+    if not args.no_cpu_baseline:
+        nb = [(n + B - 1) // B for n in lengths]
+        if len(lengths) == 1 and nb[0] > 512:
+            # long rows cost up to seconds each: a bounded spread over the first half
+            picks = [(lengths[0], I) for I in sorted({0, nb[0] // 8, nb[0] // 4, nb[0] // 2})]
+        elif len(lengths) == 1:
+            picks = [(lengths[0], I) for I in sorted({0, nb[0] // 4, nb[0] // 2, (3 * nb[0]) // 4, nb[0] - 1})]
+        else:
+            order = np.argsort(lengths)
+            picks = []
+            for s in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
+                picks += [(lengths[s], I) for I in sorted({0, nb[s] // 2, nb[s] - 1})]
+        sec, units = oracle_rows(wl, seed, picks, tau)
+        total_units = sum(b * (b + 1) // 2 for b in nb)
+        est = sec * total_units / units
+        res["cpu_baseline"] = {
+            "value": T / est, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, compress + retrieve of {len(picks)} block rows (sequence length, row) "
+                       f"{picks} ({units} row-block units, {sec:.1f} s), extrapolated by per-row work to all "
+                       f"{total_units} units of the layer (est. {est:.0f} s)"),
+            "extrapolated": True}
+        log(f"{wl.name}: oracle sample {sec:.1f} s, est. {est:.0f} s per layer")
+    return res
+
+
+def _blas_threads():
+    import threadpoolctl
+    return int(sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                   if i.get("user_api") == "blas") or len(os.sched_getaffinity(0)))
+
+
+def synth_mod():
+    import synth
+    return synth
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -301,6 +462,24 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     ctx = mf.Context.default(0)
+    if wl.n_recv_layers == 1:
+        # one layer pair at its full size (the smaller and the varlen / long-context workloads)
+        res = bench_single(mf, torch, wl, args, ctx, dev)
+        if args.probe_bytes > 0:
+            # one copy of known size: the calibration of the HBM byte counters in profiled runs
+            src = torch.ones(args.probe_bytes // 4, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            mf.copy_probe(dst, src, ctx=ctx)
+            torch.cuda.synchronize()
+            del src, dst
+        line = {"metric": f"fused retrieve tokens/s + achieved HBM GB/s vs peak ({wl.name})",
+                "value": res["retrieve"]["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+                "steps": res["retrieve"]["launches"], "warmup": 1, "ms_per_step": res["retrieve"]["ms"],
+                "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": "synthetic (seeded, generated on device)",
+                "config": {"workload": wl.name}, "result": res}
+        print(json.dumps(line), flush=True)
+        return
     L, B, tau = wl.seq_len, wl.B, float(np.float32(wl.tau))
     pi = mf.layer_map_uniform(wl.n_recv_layers, wl.n_send_layers, wl.R)
     recompute = [l for l in range(wl.n_recv_layers) if pi[l] < 0]
@@ -390,11 +569,12 @@ def main():
     kr_flops = args.steps * sum(retrieve_flops(nnzb[l], wl.H_s, wl.H_r, B, wl.d) for l in mapped)
     kr_avg_ms = kr_ms / max(n_kr, 1)
     achieved = kr_bytes / (kr_ms * 1e-3) / 1e9 if kr_ms > 0 else 0.0
-    traffic = traffic_from_profile(os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip"))
+    traffic = traffic_from_profile(RETRIEVE_SRC, wl.name)
     cp_ms = sum(rec["compress"]) / max(len(rec["compress"]), 1)
-    # compress work: two score passes over every causal block plus one over the kept blocks
+    # compress work: one score pass over every causal block (statistics) plus one over the kept
+    # blocks (gather)
     store_gb = float(np.mean([nnzb[l] * wl.H_s * B * B * 2 for l in mapped])) / 1e9
-    cp_flops = np.mean([(2 * n_causal + nnzb[l]) * 2 * wl.H_s * B * B * wl.d for l in mapped])
+    cp_flops = np.mean([(n_causal + nnzb[l]) * 2 * wl.H_s * B * B * wl.d for l in mapped])
     dense_ms = sum(rec["dense"]) / max(len(rec["dense"]), 1)
     dense_flops = 4 * wl.H_r * wl.d * sum(min(B, L - I * B) * (I * B + (min(B, L - I * B) + 1) / 2)
                                           for I in range((L + B - 1) // B))
@@ -514,6 +694,15 @@ def main():
         pvs = [mf.v_prepare(recv[l]["v"], B, cu, ctx=ctx) for l in two]
         out["fanout"] = fanout(mf, torch, wl, args, slots[(n_map - 1) % k], [(recv[l]["w"], recv[l]["v"]) for l in two],
                                pvs, kv_map, B, cu, ctx, dev)
+
+    if not args.no_configs:
+        # free the full-depth run's ring and inputs first (they return to torch's pool)
+        del slots, send, recv
+        read_gbs = out.get("hbm_read_probe", {}).get("GB_per_s")
+        out["configs"] = {}
+        for name in ("pair_8b3b_8k", "varlen_14b8b", "long_131k"):
+            out["configs"][name] = bench_single(mf, torch, synth.WORKLOADS[name], args, ctx, dev, read_gbs)
+            torch.cuda.synchronize()
 
     if not args.no_cpu_baseline:
         log("timing the oracle on a sample (CPU)")
