@@ -6,7 +6,9 @@ import os
 
 from ctypes import POINTER, c_char_p, c_float, c_int, c_int32, c_int64, c_size_t, c_uint16, c_uint64, c_void_p
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libmapflow.so")
+# MAPFLOW_LIB names another build of the library (for example one compiled with different flags)
+LIB_PATH = os.environ.get("MAPFLOW_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                                                          "libmapflow.so")
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mapflow.h")
 
 MF_OK, MF_ERR_INVALID, MF_ERR_UNSUPPORTED, MF_ERR_OOM, MF_ERR_HIP, MF_ERR_CAPACITY = range(6)

@@ -110,6 +110,7 @@ struct RetrieveArgs {
   int accumulate;        // 0: normalised output; across sender layers 1: write the unnormalised
                          // output and denominator, 2: add to them, 3: add and normalise
   int HP;                                  // heads per wave: a split holds up to 8*HP heads
+  int fast;                                // set by the launcher: straight-line fast path applies
   int8_t split_nslots[kMaxSplit];          // heads in each split; they fill its leading slots
   int8_t slot_recv[kMaxSplit][kMaxSlots];  // receiver of each slot
   int8_t slot_head[kMaxSplit][kMaxSlots];  // head within that receiver; -1 = empty

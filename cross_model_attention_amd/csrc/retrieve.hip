@@ -241,7 +241,7 @@ struct SlotInfo {
 // one after the other, so every split after the first finds the P tile in that XCD's L2.  A
 // split's slots may hold heads of different receivers (a fan-out): each slot carries its own
 // weights, V and output.
-template <int B, int D, int HP, int KC>
+template <int B, int D, int HP, int KC, bool FAST>
 __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs args) {
   const uint16_t* __restrict__ probs = args.probs;
   const int32_t* __restrict__ block_ptr = args.block_ptr;
@@ -259,6 +259,8 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   constexpr int GB = AhatLayout<B, HP>::kHeadBytes;
   constexpr int HR_MAX = 8 * HP;
   constexpr int NTG = (HP + 1) / 2;        // 16-head N-tiles of the mix
+  constexpr int HPW = HP;                  // stage 2: wave w owns slots w HP .. w HP + HP - 1
+  constexpr int NDW = NDT;
 
   __shared__ __attribute__((aligned(16))) unsigned char s_ahat[2][HR_MAX * GB];
   __shared__ float s_den[HR_MAX][RT_ROWS];
@@ -311,16 +313,29 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   auto head_of = [&](int j) { return s_head[j]; };
 
   // ---- setup: per-head scale, scaled weights, denominators ---------------------------------
-  // scaled weights (hi + lo, fp32) live in the second mixed-map buffer until the loop needs it
-  static_assert(HR_MAX * 64 * sizeof(float) <= HR_MAX * GB, "weights fit in one Ahat buffer");
-  float (*s_w)[64] = reinterpret_cast<float (*)[64]>(s_ahat[1]);
+  // The raw weights of every slot and the kept row masses of the tile's rows are read with one
+  // coalesced pass each into the second mixed-map buffer (unused until the loop); everything
+  // else is computed from LDS.  Read element by element, these would be dozens of dependent
+  // global round trips per workgroup.
+  float (*s_x)[64] = reinterpret_cast<float (*)[64]>(s_ahat[1]);
+  float (*s_rk)[RT_ROWS] = reinterpret_cast<float (*)[RT_ROWS]>(s_ahat[1] + HR_MAX * 64 * sizeof(float));
+  static_assert(HR_MAX * 64 * sizeof(float) + 64 * RT_ROWS * sizeof(float) <= HR_MAX * GB,
+                "weights and kept masses fit in one Ahat buffer");
+  for (int t = threadIdx.x; t < HR_MAX * 64; t += blockDim.x) {
+    const int j = t >> 6, h = t & 63;
+    s_x[j][h] = (head_of(j) >= 0 && h < H_s) ? s_slot[j].w[h] : 0.f;
+  }
+  for (int t = threadIdx.x; t < H_s * RT_ROWS; t += blockDim.x) {
+    const int h = t / RT_ROWS, i = t % RT_ROWS;
+    s_rk[h][i] = i < rows ? rkm[(size_t)h * T_tot + bi.tok0 + row0 + i] : 0.f;
+  }
+  __syncthreads();
+  // per-slot scale: 2^s with sum_h |W| 2^s <= 2^15
   if (threadIdx.x < HR_MAX) {
-    const int g = head_of(threadIdx.x);
     int e = 0;
-    if (g >= 0) {
-      const MF_GLOBAL float* wr = s_slot[threadIdx.x].w;
+    if (head_of(threadIdx.x) >= 0) {
       float sa = 0.f;
-      for (int h = 0; h < H_s; ++h) sa += fabsf(wr[h]);
+      for (int h = 0; h < H_s; ++h) sa += fabsf(s_x[threadIdx.x][h]);
       if (sa > 0.f && sa < __builtin_inff()) {
         int ex;
         frexpf(sa, &ex);      // sum |W| <= 2^ex
@@ -330,23 +345,23 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     s_sexp[threadIdx.x] = e;
   }
   __syncthreads();
+  // scaled weights x = W 2^s (fp32), in place
   for (int t = threadIdx.x; t < HR_MAX * 64; t += blockDim.x) {
-    const int j = t >> 6, h = t & 63, g = head_of(j);
-    float v = 0.f;
-    if (g >= 0 && h < H_s) {
-      const float x = ldexpf(s_slot[j].w[h], s_sexp[j]);
-      const float hi = bf16_to_f32(f32_to_bf16(x));
-      const float lo = bf16_to_f32(f32_to_bf16(x - hi));
-      v = hi + lo;
-    }
-    s_w[j][h] = v;
+    const int j = t >> 6, h = t & 63;
+    s_x[j][h] = ldexpf(s_x[j][h], s_sexp[j]);
   }
   __syncthreads();
+  // denominators with the weights the mix uses: hi + lo, hi = bf16(x), lo = bf16(x - hi)
   for (int t = threadIdx.x; t < HR_MAX * RT_ROWS; t += blockDim.x) {
     const int j = t / RT_ROWS, i = t % RT_ROWS;
     float den = 0.f;
     if (head_of(j) >= 0 && i < rows)
-      for (int h = 0; h < H_s; ++h) den += s_w[j][h] * rkm[(size_t)h * T_tot + bi.tok0 + row0 + i];
+      for (int h = 0; h < H_s; ++h) {
+        const float x = s_x[j][h];
+        const float hi = bf16_to_f32(f32_to_bf16(x));
+        const float lo = bf16_to_f32(f32_to_bf16(x - hi));
+        den += (hi + lo) * s_rk[h][i];
+      }
     s_den[j][i] = den;
   }
 
@@ -356,8 +371,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
 #pragma unroll
     for (int nt = 0; nt < NTG; ++nt) {
       const int jn = 16 * nt + c;
-      const int g = jn < HR_MAX ? head_of(jn) : -1;
-      const MF_GLOBAL float* wr = g >= 0 ? s_slot[jn].w : nullptr;
+      const bool live = jn < HR_MAX && head_of(jn) >= 0;
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -370,8 +384,8 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
             for (int q2 = 0; q2 < 2; ++q2) {
               const int h = 32 * kc + 8 * a + 2 * e2 + q2;
               uint32_t bits = 0;
-              if (g >= 0 && h < H_s) {
-                const float x = ldexpf(wr[h], s_sexp[jn]);
+              if (live && h < H_s) {
+                const float x = s_x[jn][h];
                 const uint16_t hb = f32_to_bf16(x);
                 bits = lo ? f32_to_bf16(x - bf16_to_f32(hb)) : hb;
               }
@@ -384,23 +398,32 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     }
   }
 
-  // stage-2 ownership: local slots w*HP .. w*HP+HP-1
-  int sg[HP];
+  // stage-2 ownership: local slots s0 .. s0+HPW-1, all output tiles
+  const int s0 = w * HPW, dt0 = 0;
+  int sg[HPW];
 #pragma unroll
-  for (int j = 0; j < HP; ++j) sg[j] = head_of(w * HP + j);
-  v4f acc[HP][NDT];
+  for (int j = 0; j < HPW; ++j) sg[j] = head_of(s0 + j);
+  v4f acc[HPW][NDW];
 #pragma unroll
-  for (int j = 0; j < HP; ++j)
+  for (int j = 0; j < HPW; ++j)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = zero4();
+    for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = zero4();
 
   const int t0 = (int)min((int64_t)block_ptr[brow], capacity);
   const int t1 = (int)min((int64_t)block_ptr[brow + 1], capacity);
   const size_t blk_elems = (size_t)HGp * B * B * 8;
   const int kbrow0 = brow - bi.I;          // block row holding key block 0 of this sequence
 
-  // P operands of this wave: rows ROWS_PER_WAVE*w + rr, all M-tiles, KC head chunks
+  // P operands of this wave: rows ROWS_PER_WAVE*w + rr, all M-tiles, KC head chunks.  The loads
+  // are unconditional: a head group past the last (when H_s is not a multiple of 32) reads the
+  // last group again, whose products meet zero weights in the mix, and the prefetch past the
+  // row's last block re-reads that block.  Conditional loads would make the compiler's wait
+  // counts conservative, and vector-memory loads retire in order: a wait for a later load (a V
+  // tile) would then also wait for the whole prefetch of the next block.
   v4u pa[ROWS_PER_WAVE][MT][KC];
+  size_t p_off[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) p_off[kc] = (size_t)min(4 * kc + a, HGp - 1) * B * B * 8;
   auto load_p = [&](int t) {
     const uint16_t* pb = probs + (size_t)t * blk_elems;
 #pragma unroll
@@ -409,11 +432,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const int hg = 4 * kc + a;
-          pa[rr][mt][kc] = hg < HGp ? ld16_nt(pb + (((size_t)hg * B + r) * B + 16 * mt + c) * 8)
-                                    : zero_u4();
-        }
+        for (int kc = 0; kc < KC; ++kc) pa[rr][mt][kc] = ld16_nt(pb + p_off[kc] + ((size_t)r * B + 16 * mt + c) * 8);
     }
   };
   if (t0 < t1) load_p(t0);
@@ -421,24 +440,15 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
 
   // V operand tiles of the wave's first slot for key chunk 0 are fetched before the head mix,
   // so their latency hides under it; later chunks and other V heads are loaded on use.
-  const MF_GLOBAL uint16_t* vj[HP];
+  const MF_GLOBAL uint16_t* vj[HPW];
 #pragma unroll
-  for (int j = 0; j < HP; ++j) vj[j] = s_slot[w * HP + j].v + lane * 8;
+  for (int j = 0; j < HPW; ++j) vj[j] = s_slot[s0 + j].v + lane * 8 + dt0 * 512;
   const MF_GLOBAL uint16_t* const v0 = vj[0];
   auto vtile = [&](const MF_GLOBAL uint16_t* vb, int kbrow, int ch) {
     return vb + (((size_t)kbrow * NCH + ch) * NDT) * 512;
   };
-  for (int t = t0; t < t1; ++t) {
-    unsigned char* buf = s_ahat[(t - t0) & 1];
-    const int J = block_idx[t];
-    const int kbrow = kbrow0 + J;
-    v8h vpre[NCH][NDT];
-    {
-      const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, 0);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
-    }
-    // ---- stage 1: head mix -> fp16 Ahat in LDS ----
+  // ---- stage 1: head mix -> fp16 Ahat in LDS (rows of this wave, every head of the split) ----
+  auto mix = [&](unsigned char* buf) {
 #pragma unroll
     for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
       const int ii = ROWS_PER_WAVE * w + rr;
@@ -446,7 +456,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
       for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
         for (int nt = 0; nt < NTG; ++nt) {
-          v4f mix[2];
+          v4f mx[2];
 #pragma unroll
           for (int half = 0; half < 2; ++half) {
             v4f m4 = zero4();
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
               m4 = mfma_bf16(p8, as_v8s(s_wop[nt][kc][0][lane]), m4);
               m4 = mfma_bf16(p8, as_v8s(s_wop[nt][kc][1][lane]), m4);
             }
-            mix[half] = m4;
+            mx[half] = m4;
           }
           // lane (a, c): local head 16 nt + c, keys 32 ch + 16 half + 4a + i -> 8 fp16 values
           const int g = 16 * nt + c;
@@ -466,68 +476,117 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
             for (int half = 0; half < 2; ++half)
 #pragma unroll
               for (int p2 = 0; p2 < 2; ++p2) {
-                const f2 v2 = {mix[half][2 * p2], mix[half][2 * p2 + 1]};
+                const f2 v2 = {mx[half][2 * p2], mx[half][2 * p2 + 1]};
                 pk[2 * half + p2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, h2));
               }
             *reinterpret_cast<v4u*>(buf + g * GB + ii * RB + (ch * 4 + a) * 16) = v4u{pk[0], pk[1], pk[2], pk[3]};
           }
         }
       }
-    }
-    if (t + 1 < t1) load_p(t + 1);
-    __syncthreads();
+      }
+  };
 
-    // ---- stage 2: P.V for this wave's receiver heads ----
+  // FAST: every slot of every wave holds a head and a wave's heads share one V group (they belong
+  // to one KV head of one receiver, as with grouped-query receivers; the host checks it).
+  // Straight-line loads, software-pipelined in consumption order: a key chunk's V tiles for the
+  // next block are requested right after this block's last product with them, and the next
+  // block's P right after the mix.  In issue order every wait of a block then covers only older
+  // loads (vector-memory loads retire in order), and each load has a whole stage to land.
+  if constexpr (FAST) {
+    v8h vt[NCH][NDW];
+    auto load_v = [&](int t, int ch) {
+      const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow0 + block_idx[t], ch);
+#pragma unroll
+      for (int dt = 0; dt < NDW; ++dt) vt[ch][dt] = as_v8h(ld16(vb + dt * 512));
+    };
+    if (t0 < t1) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) load_v(t0, ch);
+    }
+    for (int t = t0; t < t1; ++t) {
+      unsigned char* buf = s_ahat[(t - t0) & 1];
+      const int tn = min(t + 1, t1 - 1);
+      mix(buf);
+      load_p(tn);
+      __syncthreads();
+      // ---- stage 2: P.V for this wave's receiver heads ----
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + (ch * 4 + a) * 16));
+#pragma unroll
+          for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vt[ch][dt], acc[j][dt]);
+        }
+        load_v(tn, ch);
+      }
+    }
+  } else {
+  for (int t = t0; t < t1; ++t) {
+    unsigned char* buf = s_ahat[(t - t0) & 1];
+    const int J = block_idx[t];
+    const int kbrow = kbrow0 + J;
+    v8h vpre[NCH][NDW];
+    {
+      const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, 0);
+#pragma unroll
+      for (int dt = 0; dt < NDW; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
+    }
+    mix(buf);
+    load_p(min(t + 1, t1 - 1));
+    __syncthreads();
+    // ---- stage 2: P.V for this wave's receiver heads and output tiles ----
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       if (ch > 0) {
         const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, ch);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
+        for (int dt = 0; dt < NDW; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
       }
 #pragma unroll
-      for (int j = 0; j < HP; ++j) {
+      for (int j = 0; j < HPW; ++j) {
         const int g = sg[j];
         if (g < 0) continue;
-        v8h vop[NDT];
+        v8h vop[NDW];
         if (vj[j] == v0) {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vop[dt] = vpre[ch][dt];
+          for (int dt = 0; dt < NDW; ++dt) vop[dt] = vpre[ch][dt];
         } else {
           const MF_GLOBAL uint16_t* vb = vtile(vj[j], kbrow, ch);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
+          for (int dt = 0; dt < NDW; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
         }
-        const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (w * HP + j) * GB + c * RB + (ch * 4 + a) * 16));
+        const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + (ch * 4 + a) * 16));
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
+        for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
       }
     }
+  }
   }
 
   // ---- epilogue ----
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < HP; ++j) {
+  for (int j = 0; j < HPW; ++j) {
     const int g = sg[j];
     if (g < 0) continue;
     // den carries the same 2^s_g as the mixed map, so only V's scale is undone here
-    const SlotInfo& si = s_slot[w * HP + j];
+    const SlotInfo& si = s_slot[s0 + j];
     const float unscale = ldexpf(1.f, -si.vexp);
     if (args.accumulate == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int ii = 4 * a + i;
         if (ii >= rows) continue;
-        const float inv = unscale / s_den[w * HP + j][ii];
+        const float inv = unscale / s_den[s0 + j][ii];
         MF_GLOBAL float* orow = si.o + (size_t)(bi.tok0 + row0 + ii) * si.ostride;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
+        for (int dt = 0; dt < NDW; ++dt) orow[16 * (dt0 + dt) + c] = acc[j][dt][i] * inv;
       }
     } else {
       // cross-layer mix: this layer's unnormalised output and denominator in true units (the
       // head's weight scale 2^s_g undone), summed over the layers, divided by the last one
-      const float wun = ldexpf(1.f, -s_sexp[w * HP + j]);
+      const float wun = ldexpf(1.f, -s_sexp[s0 + j]);
       const int mode = args.accumulate;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -536,17 +595,19 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
         const size_t tok = (size_t)(bi.tok0 + row0 + ii);
         MF_GLOBAL float* orow = si.o + tok * si.ostride;
         MF_GLOBAL float* dp = si.dn + tok * (si.ostride / D);
-        float den = s_den[w * HP + j][ii] * wun;
+        float den = s_den[s0 + j][ii] * wun;
         if (mode >= 2) den += *dp;
         const float num = unscale * wun;
         const float inv = mode == 3 ? 1.f / den : 1.f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        for (int dt = 0; dt < NDW; ++dt) {
           float v = acc[j][dt][i] * num;
-          if (mode >= 2) v += orow[16 * dt + c];
-          orow[16 * dt + c] = v * inv;
+          if (mode >= 2) v += orow[16 * (dt0 + dt) + c];
+          orow[16 * (dt0 + dt) + c] = v * inv;
         }
-        if (mode != 3 && c == 0) *dp = den;
+        // modes 1 and 2 only store the denominator (one wave of the slot does), mode 3 only
+        // reads it: with the columns split over two waves neither reads the other's store
+        if (mode != 3 && dt0 == 0 && c == 0) *dp = den;
       }
     }
   }
@@ -557,26 +618,49 @@ bool retrieve_supported(int B, int d, int H_r, int H_s) {
          H_s <= 64;
 }
 
-template <int B, int D, int HP, int KC>
+template <int B, int D, int HP, int KC, bool FAST>
 static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
   constexpr int NRT = B / RT_ROWS;
   const unsigned groups = (unsigned)((a.n_order + 7) / 8);
-  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC, FAST>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0, s, a);
   return hipGetLastError();
 }
 
 template <int B, int D>
 static hipError_t retrieve_bd(const RetrieveArgs& a, hipStream_t s) {
   const int KC = ((a.H_s + 7) / 8 + 3) / 4;
-#define MF_RETRIEVE_CASES(KC_)                          \
-  switch (a.HP) {                                       \
-    case 1: return retrieve_t<B, D, 1, KC_>(a, s);      \
-    case 2: return retrieve_t<B, D, 2, KC_>(a, s);      \
-    case 3: return retrieve_t<B, D, 3, KC_>(a, s);      \
+  // the fast path does not fit the register file with 3 heads per wave and two head chunks
+  if (a.fast && !(a.HP == 3 && KC == 2)) {
+    switch (a.HP * 4 + KC) {
+      case 1 * 4 + 1: return retrieve_t<B, D, 1, 1, true>(a, s);
+      case 2 * 4 + 1: return retrieve_t<B, D, 2, 1, true>(a, s);
+      case 3 * 4 + 1: return retrieve_t<B, D, 3, 1, true>(a, s);
+      case 1 * 4 + 2: return retrieve_t<B, D, 1, 2, true>(a, s);
+      case 2 * 4 + 2: return retrieve_t<B, D, 2, 2, true>(a, s);
+    }
+    return hipErrorInvalidValue;
   }
-  if (KC == 1) { MF_RETRIEVE_CASES(1) } else { MF_RETRIEVE_CASES(2) }
-#undef MF_RETRIEVE_CASES
+  switch (a.HP * 4 + KC) {
+    case 1 * 4 + 1: return retrieve_t<B, D, 1, 1, false>(a, s);
+    case 2 * 4 + 1: return retrieve_t<B, D, 2, 1, false>(a, s);
+    case 3 * 4 + 1: return retrieve_t<B, D, 3, 1, false>(a, s);
+    case 1 * 4 + 2: return retrieve_t<B, D, 1, 2, false>(a, s);
+    case 2 * 4 + 2: return retrieve_t<B, D, 2, 2, false>(a, s);
+    case 3 * 4 + 2: return retrieve_t<B, D, 3, 2, false>(a, s);
+  }
   return hipErrorInvalidValue;
+}
+
+// Every slot of every wave holds a head, and the HP slots of each wave share one receiver and KV
+// head: the kernel may then load one V tile set per wave with straight-line code.
+static bool slots_fast(const RetrieveArgs& a) {
+  for (int k = 0; k < a.n_split; ++k)
+    for (int w = 0; w < 8; ++w)
+      for (int j = w * a.HP; j < (w + 1) * a.HP; ++j) {
+        if (a.slot_head[k][j] < 0) return false;
+        if (a.slot_recv[k][j] != a.slot_recv[k][w * a.HP] || a.slot_kv[k][j] != a.slot_kv[k][w * a.HP]) return false;
+      }
+  return true;
 }
 
 hipError_t retrieve(const RetrieveArgs& a, hipStream_t s) {
@@ -593,10 +677,12 @@ hipError_t retrieve(const RetrieveArgs& a, hipStream_t s) {
         return hipErrorInvalidValue;
     }
   }
-  if (a.B == 64 && a.d == 128) return retrieve_bd<64, 128>(a, s);
-  if (a.B == 64 && a.d == 64) return retrieve_bd<64, 64>(a, s);
-  if (a.B == 32 && a.d == 128) return retrieve_bd<32, 128>(a, s);
-  if (a.B == 32 && a.d == 64) return retrieve_bd<32, 64>(a, s);
+  RetrieveArgs b = a;
+  b.fast = slots_fast(a) ? 1 : 0;
+  if (a.B == 64 && a.d == 128) return retrieve_bd<64, 128>(b, s);
+  if (a.B == 64 && a.d == 64) return retrieve_bd<64, 64>(b, s);
+  if (a.B == 32 && a.d == 128) return retrieve_bd<32, 128>(b, s);
+  if (a.B == 32 && a.d == 64) return retrieve_bd<32, 64>(b, s);
   return hipErrorInvalidValue;
 }
 
