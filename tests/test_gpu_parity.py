@@ -423,6 +423,26 @@ def test_chunked_prefill_rows_equal_the_full_store(mf):
                 assert len(_rows_of(hp, r)[0]) == 0, f"row {r} outside the range kept blocks"
             r += 1
     assert np.array_equal(hf["row_kept_mass"][:, active_tok], hp["row_kept_mass"][:, active_tok])
+    # the range store's rows against the oracle: kept sets (tie rule), every stored value against
+    # the exact map, kept mass the sum of the stored values
+    ref = oracle.compress(x["q_s"], x["k_s"], cu, tau, wl.B, keep_exact=True)
+    r = 0
+    for s_, n in enumerate(lengths):
+        for I in range((n + wl.B - 1) // wl.B):
+            if I >= row_begin[s_]:
+                idx, bits = _rows_of(hp, r)
+                ok, why = sets_agree(idx.tolist(), ref.rows[r], tau)
+                assert ok, f"range row {r}: {why}"
+                lo = int(hp["block_ptr"][r])
+                for t, J in enumerate(idx.tolist()):
+                    if J in ref.rows[r]["exact"]:
+                        A = ref.rows[r]["exact"][J]
+                        err = np.abs(hp["probs"][lo + t] - A)
+                        assert np.all(err <= ulp_bf16(A) + 1e-6), f"range row {r} block {J}"
+                rows_b, tok0 = ref.rows[r]["rows"], ref.rows[r]["tok0"]
+                want = hp["probs"][lo:lo + len(idx), :, :rows_b, :].sum(axis=(0, 3))
+                assert np.allclose(hp["row_kept_mass"][:, tok0:tok0 + rows_b], want, rtol=1e-6, atol=1e-7)
+            r += 1
     W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
     O_full = mf.retrieve(full, W, V, x["kv_head_map"])
     O_part = torch.full_like(O_full, float("nan"))
@@ -431,6 +451,20 @@ def test_chunked_prefill_rows_equal_the_full_store(mf):
     act = torch.from_numpy(active_tok).cuda()
     assert torch.equal(O_part[act], O_full[act])
     assert torch.isnan(O_part[~act]).all()
+    # the range retrieve's rows against the oracle run on the range store's own blocks
+    gp = gpu_store_for_oracle(hp, cu, wl.B, 8)
+    got, want = [], []
+    for b, (s_, I) in enumerate(brow_table(cu, wl.B)):
+        if I < row_begin[s_]:
+            continue
+        lo, hi = int(hp["block_ptr"][b]), int(hp["block_ptr"][b + 1])
+        n = int(cu[s_ + 1] - cu[s_])
+        rows_b, tok0 = min(n, (I + 1) * wl.B) - I * wl.B, int(cu[s_]) + I * wl.B
+        blocks = {int(gp.block_idx[t]): gp.probs[t] for t in range(lo, hi)}
+        want.append(oracle.retrieve_block_row(blocks, wl.B, rows_b, tok0, s_, int(cu[s_]), n, x["w"], x["v_r"],
+                                              x["kv_head_map"]))
+        got.append(O_part[tok0:tok0 + rows_b].cpu().numpy())
+    assert_out_close(np.concatenate(got), np.concatenate(want), "O_r (range store)")
     # the fused prefill on the range store: same store, attention rows of the range only
     pre = mf.BlockStore.create(8, wl.B, x["cu_seqlens"], row_begin=row_begin)
     Vs = to_dev(v_s, "bf16")
@@ -494,6 +528,28 @@ def test_prefix_cache_reuses_a_previous_request(mf):
     O_whole = mf.retrieve(whole, W, V, x["kv_head_map"])
     torch.cuda.synchronize()
     assert torch.equal(O, O_whole)
+    # the cached-prefix rows and the range store's rows, each retrieved by the oracle from the
+    # GPU's own blocks of the store that served them
+    hv0, hn = view.to_host(), new.to_host()
+    cu2 = [0, n2]
+    want = np.zeros((n2, 12, 128))
+    for I in range((n2 + B - 1) // B):
+        src, b = (hv0, I) if I < rows else (hn, I)
+        lo, hi = int(src["block_ptr"][b]), int(src["block_ptr"][b + 1])
+        blocks = {int(src["block_idx"][t]): src["probs"][t] for t in range(lo, hi)}
+        rows_b = min(n2, (I + 1) * B) - I * B
+        want[I * B:I * B + rows_b] = oracle.retrieve_block_row(blocks, B, rows_b, I * B, 0, 0, n2, x["w"],
+                                                               x["v_r"], x["kv_head_map"])
+    assert_out_close(O.cpu().numpy(), want, "O_r (cached prefix + range store)")
+    ref_c = oracle.compress(x["q_s"], x["k_s"], np.array(cu2), tau, B, keep_exact=True)
+    for I in range(rows):                                  # the cached rows against the exact map
+        lo, hi = int(hv0["block_ptr"][I]), int(hv0["block_ptr"][I + 1])
+        ok, why = sets_agree(hv0["block_idx"][lo:hi].tolist(), ref_c.rows[I], tau)
+        assert ok, f"cached row {I}: {why}"
+        for t in range(lo, hi):
+            A = ref_c.rows[I]["exact"].get(int(hv0["block_idx"][t]))
+            if A is not None:
+                assert np.all(np.abs(hv0["probs"][t] - A) <= ulp_bf16(A) + 1e-6), f"cached row {I}"
     # cache request 2's complete rows from the view and the new rows
     cache.insert(3, tokens, [view, new], n2 // B)
     rows2, view2 = cache.lookup(3, tokens, B)
@@ -540,11 +596,14 @@ def test_compress_variants(mf, case):
     mf.compress_into(store, Q, K, tau, per_head_select=case["sel"], per_head_norm=case["norm"])
     store.sync()
     host = store.to_host()
-    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B, per_head_select=case["sel"],
-                          per_head_norm=case["norm"])
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, wl.B, keep_exact=True,
+                          per_head_select=case["sel"], per_head_norm=case["norm"])
     assert np.array_equal(host["block_ptr"], ref.block_ptr)
     assert np.array_equal(host["block_idx"], ref.block_idx)
-    assert np.all(np.abs(host["probs"] - ref.probs) <= ulp_bf16(ref.probs) + 1e-6)
+    # stored values against the exact (unrounded) map of the variant, zeros where a head did not
+    # select the block
+    err = np.abs(host["probs"] - ref.exact)
+    assert np.all(err <= ulp_bf16(ref.exact) + 1e-6), f"max excess {(err - ulp_bf16(ref.exact)).max():.3e}"
     cu, B = x["cu_seqlens"], wl.B
     for b, (s, I) in enumerate(brow_table(cu, B)):
         n = int(cu[s + 1] - cu[s])

@@ -1,0 +1,100 @@
+"""GPU checks of the fused retrieve against what the mathematics fixes, beside the element-wise
+oracle comparisons of test_gpu_parity.py:
+
+* a V whose rows are all equal to v gives O = v for every query row, whatever the kept blocks
+  and the mixing weights (the renormalised mixed rows sum to one);
+* a "read-out" V, V[kv, j0 + c, c] = 1 and 0 elsewhere, makes O[., g, c] equal the renormalised
+  mixed map of receiver head g at key j0 + c, so the on-chip mixed map itself is compared with
+  the oracle's (not only its products with V);
+* permuting the sender heads (Q, K and the columns of W together) leaves the output unchanged up
+  to rounding: the GPU's head mix depends on the heads only through W.
+
+[MapFlow开源, section 算得省的:融合内核执行]: the kernel mixes the sender heads linearly on chip,
+renormalises the rows and multiplies by the receiver's own V.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import assert_out_close, gpu_store_for_oracle, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mf():
+    import cross_model_attention_amd as m
+    return m
+
+
+def _case(seed, lengths, H_s=32, H_r=24, H_kv=8, d=128):
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, seed, lengths=lengths, H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+    return wl, x, float(np.float32(wl.tau))
+
+
+def _compress(mf, x, tau, B):
+    store = mf.compress(to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16"), tau, B, cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    return store
+
+
+@pytest.mark.parametrize("lengths,heads", [([300, 77], (32, 24, 8, 128)), ([200], (40, 32, 8, 64))])
+def test_constant_v_gives_that_row(mf, lengths, heads):
+    wl, x, tau = _case(41, lengths, *heads)
+    say(f"case: constant V lengths={lengths} heads={heads}")
+    store = _compress(mf, x, tau, wl.B)
+    T, H_kv, d = x["T"], x["H_kv"], x["d"]
+    v = synth.bf16_bits_to_f32(synth.bf16_bits_from_f32(
+        np.random.default_rng(41).standard_normal((H_kv, d)).astype(np.float32)))
+    V = np.broadcast_to(v[None], (T, H_kv, d)).copy()
+    O = mf.retrieve(store, to_dev(x["w"]), to_dev(V, "bf16"), x["kv_head_map"])
+    torch.cuda.synchronize()
+    want = np.broadcast_to(v[np.asarray(x["kv_head_map"])][None], O.shape)
+    assert_out_close(O.cpu().numpy(), want, "O_r with constant V")
+
+
+@pytest.mark.parametrize("j0", [0, 64])
+def test_v_readout_exposes_the_mixed_map(mf, j0):
+    wl, x, tau = _case(42, [330, 150])
+    say(f"case: V read-out j0={j0}")
+    store = _compress(mf, x, tau, wl.B)
+    host = store.to_host()
+    T, H_kv, d, cu = x["T"], x["H_kv"], x["d"], x["cu_seqlens"]
+    V = np.zeros((T, H_kv, d), dtype=np.float32)
+    for s in range(len(cu) - 1):
+        for c in range(d):
+            j = j0 + c
+            if j < cu[s + 1] - cu[s]:
+                V[cu[s] + j, :, c] = 1.0
+    O = mf.retrieve(store, to_dev(x["w"]), to_dev(V, "bf16"), x["kv_head_map"])
+    torch.cuda.synchronize()
+    got = O.cpu().numpy().astype(np.float64)
+    want = oracle.retrieve(gpu_store_for_oracle(host, cu, wl.B, x["H_s"]), x["w"], V, x["kv_head_map"])
+    assert_out_close(got, want, "read-out of the mixed map")
+    # a renormalised mixed map with Dirichlet (non-negative) weights lies in [0, 1]
+    assert got.min() >= -1e-3 and got.max() <= 1 + 1e-3
+
+
+def test_sender_head_permutation_invariance(mf):
+    wl, x, tau = _case(43, [280, 96])
+    say("case: sender-head permutation")
+    perm = np.random.default_rng(43).permutation(x["H_s"])
+    store = _compress(mf, x, tau, wl.B)
+    xp = dict(x, q_s=np.ascontiguousarray(x["q_s"][perm]), k_s=np.ascontiguousarray(x["k_s"][perm]),
+              w=np.ascontiguousarray(x["w"][:, perm]))
+    store_p = _compress(mf, xp, tau, wl.B)
+    h, hp = store.to_host(), store_p.to_host()
+    # the head-summed masses only change in rounding order: the same blocks are kept
+    assert np.array_equal(h["block_ptr"], hp["block_ptr"]) and np.array_equal(h["block_idx"], hp["block_idx"])
+    assert np.array_equal(h["probs"][:, perm], hp["probs"]), "stored values move with their heads"
+    V = to_dev(x["v_r"], "bf16")
+    O = mf.retrieve(store, to_dev(x["w"]), V, x["kv_head_map"])
+    Op = mf.retrieve(store_p, to_dev(xp["w"]), V, x["kv_head_map"])
+    torch.cuda.synchronize()
+    assert_out_close(Op.cpu().numpy(), O.cpu().numpy().astype(np.float64), "O_r with permuted sender heads")
+    assert_out_close(Op.cpu().numpy(),
+                     oracle.retrieve(gpu_store_for_oracle(h, x["cu_seqlens"], wl.B, x["H_s"]), x["w"], x["v_r"],
+                                     x["kv_head_map"]), "O_r (permuted) vs the oracle")
