@@ -121,6 +121,20 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS (and scalar memory)
+// operations, then the hardware barrier.  __syncthreads also carries a release fence, which
+// waits for every outstanding global store and load of the wave; in a loop that streams stores
+// and prefetches loads across block boundaries that fence would drain both at every barrier.
+// Use it where only LDS data (including LDS filled by DMA after its own explicit wait) is
+// exchanged between the waves.  The empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Per block row: {first token of the row, first token of its sequence, sequence length, I}.
 struct BrowInfo {
   int tok0, seq0, n, I;

@@ -19,6 +19,8 @@
 // Scores s = q.k / sqrt(d) are formed by MFMA (bf16 inputs: 16x16x32 bf16; fp32 inputs:
 // 16x16x4 f32) with fp32 accumulation; exponentials use base 2 with log2(e) folded into the
 // scale.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "sweep.h"
@@ -416,10 +418,10 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
 // values accumulated on MFMA: the packed probabilities of two key slices form the B operand
 // (8 keys of row c per lane) against an all-ones A operand, so each product adds 32 keys of 16
 // rows.  rsum[mt] ends with the row total of row 16 mt + c in every element.
-template <typename T, int B, int D>
+template <typename T, int B, int D, bool HAS_PREV>
 __device__ __forceinline__ void gather_block(bool MASKED, const Frag<T, D> (&qf)[B / 16], const float (&l2)[B / 16],
                                              Frag<T, D> (&kb)[B / 16], const unsigned char* ktj,
-                                             const unsigned char* ktn, bool has_next, int J, int rows,
+                                             const unsigned char* ktn, int J, int rows,
                                              int qdiag, float scale2, unsigned char* tile, const int (&woff)[4],
                                              int w, int lane, int a, int c, v4f (&rsum)[B / 16],
                                              const unsigned char* prev, unsigned char* prev_dst) {
@@ -433,13 +435,16 @@ __device__ __forceinline__ void gather_block(bool MASKED, const Frag<T, D> (&qf)
   uint32_t pend[MT][2];                            // packed probabilities of the even slice
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    // the slice NT-1 ahead (the last of this block, or one of the next block's) into the
-    // register set slice nt-1 has finished with
+    // the slice NT-1 ahead (the last of this block, or one of the next block's; past the chunk's
+    // last block, this block's own slice again) into the register set slice nt-1 has finished
+    // with.  Every load and store of the loop is unconditional: vector-memory operations complete
+    // in issue order on one counter, and conditional ones would make the compiler's wait counts
+    // conservative enough to wait for the slices prefetched ahead.
     if (nt == 0) ktile_load<D>(kb[NT - 1], ktj + (NT - 1) * SB, lane);
-    else if (has_next) ktile_load<D>(kb[nt - 1], ktn + (nt - 1) * SB, lane);
+    else ktile_load<D>(kb[nt - 1], ktn + (nt - 1) * SB, lane);
     // a part of the previous block's tile goes out after the key loads, so no wait on a key
-    // slice ever covers these stores (one counter, completed in issue order)
-    if (prev != nullptr) stream_tile<B>(prev, prev_dst, nt, NT, w, lane);
+    // slice ever covers these stores
+    if constexpr (HAS_PREV) stream_tile<B>(prev, prev_dst, nt, NT, w, lane);
     // the slice's score tiles, the MT accumulation chains interleaved step by step over the head
     // dimension so that no product waits on the one just issued
     v4f scs[MT];
@@ -492,7 +497,7 @@ struct GatherLds {
   static constexpr int kBufs = 2;
 };
 
-template <typename T, int B, int D>
+template <typename T, int B, int D, bool SELH>
 __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T* __restrict__ K,
                                                 int H_s, int64_t T_tot,
                                                 const int32_t* __restrict__ info,
@@ -578,22 +583,23 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
     for (int nt = 0; nt + 1 < NT; ++nt) ktile_load<D>(kb[nt], k0 + nt * SB, lane);
   }
   double rsum_chunk = 0.0;
-  for (int t = t0; t < t1; ++t) {
+  // one kept block: scores, probabilities into the record tile, row sums; with HAS_PREV the
+  // previous block's tile streams out meanwhile (the first block of the chunk has none)
+  auto one = [&](auto has_prev, int t) {
+    constexpr bool HP_ = decltype(has_prev)::value;
     const int J = block_idx[t];
-    const bool has_next = t + 1 < t1;
-    const int Jn = has_next ? block_idx[t + 1] : J;
+    const int Jn = block_idx[min(t + 1, t1 - 1)];
     unsigned char* tile = s_out[(t - t0) % NBUF];
     v4f rsum[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) rsum[mt] = zero4();
-    // with two tile buffers the previous block's tile is streamed during this block
-    const bool overlap = NBUF == 2 && t > t0;
-    const unsigned char* prev = overlap ? s_out[(t - t0 - 1) % NBUF] : nullptr;
+    const unsigned char* prev = s_out[(t - t0 + 1) % NBUF];
     unsigned char* prev_dst = reinterpret_cast<unsigned char*>(probs) + ((size_t)(t - 1) * HG + hg) * (size_t)TILE;
     // a head that did not select this block (per-head selection) stores zeros
-    const bool keep = active && (hflags == nullptr || hflags[((size_t)h * n_brow + brow) * nb_max + J]);
-    gather_block<T, B, D>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), has_next, J,
-                          keep ? rows : 0, qdiag, scale2, tile, woff, w, lane, a, c, rsum, prev, prev_dst);
+    bool keep = active;
+    if constexpr (SELH) keep = keep && hflags[((size_t)h * n_brow + brow) * nb_max + J];
+    gather_block<T, B, D, HP_>(!keep || J == bi.I || rows < B, qf, l2, kb, kt_block(J), kt_block(Jn), J,
+                               keep ? rows : 0, qdiag, scale2, tile, woff, w, lane, a, c, rsum, prev, prev_dst);
     {
       // row sums of the stored values, summed over the chunk in column order: lane (a, c) holds
       // row 16 a + c
@@ -602,17 +608,17 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
       for (int mt = 1; mt < MT; ++mt) v = a == mt ? rsum[mt][0] : v;
       rsum_chunk += (double)v;
     }
-    __syncthreads();
-    if (NBUF == 1) {                               // single buffer: stream now, then reuse
-      stream_tile<B>(tile, reinterpret_cast<unsigned char*>(probs) + ((size_t)t * HG + hg) * (size_t)TILE, 0, 1, w,
-                     lane);
-      __syncthreads();
-    }
-  }
-  if (NBUF == 2)                                   // the last block's tile
-    stream_tile<B>(s_out[(t1 - 1 - t0) % NBUF],
-                   reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1, w,
-                   lane);
+    // the tile is complete for streaming in the next block, and the other buffer (streamed during
+    // this block) may be written again; the stores and key loads in flight stay in flight
+    lds_barrier();
+  };
+  static_assert(NBUF == 2, "the previous block's tile streams from the other buffer");
+  one(std::false_type{}, t0);
+  for (int t = t0 + 1; t < t1; ++t) one(std::true_type{}, t);
+  // the last block's tile
+  stream_tile<B>(s_out[(t1 - 1 - t0) % NBUF],
+                 reinterpret_cast<unsigned char*>(probs) + ((size_t)(t1 - 1) * HG + hg) * (size_t)TILE, 0, 1, w,
+                 lane);
   // the chunk's row sums, one slot per (block row, chunk)
   const int n_chunk = (nb_max + kGatherChunk - 1) / kGatherChunk;
   if (active && a < MT) part[(((size_t)brow * n_chunk + chunk) * H_s + h) * B + 16 * a + c] = rsum_chunk;
@@ -668,11 +674,16 @@ static hipError_t gather_t(const CompressArgs& a, hipStream_t s) {
   // grid: with the XCD mapping, 8 XCDs x ceil(n_brow / (8 / HG)) block rows x chunks
   const unsigned items = (8 % HG) == 0 ? 8u * (unsigned)((a.n_order + 8 / HG - 1) / (8 / HG)) * chunks
                                        : (unsigned)a.n_order * HG * chunks;
-  hipLaunchKernelGGL((k_gather<T, B, D>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
-                     (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.n_order, a.block_ptr, a.block_idx,
-                     a.counters, a.capacity, (a.options & 2) ? a.lse2n : a.lse2, a.scale2,
-                     (const unsigned char*)a.ktile, (a.options & 1) ? a.hflags : nullptr, a.nb_max, a.probs,
-                     a.part);
+  if (a.options & 1)
+    hipLaunchKernelGGL((k_gather<T, B, D, true>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
+                       (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.n_order, a.block_ptr, a.block_idx,
+                       a.counters, a.capacity, (a.options & 2) ? a.lse2n : a.lse2, a.scale2,
+                       (const unsigned char*)a.ktile, a.hflags, a.nb_max, a.probs, a.part);
+  else
+    hipLaunchKernelGGL((k_gather<T, B, D, false>), dim3(items), dim3(512), 0, s, (const T*)a.Q,
+                       (const T*)a.K, a.H_s, a.T, a.info, a.order, a.n_brow, a.n_order, a.block_ptr, a.block_idx,
+                       a.counters, a.capacity, (a.options & 2) ? a.lse2n : a.lse2, a.scale2,
+                       (const unsigned char*)a.ktile, nullptr, a.nb_max, a.probs, a.part);
   return hipGetLastError();
 }
 

@@ -231,6 +231,10 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
     }
   };
   auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0): the DMA has landed
+  // the same with the QT statistics stores issued after the DMA still allowed in flight
+  // (vector-memory operations complete in issue order, so the older DMA has landed)
+  static_assert(QT == 2, "the wait below counts QT stores");
+  auto dma_wait_but_stores = [] { __builtin_amdgcn_s_waitcnt(0x0F72); };   // vmcnt(2)
   auto fetch_k = [&](v4u (&kst)[CPT], int J) {
     if constexpr (DMA) return;
 #pragma unroll
@@ -270,10 +274,22 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   }
   const int kbrow0 = pairs[2 * pr] - b0.I;                // block row holding key block 0
   v4u kst[CPT];
+  // A block's statistics are stored during the next block, right after that block's key DMA, so
+  // the wait for the DMA at its end need not cover them.
+  float2 zpend[QT];
+  int Jpend = -1;                                         // block whose statistics are pending
   auto block = [&](int J) {
     if (J + 1 <= Jend) {
       fetch_k(kst, J + 1);
       dma_k(J + 1, (J + 1) & 1);                            // that buffer was last read in block J - 1
+    }
+    const bool stored = STATS && Jpend >= 0;
+    if (stored) {
+      if (a == 0) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) zrow[(size_t)Jpend * B + q0 + 16 * qt + c] = zpend[qt];
+      }
+      Jpend = -1;
     }
     if (mine && J <= bi.I) {
       const unsigned char* kt = s_k[J & 1];
@@ -319,7 +335,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
           zr = masked ? block_stats<MT, true, ATTN>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
                       : block_stats<MT, false, ATTN>(s[qt], 0, true, scale2);
         }
-        if (STATS && a == 0) zrow[(size_t)J * B + qr] = zr;
+        if (STATS) zpend[qt] = zr;
         const float mprev = m_run[qt];
         if (!done && zr.x > 0.f) {
           const float mn = __builtin_fmaxf(m_run[qt], zr.y);
@@ -347,6 +363,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
           }
         }
       }
+      if (STATS) Jpend = J;
       if constexpr (ATTN) {
         // P.V on the fp16 MFMA; each V operand tile serves both query tiles
         const uint16_t* vb = ao.vfrag + ((((size_t)hd.vhead * n_brow + kbrow0 + J) * NCH) * NDT) * 512 + lane * 8;
@@ -361,8 +378,11 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
       }
     }
     if (J + 1 <= Jend) stage_k(kst, (J + 1) & 1);
-    if (DMA) dma_wait();
-    __syncthreads();
+    if (DMA) {
+      if (stored) dma_wait_but_stores();
+      else dma_wait();
+    }
+    lds_barrier();
   };
   fetch_k(kst, 0);
   stage_k(kst, 0);
@@ -370,6 +390,10 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   if (DMA) dma_wait();
   __syncthreads();
   for (int J = 0; J <= Jend; ++J) block(J);
+  if (STATS && Jpend >= 0 && a == 0) {                     // the last block's statistics
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) zrow[(size_t)Jpend * B + q0 + 16 * qt + c] = zpend[qt];
+  }
   // ---- row logsumexp, then block masses (one coalesced read per block and wave) ------------
   if (STATS && mine && a == 0) {
 #pragma unroll
