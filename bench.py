@@ -582,6 +582,9 @@ def main():
     out = {
         "metric": "fused retrieve tokens/s + achieved HBM GB/s vs peak, 8B->3B map at L=32k",
         "value": L / (ms_step * 1e-3),
+        "value_definition": ("L / step time: one whole receiver prefill (dense recompute of the first layers, the "
+                             "mapped layers' compresses and their fused retrieves); the retrieve alone is "
+                             "retrieve.tokens_per_s_per_layer and retrieve.full_stack_tokens_per_s"),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,

@@ -219,7 +219,12 @@ mf_status mf_bsr_upload(mf_ctx* ctx, mf_bsr* bsr, const int32_t* block_ptr_host,
                         const int32_t* block_idx_host, const uint16_t* probs_host,
                         const float* row_kept_mass_host);
 
-/* Free the device arrays of a store created by this library; zeroes *bsr. */
+/*
+ * Free the device arrays of a store created by this library and zero *bsr.  The device is
+ * synchronised first (no enqueued work may still read or write the arrays), then the memory goes
+ * back through the allocator the store was created with.  ctx may be NULL (for example after
+ * mf_destroy); a store that a prefix cache owns is refused with MF_ERR_INVALID.
+ */
 mf_status mf_bsr_free(mf_ctx* ctx, mf_bsr* bsr);
 
 /*
@@ -308,6 +313,12 @@ mf_status mf_v_prepare(mf_ctx* ctx, const int32_t* cu_seqlens_host, int32_t n_se
                        const int32_t* page_table, int32_t page_size, int32_t pages_per_seq,
                        mf_vfrag* out, void* stream);
 
+/*
+ * Free what the library allocated for prepared V (its geometry tables and exponents, and frag
+ * unless the caller provided it) and zero *vf; caller-provided frag memory is left alone.  Same
+ * rules as mf_bsr_free: the device is synchronised first, the memory goes back through the
+ * allocator it came from, ctx may be NULL.
+ */
 mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf);
 
 /*
