@@ -93,7 +93,9 @@ struct RecvArgs {
 
 constexpr int kMaxRecv = 4;    // receivers per fused retrieve
 constexpr int kMaxSplit = 8;   // workgroups per row tile (head splits over all receivers)
-constexpr int kMaxSlots = 24;  // receiver heads per split (8 waves x 3)
+constexpr int kMaxSlots = 32;  // slot-table entries per split (8 waves x 4)
+constexpr int kSplitMax = 24;  // heads per split of the general schedule (8 waves x 3); 32 only for
+                               // the half-block fast path of one grouped-query receiver
 
 struct RetrieveArgs {
   const uint16_t* probs;
@@ -109,7 +111,7 @@ struct RetrieveArgs {
   int n_recv, n_split;
   int accumulate;        // 0: normalised output; across sender layers 1: write the unnormalised
                          // output and denominator, 2: add to them, 3: add and normalise
-  int HP;                                  // heads per wave: a split holds up to 8*HP heads
+  int HP;                                  // heads per wave (1..4): a split holds up to 8*HP heads
   int fast;                                // set by the launcher: straight-line fast path applies
   int8_t split_nslots[kMaxSplit];          // heads in each split; they fill its leading slots
   int8_t slot_recv[kMaxSplit][kMaxSlots];  // receiver of each slot

@@ -212,12 +212,18 @@ constexpr int ROWS_PER_WAVE = RT_ROWS / RT_WAVES;
 // make the 16-byte stage-2 reads (lane (a, c): row c, key chunk a) and stage-1 writes (lane (a,
 // c): head c, key chunk a) bank-conflict free on gfx950; with 32 receiver heads that padding
 // does not fit twice in LDS, so HP = 4 keeps 16-byte padding (2-way conflicts).
-template <int B, int HP>
+template <int B, int HP, bool HALF = false>
 struct AhatLayout {
   static constexpr bool kWide = HP <= 3;
   static constexpr int kRowBytes = kWide ? 160 : B * 2 + 16;
   static constexpr int kHeadBytes = RT_ROWS * kRowBytes + (kWide ? 32 : 0);
   static_assert(!kWide || B * 2 <= 160, "row must fit its stride");
+};
+// HALF: the mixed map of one 32-key half block at a time, 80-byte rows, 1296-byte heads
+template <int B, int HP>
+struct AhatLayout<B, HP, true> {
+  static constexpr int kRowBytes = 80;
+  static constexpr int kHeadBytes = RT_ROWS * kRowBytes + 16;
 };
 
 // Per-slot receiver data of a work item: the slot's weight row, its V operand tiles (KV head
@@ -241,7 +247,7 @@ struct SlotInfo {
 // one after the other, so every split after the first finds the P tile in that XCD's L2.  A
 // split's slots may hold heads of different receivers (a fan-out): each slot carries its own
 // weights, V and output.
-template <int B, int D, int HP, int KC, bool FAST>
+template <int B, int D, int HP, int KC, bool FAST, bool HALF = false>
 __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs args) {
   const uint16_t* __restrict__ probs = args.probs;
   const int32_t* __restrict__ block_ptr = args.block_ptr;
@@ -255,8 +261,9 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   constexpr int MT = B / 16;               // 16-key M-tiles per row
   constexpr int NCH = B / 32;              // 32-key chunks per block
   constexpr int NDT = D / 16;              // 16-column output tiles
-  constexpr int RB = AhatLayout<B, HP>::kRowBytes;
-  constexpr int GB = AhatLayout<B, HP>::kHeadBytes;
+  constexpr int RB = AhatLayout<B, HP, HALF>::kRowBytes;
+  constexpr int GB = AhatLayout<B, HP, HALF>::kHeadBytes;
+  static_assert(!HALF || (FAST && B == 64), "the half-block schedule is a fast path for B = 64");
   constexpr int HR_MAX = 8 * HP;
   constexpr int NTG = (HP + 1) / 2;        // 16-head N-tiles of the mix
   constexpr int HPW = HP;                  // stage 2: wave w owns slots w HP .. w HP + HP - 1
@@ -420,19 +427,22 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   // row's last block re-reads that block.  Conditional loads would make the compiler's wait
   // counts conservative, and vector-memory loads retire in order: a wait for a later load (a V
   // tile) would then also wait for the whole prefetch of the next block.
-  v4u pa[ROWS_PER_WAVE][MT][KC];
+  // HALF holds the M-tiles of one 32-key half block (2h, 2h + 1), else all of the block's.
+  constexpr int PM = HALF ? 2 : MT;
+  v4u pa[ROWS_PER_WAVE][PM][KC];
   size_t p_off[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) p_off[kc] = (size_t)min(4 * kc + a, HGp - 1) * B * B * 8;
-  auto load_p = [&](int t) {
+  auto load_p = [&](int t, int h = 0) {
     const uint16_t* pb = probs + (size_t)t * blk_elems;
 #pragma unroll
     for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
       const int r = row0 + ROWS_PER_WAVE * w + rr;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
+      for (int mt = 0; mt < PM; ++mt)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) pa[rr][mt][kc] = ld16_nt(pb + p_off[kc] + ((size_t)r * B + 16 * mt + c) * 8);
+        for (int kc = 0; kc < KC; ++kc)
+          pa[rr][mt][kc] = ld16_nt(pb + p_off[kc] + ((size_t)r * B + 16 * (mt + PM * h) + c) * 8);
     }
   };
   if (t0 < t1) load_p(t0);
@@ -448,12 +458,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     return vb + (((size_t)kbrow * NCH + ch) * NDT) * 512;
   };
   // ---- stage 1: head mix -> fp16 Ahat in LDS (rows of this wave, every head of the split) ----
+  // (HALF: the one 32-key chunk held in pa, into a half-block buffer)
+  constexpr int NCM = HALF ? 1 : NCH;
   auto mix = [&](unsigned char* buf) {
 #pragma unroll
     for (int rr = 0; rr < ROWS_PER_WAVE; ++rr) {
       const int ii = ROWS_PER_WAVE * w + rr;
 #pragma unroll
-      for (int ch = 0; ch < NCH; ++ch) {
+      for (int ch = 0; ch < NCM; ++ch) {
 #pragma unroll
         for (int nt = 0; nt < NTG; ++nt) {
           v4f mx[2];
@@ -492,7 +504,37 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   // next block are requested right after this block's last product with them, and the next
   // block's P right after the mix.  In issue order every wait of a block then covers only older
   // loads (vector-memory loads retire in order), and each load has a whole stage to land.
-  if constexpr (FAST) {
+  if constexpr (HALF) {
+    // 32 heads: a block as two 32-key halves, each with its own mixed-map buffer and barrier, so
+    // that only one half's P and V operands are held; the next half's are requested right after
+    // the mix and the products of this one
+    v8h vt[NDW];
+    auto load_v = [&](int t, int h) {
+      const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow0 + block_idx[t], h);
+#pragma unroll
+      for (int dt = 0; dt < NDW; ++dt) vt[dt] = as_v8h(ld16(vb + dt * 512));
+    };
+    if (t0 < t1) load_v(t0, 0);
+    for (int t = t0; t < t1; ++t) {
+      const int tn = min(t + 1, t1 - 1);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        unsigned char* buf = s_ahat[h];
+        mix(buf);
+        if (h == 0) load_p(t, 1);
+        else load_p(tn, 0);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < HPW; ++j) {
+          const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + a * 16));
+#pragma unroll
+          for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vt[dt], acc[j][dt]);
+        }
+        if (h == 0) load_v(t, 1);
+        else load_v(tn, 0);
+      }
+    }
+  } else if constexpr (FAST) {
     v8h vt[NCH][NDW];
     auto load_v = [&](int t, int ch) {
       const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow0 + block_idx[t], ch);
@@ -618,17 +660,26 @@ bool retrieve_supported(int B, int d, int H_r, int H_s) {
          H_s <= 64;
 }
 
-template <int B, int D, int HP, int KC, bool FAST>
+template <int B, int D, int HP, int KC, bool FAST, bool HALF = false>
 static hipError_t retrieve_t(const RetrieveArgs& a, hipStream_t s) {
   constexpr int NRT = B / RT_ROWS;
   const unsigned groups = (unsigned)((a.n_order + 7) / 8);
-  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC, FAST>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0, s, a);
+  hipLaunchKernelGGL((k_retrieve<B, D, HP, KC, FAST, HALF>), dim3(groups * 8 * NRT * a.n_split), dim3(RT_WAVES * 64), 0,
+                     s, a);
   return hipGetLastError();
 }
 
 template <int B, int D>
 static hipError_t retrieve_bd(const RetrieveArgs& a, hipStream_t s) {
   const int KC = ((a.H_s + 7) / 8 + 3) / 4;
+  // 4 heads per wave: only the half-block fast path (B = 64)
+  if (a.HP == 4) {
+    if constexpr (B == 64) {
+      if (a.fast && KC == 1) return retrieve_t<B, D, 4, 1, true, true>(a, s);
+      if (a.fast && KC == 2) return retrieve_t<B, D, 4, 2, true, true>(a, s);
+    }
+    return hipErrorInvalidValue;
+  }
   // the fast path does not fit the register file with 3 heads per wave and two head chunks
   if (a.fast && !(a.HP == 3 && KC == 2)) {
     switch (a.HP * 4 + KC) {
@@ -664,7 +715,7 @@ static bool slots_fast(const RetrieveArgs& a) {
 }
 
 hipError_t retrieve(const RetrieveArgs& a, hipStream_t s) {
-  if (a.n_recv < 1 || a.n_recv > kMaxRecv || a.n_split < 1 || a.n_split > kMaxSplit || a.HP < 1 || a.HP > 3)
+  if (a.n_recv < 1 || a.n_recv > kMaxRecv || a.n_split < 1 || a.n_split > kMaxSplit || a.HP < 1 || a.HP > 4)
     return hipErrorInvalidValue;
   for (int k = 0; k < a.n_split; ++k) {
     const int n = a.split_nslots[k];
