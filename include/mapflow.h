@@ -334,7 +334,9 @@ mf_status mf_vfrag_free(mf_ctx* ctx, mf_vfrag* vf);
  *   O                 fp32 [T][H_r][d] device; must not alias any input
  * Limits: H_r <= 48, H_s <= 64, d in {64, 128}, B in {32, 64}, vf geometry equal to the store's.
  * Above 24 receiver heads the heads are mixed by two workgroups per row tile (equal halves),
- * each reading the tile (the second read is served by L2).
+ * each reading the tile (the second read is served by L2), except for a receiver of exactly 32
+ * heads at B = 64 whose KV heads each serve a multiple of 4 query heads: one workgroup mixes all
+ * 32, taking each kept block as two 32-key halves.
  * Rows of the mixed map are rounded to fp16 (scaled by a power of two per receiver head) before
  * the V product; sums are fp32.
  */
@@ -352,10 +354,11 @@ mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W, i
  *   n_recv            1..4
  *   W, H_r, vf, kv_head_map_host, O   host arrays of n_recv entries; entry r has the meaning,
  *                     layout and limits of the same argument of mf_retrieve_prepared
- * All receivers share the head dimension d.  The heads of all receivers are cut into
- * ceil(sum H_r / 24) near-equal runs, one workgroup per run and row tile; a run may hold heads
- * of two receivers.  Outputs must not alias each other or any input.  Validation happens before
- * any launch: on an error nothing is written.
+ * All receivers share the head dimension d.  Each receiver's heads, in KV-head order, form one
+ * part of at most 24 heads, or two equal parts above 24; parts are packed first-fit, largest
+ * first, into workgroups of at most 24 heads per row tile (a workgroup may hold parts of several
+ * receivers), with one launch per width (heads per wave).  Outputs must not alias each other or
+ * any input.  Validation happens before any launch: on an error nothing is written.
  */
 mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_recv, const float* const* W,
                             const int32_t* H_r, const mf_vfrag* const* vf,
