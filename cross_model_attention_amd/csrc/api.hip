@@ -973,19 +973,21 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   // whatever its head count within one width, and the splits of one row tile only share the P
   // tile through L2 while they advance at the same rate, so splits are grouped by width
   // (HP = ceil(heads / 8)) and each group is one launch.
-  // One grouped-query receiver of 32 heads whose KV groups fill whole waves (4 heads each, in KV
-  // order) is the exception: it runs as a single 32-head split on the half-block fast path
-  // (B = 64), so its P tiles are read once per row tile.
-  bool one32 = n_recv == 1 && H_r[0] == 32 && bsr->B == 64;
-  for (int wv = 0; one32 && wv < 8; ++wv)
-    for (int i = 1; i < 4; ++i)
-      if (hm[0].kv[hm[0].perm[4 * wv + i]] != hm[0].kv[hm[0].perm[4 * wv]]) one32 = false;
-  const int split_cap = one32 ? 32 : mf::kSplitMax;
+  // A grouped-query receiver of 32 heads whose KV groups fill whole waves (4 heads each, in KV
+  // order) is the exception: it forms one 32-head part with a split of its own, run on the
+  // half-block fast path (B = 64), so its P tiles are read once per row tile.
+  bool whole32[mf::kMaxRecv];
+  for (int r = 0; r < n_recv; ++r) {
+    whole32[r] = H_r[r] == 32 && bsr->B == 64;
+    for (int wv = 0; whole32[r] && wv < 8; ++wv)
+      for (int i = 1; i < 4; ++i)
+        if (hm[r].kv[hm[r].perm[4 * wv + i]] != hm[r].kv[hm[r].perm[4 * wv]]) whole32[r] = false;
+  }
   struct Part { int r, g0, n; };
   Part parts[2 * mf::kMaxRecv];
   int n_parts = 0;
   for (int r = 0; r < n_recv; ++r) {
-    const int halves = H_r[r] <= split_cap ? 1 : 2;
+    const int halves = (H_r[r] <= mf::kSplitMax || whole32[r]) ? 1 : 2;
     for (int p = 0, g0 = 0; p < halves; ++p) {
       const int n = H_r[r] / halves + (p < H_r[r] % halves ? 1 : 0);
       parts[n_parts++] = Part{r, g0, n};
@@ -996,7 +998,8 @@ static mf_status retrieve_launch(mf_ctx* ctx, const mf_bsr* bsr, int n_recv, con
   int split_of[2 * mf::kMaxRecv], split_heads[2 * mf::kMaxRecv], n_split = 0;
   for (int i = 0; i < n_parts; ++i) {
     int k = 0;
-    while (k < n_split && split_heads[k] + parts[i].n > split_cap) ++k;
+    // a part above kSplitMax heads (a whole 32-head receiver) opens a split that nothing joins
+    while (k < n_split && (split_heads[k] + parts[i].n > mf::kSplitMax)) ++k;
     if (k == n_split) split_heads[n_split++] = 0;
     split_heads[k] += parts[i].n;
     split_of[i] = k;
