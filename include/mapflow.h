@@ -355,9 +355,11 @@ mf_status mf_retrieve_prepared(mf_ctx* ctx, const mf_bsr* bsr, const float* W, i
  *   W, H_r, vf, kv_head_map_host, O   host arrays of n_recv entries; entry r has the meaning,
  *                     layout and limits of the same argument of mf_retrieve_prepared
  * All receivers share the head dimension d.  Each receiver's heads, in KV-head order, form one
- * part of at most 24 heads, or two equal parts above 24; parts are packed first-fit, largest
- * first, into workgroups of at most 24 heads per row tile (a workgroup may hold parts of several
- * receivers), with one launch per width (heads per wave).  Outputs must not alias each other or
+ * part of at most 24 heads, or two equal parts above 24 (a 32-head receiver that one workgroup
+ * mixes alone, as described for mf_retrieve_prepared, stays one part with a workgroup of its
+ * own); parts are packed first-fit, largest first, into workgroups of at most 24 heads per row
+ * tile (a workgroup may hold parts of several receivers), with one launch per width (heads per
+ * wave).  Outputs must not alias each other or
  * any input.  Validation happens before any launch: on an error nothing is written.
  */
 mf_status mf_retrieve_multi(mf_ctx* ctx, const mf_bsr* bsr, int32_t n_recv, const float* const* W,

@@ -191,7 +191,8 @@ def test_retrieve_on_oracle_store(mf, case):
 
 
 @pytest.mark.parametrize("case", [
-    # 14B-like sender fanned out to an 8B-like receiver (two head parts) and two small ones
+    # 14B-like sender fanned out to an 8B-like receiver (one 32-head part on the half-block path)
+    # and two small ones
     dict(wl="varlen_14b8b", seed=2, lengths=[260, 45], H_s=40, d=128, recv=[(32, 8), (16, 2), (5, 5)]),
     # 24 heads (one part) next to 48 heads (two parts), both at 3 heads per wave
     dict(wl="pair_8b3b_8k", seed=5, lengths=[300], H_s=32, d=128, recv=[(24, 8), (48, 8)]),
