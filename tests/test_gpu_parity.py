@@ -166,6 +166,10 @@ def _upload_oracle_store(mf, ref, x):
     dict(wl="pair_8b3b_8k", seed=3, lengths=[190], heads=(8, 5, 5, 128)),
     dict(wl="pair_8b3b_8k", seed=4, lengths=[170, 33], heads=(16, 48, 8, 64)),   # 48 heads: split
     dict(wl="varlen_14b8b", seed=1, lengths=[150], heads=(40, 25, 5, 128)),      # split, 1 head left
+    # 32 heads: one half-block workgroup (KV groups of 4), or two 16-head splits (KV groups of 2)
+    dict(wl="pair_8b3b_8k", seed=11, lengths=[260, 3, 129], heads=(32, 32, 4, 128)),
+    dict(wl="varlen_14b8b", seed=12, lengths=[211], heads=(40, 32, 16, 128)),
+    dict(wl="pair_8b3b_8k", seed=13, lengths=[160], heads=(48, 32, 8, 64)),
 ])
 def test_retrieve_on_oracle_store(mf, case):
     wl = synth.WORKLOADS[case["wl"]]
