@@ -6,7 +6,8 @@
 // of sender heads into receiver heads in on-chip memory, multiplies by the receiver's own V and
 // accumulates, writing only the output.  Neither the dense map nor the mixed map touches HBM.
 //
-// k_retrieve, one workgroup (8 waves) per (block row, 16-row tile), all receiver heads:
+// k_retrieve, one workgroup (8 waves) per (block row, 16-row tile, head split); a split holds up
+// to 24 receiver heads, or 32 on the half-block path (each block taken as two 32-key halves):
 //   for each kept block J of the row, in column order:
 //     stage 1  head mix on MFMA (bf16): Ahat[g, i, j] = sum_h Ws[g, h] P[h, i, j] for the 16 rows
 //              x B keys, where Ws = W * 2^s_g is split into bf16 hi + lo parts so the product
@@ -267,7 +268,6 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   constexpr int HR_MAX = 8 * HP;
   constexpr int NTG = (HP + 1) / 2;        // 16-head N-tiles of the mix
   constexpr int HPW = HP;                  // stage 2: wave w owns slots w HP .. w HP + HP - 1
-  constexpr int NDW = NDT;
 
   __shared__ __attribute__((aligned(16))) unsigned char s_ahat[2][HR_MAX * GB];
   __shared__ float s_den[HR_MAX][RT_ROWS];
@@ -406,15 +406,15 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   }
 
   // stage-2 ownership: local slots s0 .. s0+HPW-1, all output tiles
-  const int s0 = w * HPW, dt0 = 0;
+  const int s0 = w * HPW;
   int sg[HPW];
 #pragma unroll
   for (int j = 0; j < HPW; ++j) sg[j] = head_of(s0 + j);
-  v4f acc[HPW][NDW];
+  v4f acc[HPW][NDT];
 #pragma unroll
   for (int j = 0; j < HPW; ++j)
 #pragma unroll
-    for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = zero4();
+    for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = zero4();
 
   const int t0 = (int)min((int64_t)block_ptr[brow], capacity);
   const int t1 = (int)min((int64_t)block_ptr[brow + 1], capacity);
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   // so their latency hides under it; later chunks and other V heads are loaded on use.
   const MF_GLOBAL uint16_t* vj[HPW];
 #pragma unroll
-  for (int j = 0; j < HPW; ++j) vj[j] = s_slot[s0 + j].v + lane * 8 + dt0 * 512;
+  for (int j = 0; j < HPW; ++j) vj[j] = s_slot[s0 + j].v + lane * 8;
   const MF_GLOBAL uint16_t* const v0 = vj[0];
   auto vtile = [&](const MF_GLOBAL uint16_t* vb, int kbrow, int ch) {
     return vb + (((size_t)kbrow * NCH + ch) * NDT) * 512;
@@ -508,11 +508,11 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     // 32 heads: a block as two 32-key halves, each with its own mixed-map buffer and barrier, so
     // that only one half's P and V operands are held; the next half's are requested right after
     // the mix and the products of this one
-    v8h vt[NDW];
+    v8h vt[NDT];
     auto load_v = [&](int t, int h) {
       const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow0 + block_idx[t], h);
 #pragma unroll
-      for (int dt = 0; dt < NDW; ++dt) vt[dt] = as_v8h(ld16(vb + dt * 512));
+      for (int dt = 0; dt < NDT; ++dt) vt[dt] = as_v8h(ld16(vb + dt * 512));
     };
     if (t0 < t1) load_v(t0, 0);
     for (int t = t0; t < t1; ++t) {
@@ -528,18 +528,18 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
         for (int j = 0; j < HPW; ++j) {
           const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + a * 16));
 #pragma unroll
-          for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vt[dt], acc[j][dt]);
+          for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vt[dt], acc[j][dt]);
         }
         if (h == 0) load_v(t, 1);
         else load_v(tn, 0);
       }
     }
   } else if constexpr (FAST) {
-    v8h vt[NCH][NDW];
+    v8h vt[NCH][NDT];
     auto load_v = [&](int t, int ch) {
       const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow0 + block_idx[t], ch);
 #pragma unroll
-      for (int dt = 0; dt < NDW; ++dt) vt[ch][dt] = as_v8h(ld16(vb + dt * 512));
+      for (int dt = 0; dt < NDT; ++dt) vt[ch][dt] = as_v8h(ld16(vb + dt * 512));
     };
     if (t0 < t1) {
 #pragma unroll
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
         for (int j = 0; j < HPW; ++j) {
           const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + (ch * 4 + a) * 16));
 #pragma unroll
-          for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vt[ch][dt], acc[j][dt]);
+          for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vt[ch][dt], acc[j][dt]);
         }
         load_v(tn, ch);
       }
@@ -568,11 +568,11 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     unsigned char* buf = s_ahat[(t - t0) & 1];
     const int J = block_idx[t];
     const int kbrow = kbrow0 + J;
-    v8h vpre[NCH][NDW];
+    v8h vpre[NCH][NDT];
     {
       const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, 0);
 #pragma unroll
-      for (int dt = 0; dt < NDW; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
+      for (int dt = 0; dt < NDT; ++dt) vpre[0][dt] = as_v8h(ld16(vb + dt * 512));
     }
     mix(buf);
     load_p(min(t + 1, t1 - 1));
@@ -583,24 +583,24 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
       if (ch > 0) {
         const MF_GLOBAL uint16_t* vb = vtile(v0, kbrow, ch);
 #pragma unroll
-        for (int dt = 0; dt < NDW; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
+        for (int dt = 0; dt < NDT; ++dt) vpre[ch][dt] = as_v8h(ld16(vb + dt * 512));
       }
 #pragma unroll
       for (int j = 0; j < HPW; ++j) {
         const int g = sg[j];
         if (g < 0) continue;
-        v8h vop[NDW];
+        v8h vop[NDT];
         if (vj[j] == v0) {
 #pragma unroll
-          for (int dt = 0; dt < NDW; ++dt) vop[dt] = vpre[ch][dt];
+          for (int dt = 0; dt < NDT; ++dt) vop[dt] = vpre[ch][dt];
         } else {
           const MF_GLOBAL uint16_t* vb = vtile(vj[j], kbrow, ch);
 #pragma unroll
-          for (int dt = 0; dt < NDW; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
+          for (int dt = 0; dt < NDT; ++dt) vop[dt] = as_v8h(ld16(vb + dt * 512));
         }
         const v8h aop = as_v8h(*reinterpret_cast<const v4u*>(buf + (s0 + j) * GB + c * RB + (ch * 4 + a) * 16));
 #pragma unroll
-        for (int dt = 0; dt < NDW; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
+        for (int dt = 0; dt < NDT; ++dt) acc[j][dt] = mfma_f16(aop, vop[dt], acc[j][dt]);
       }
     }
   }
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
         const float inv = unscale / s_den[s0 + j][ii];
         MF_GLOBAL float* orow = si.o + (size_t)(bi.tok0 + row0 + ii) * si.ostride;
 #pragma unroll
-        for (int dt = 0; dt < NDW; ++dt) orow[16 * (dt0 + dt) + c] = acc[j][dt][i] * inv;
+        for (int dt = 0; dt < NDT; ++dt) orow[16 * dt + c] = acc[j][dt][i] * inv;
       }
     } else {
       // cross-layer mix: this layer's unnormalised output and denominator in true units (the
@@ -642,14 +642,14 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
         const float num = unscale * wun;
         const float inv = mode == 3 ? 1.f / den : 1.f;
 #pragma unroll
-        for (int dt = 0; dt < NDW; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
           float v = acc[j][dt][i] * num;
-          if (mode >= 2) v += orow[16 * (dt0 + dt) + c];
-          orow[16 * (dt0 + dt) + c] = v * inv;
+          if (mode >= 2) v += orow[16 * dt + c];
+          orow[16 * dt + c] = v * inv;
         }
-        // modes 1 and 2 only store the denominator (one wave of the slot does), mode 3 only
-        // reads it: with the columns split over two waves neither reads the other's store
-        if (mode != 3 && dt0 == 0 && c == 0) *dp = den;
+        // modes 1 and 2 store the running denominator (lane column 0 of the slot's wave), mode 3
+        // only reads it
+        if (mode != 3 && c == 0) *dp = den;
       }
     }
   }
