@@ -96,52 +96,59 @@ def traffic_from_profile(kernel_src, workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, args, mapped_layers, n_mapped, recompute_layers):
-    """The oracle as it stands, on a bounded stratified sample of block rows of one layer pair at
-    the full sequence length, extrapolated by per-row work (rows cost proportional to I + 1) to
-    the whole step.  Labelled as a sampled extrapolation."""
-    import threadpoolctl
-
+def cpu_baseline(torch, wl, args, store, send_qk, recv_map, recv_dense, kv_map, n_mapped, n_recompute):
+    """The oracle as it stands, on a bounded stratified sample of block rows of the last mapped
+    layer pair at the full sequence length, on the benchmark's own device inputs; extrapolated by
+    per-row work (rows cost proportional to I + 1) to the whole step and labelled as a sampled
+    extrapolation.  The same rows of the GPU's store and output, and one block row of the first
+    recomputed layer's dense attention, are then compared with the oracle's (untimed)."""
     import oracle
-    import synth
 
     L, B = wl.seq_len, wl.B
     nb = (L + B - 1) // B
-    x = synth.make_layer_inputs(wl, args.seed, layer=mapped_layers[0])
-    Q = x["q_s"].astype(np.float64)
-    K = x["k_s"].astype(np.float64)
     tau = float(np.float32(wl.tau))
     step = max(1, nb // max(args.cpu_rows, 1))
     rows = [min(nb - 1, step // 2 + k * step) for k in range(args.cpu_rows)]
-    threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
-                  if i.get("user_api") == "blas") or len(os.sched_getaffinity(0))
-    t0 = time.perf_counter()
-    units = 0
-    for I in rows:
-        r = oracle.block_row_compress(Q, K, 0, L, I, B, tau)
-        oracle.retrieve_block_row(r["probs"], B, r["rows"], r["tok0"], 0, 0, L, x["w"], x["v_r"],
-                                  x["kv_head_map"])
-        units += I + 1
-    t_pair = time.perf_counter() - t0
-    d = synth.make_dense_inputs(wl, args.seed, layer=0, lengths=[L])
-    I = rows[len(rows) // 2]
-    t1 = time.perf_counter()
-    r0, r1 = I * B, min(L, (I + 1) * B)
-    for g in range(wl.H_r):
-        kv = g // (wl.H_r // wl.H_kv)
-        A, _ = oracle.attention_rows(d["q"][:, g].astype(np.float64), d["k"][:, kv].astype(np.float64), r0, r1)
-        _ = A @ d["v"][:r1, kv].astype(np.float64)
-    t_dense = time.perf_counter() - t1
+    cu = np.array([0, L], dtype=np.int64)
+    t_pair, units, check = oracle_sample(torch, wl, [(0, I) for I in rows], cu, tau, send_qk[0], send_qk[1],
+                                         recv_map["w"], recv_map["v"], kv_map, store, recv_map["o"])
+    est_dense, t_dense = 0.0, 0.0
+    if recv_dense is not None:
+        I = rows[len(rows) // 2]
+        r0, r1 = I * B, min(L, (I + 1) * B)
+        host = lambda t: t.float().cpu().numpy().astype(np.float64)
+        q, k, v = host(recv_dense["q"][:r1]), host(recv_dense["k"][:r1]), host(recv_dense["v"][:r1])
+        ref = np.zeros((r1 - r0, wl.H_r, wl.d))
+        t1 = time.perf_counter()
+        for g in range(wl.H_r):
+            A, _ = oracle.attention_rows(q[:, g], k[:, kv_map[g]], r0, r1)
+            ref[:, g] = A @ v[:r1, kv_map[g]]
+        t_dense = time.perf_counter() - t1
+        est_dense = n_recompute * (nb * (nb + 1) // 2) * (t_dense / (I + 1))
+        got = recv_dense["o"][r0:r1].double().cpu().numpy()
+        check["dense_recompute"] = dict(_errors(got, ref), block_row=I)
+        check["pass"] = check["pass"] and _within(check["dense_recompute"])
     full_units = nb * (nb + 1) // 2
-    est = n_mapped * full_units * (t_pair / units) + len(recompute_layers) * full_units * (t_dense / (I + 1))
-    return {"value": L / est, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, compress + retrieve of block rows {rows} of one L={L} layer "
-                       f"pair ({units} row-block units, {t_pair:.1f} s) and dense attention of block row "
-                       f"{I} of one recomputed layer ({t_dense:.1f} s), extrapolated by per-row work to "
-                       f"{n_mapped} mapped + {len(recompute_layers)} recomputed layers "
-                       f"(est. {est:.0f} s per step)"),
-            "extrapolated": True, "cpu_model": _cpu_model(),
-            "usable_cpus": len(os.sched_getaffinity(0))}
+    est = n_mapped * full_units * (t_pair / units) + est_dense
+    base = {"value": L / est, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle on the benchmark's own inputs: compress + retrieve of block rows {rows} "
+                       f"of the last mapped L={L} layer pair ({units} row-block units, {t_pair:.1f} s) and dense "
+                       f"attention of one block row of a recomputed layer ({t_dense:.1f} s), extrapolated by per-row "
+                       f"work to {n_mapped} mapped + {n_recompute} recomputed layers (est. {est:.0f} s per step)"),
+            "extrapolated": True, "cpu_model": _cpu_model(), "usable_cpus": len(os.sched_getaffinity(0))}
+    return base, check
+
+
+O_REL_FRO, O_MAX_ABS = 1e-3, 5e-3      # output tolerance against the oracle (relative Frobenius, max abs)
+
+
+def _errors(got, ref):
+    return {"rel_fro": float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)),
+            "max_abs": float(np.abs(got - ref).max()) if ref.size else 0.0}
+
+
+def _within(e):
+    return e["rel_fro"] <= O_REL_FRO and e["max_abs"] <= O_MAX_ABS
 
 
 def _cpu_model():
@@ -303,42 +310,69 @@ def _paged_pool_torch(torch, V, lengths, table, page_size, n_pages):
     return pool.view(n_pages, page_size, *V.shape[1:])
 
 
-def oracle_rows(wl, seed, picks, tau):
-    """The oracle (compress + retrieve of one block row) on sampled block rows of a workload.
+def oracle_sample(torch, wl, picks, cu, tau, q, k, w, v, kv_map, store, O, page=None):
+    """The oracle (fp64 compress + retrieve of one block row) on sampled block rows of the
+    benchmark's own device inputs, timed on the host cores; then the GPU's kept sets and output
+    rows of the same block rows compared with it (untimed).
 
-    picks: list of (sequence length n, block row I).  The inputs of a row are drawn with the
-    workload's recipe (planted keys, Dirichlet W, N(0,1) V) at the row's own shape: its queries
-    and every key up to the end of the row, per head, so that the oracle's work equals that of
-    the same row of the full workload.  Returns (seconds, work units = sum of I + 1)."""
+    picks: (sequence s, block row I).  The oracle gets each sampled sequence's tokens up to the end
+    of its last sampled row, so its work equals that of the same rows of the full workload.
+    q, k: [H_s, T, d]; w: [H_r, H_s]; v: V_r [T, H_kv, d], or with page = (table, page_size) the page
+    pool [n_pages, page_size, H_kv, d].  The outputs are compared twice: with the oracle's retrieve on
+    its own kept blocks, and on the blocks the GPU stored (a comparison that a tie at the selection
+    boundary cannot move).  Returns (seconds, work units = sum of I + 1, check)."""
     import oracle
 
-    H_s, d, B = wl.H_s, wl.d, wl.B
-    rng = np.random.default_rng(np.random.SeedSequence([seed, 7777]))
-    a = 0.75 * math.sqrt(d)
-    kv = np.array([g // (wl.H_r // wl.H_kv) for g in range(wl.H_r)], dtype=np.int32)
-    W = rng.dirichlet(np.full(H_s, 0.5), size=wl.H_r)
-    seconds, units = 0.0, 0
-    for n in sorted({n for n, _ in picks}):
-        rows_here = [I for m, I in picks if m == n]
-        r1max = min(n, (max(rows_here) + 1) * B)
-        u = rng.standard_normal((H_s, d))
-        u /= np.linalg.norm(u, axis=1, keepdims=True)
-        K = rng.standard_normal((H_s, r1max, d), dtype=np.float32)
-        hot = np.concatenate([[0], rng.choice(np.arange(1, max(r1max, 2)), size=int(round(wl.hot_frac * r1max)),
-                                              replace=False)])
-        K[:, hot, :] += (a * u[:, None, :]).astype(np.float32)
-        Q = np.zeros_like(K)
-        V = rng.standard_normal((r1max, wl.H_kv, d), dtype=np.float32)
-        for I in rows_here:
-            r0, r1 = I * B, min(n, (I + 1) * B)
-            Q[:, r0:r1] = rng.standard_normal((H_s, r1 - r0, d), dtype=np.float32) + (a * u[:, None, :])
+    B = wl.B
+    host = lambda t: t.float().cpu().numpy()
+    W = host(w).astype(np.float64)
+    kvm = np.asarray(kv_map, dtype=np.int32)
+    table, psz = page if page is not None else (None, 16)
+    pool = host(v) if page is not None else None
+    ptr = store.meta_to_host()["block_ptr"]
+    nb = [(int(cu[s + 1] - cu[s]) + B - 1) // B for s in range(len(cu) - 1)]
+    first = np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
+    seconds, units, same, other = 0.0, 0, 0, []
+    acc = {"own": [0.0, 0.0, 0.0], "gpu": [0.0, 0.0, 0.0]}      # squared error, squared reference, max
+    for s in sorted({s for s, _ in picks}):
+        rows_here = sorted(I for t, I in picks if t == s)
+        c0, n = int(cu[s]), int(cu[s + 1] - cu[s])
+        r1max = min(n, (rows_here[-1] + 1) * B)
+        Q = host(q[:, c0:c0 + r1max]).astype(np.float64)
+        K = host(k[:, c0:c0 + r1max]).astype(np.float64)
+        V = pool if page is not None else host(v[c0:c0 + r1max])
+        done = []
         t0 = time.perf_counter()
         for I in rows_here:
-            r = oracle.block_row_compress(Q, K, 0, min(n, r1max), I, B, tau)
-            oracle.retrieve_block_row(r["probs"], B, r["rows"], r["tok0"], 0, 0, min(n, r1max), W, V, kv)
+            r = oracle.block_row_compress(Q, K, 0, r1max, I, B, tau)
+            o = oracle.retrieve_block_row(r["probs"], B, r["rows"], r["tok0"], s, 0, r1max, W, V, kvm, table, psz)
+            done.append((I, r, o))
             units += I + 1
         seconds += time.perf_counter() - t0
-    return seconds, units
+        for I, r, o in done:
+            b = int(first[s]) + I
+            lo, hi = int(ptr[b]), int(ptr[b + 1])
+            blk = store.blocks_to_host(lo, hi - lo)
+            kept = blk["block_idx"].tolist()
+            if kept == list(r["kept"]):
+                same += 1
+            else:
+                other.append([s, I])
+            og = oracle.retrieve_block_row({J: blk["probs"][t] for t, J in enumerate(kept)}, B, r["rows"],
+                                           r["tok0"], s, 0, r1max, W, V, kvm, table, psz)
+            g = O[c0 + r["tok0"]: c0 + r["tok0"] + r["rows"]].double().cpu().numpy()
+            for key, ref in (("own", o), ("gpu", og)):
+                e = acc[key]
+                e[0] += float(((g - ref) ** 2).sum())
+                e[1] += float((ref ** 2).sum())
+                e[2] = max(e[2], float(np.abs(g - ref).max()))
+        del Q, K
+    err = {key: {"rel_fro": (e[0] / max(e[1], 1e-300)) ** 0.5, "max_abs": e[2]} for key, e in acc.items()}
+    check = {"block_rows": len(picks), "kept_sets_identical": same, "rows_with_other_sets": other,
+             "O_vs_oracle": err["own"], "O_vs_oracle_on_gpu_blocks": err["gpu"],
+             "tolerance": {"rel_fro": O_REL_FRO, "max_abs": O_MAX_ABS}}
+    check["pass"] = _within(err["own"]) and _within(err["gpu"])
+    return seconds, units, check
 
 
 def bench_single(mf, torch, wl, args, ctx, dev, read_gbs=None, reps=10):
@@ -407,29 +441,32 @@ def bench_single(mf, torch, wl, args, ctx, dev, read_gbs=None, reps=10):
     }
     log(f"{wl.name}: T={T} nnzb={nnzb} density {nnzb / n_causal:.4f}; retrieve {ms:.3f} ms "
         f"({gbs:.0f} GB/s, {gbs / HBM_PEAK_GBS:.3f} of peak); compress {cp_ms:.2f} ms; V prep {res['v_prepare_ms']:.3f} ms")
-    del store, pv, O, Q, K, Vin, x, r
     if not args.no_cpu_baseline:
         nb = [(n + B - 1) // B for n in lengths]
         if len(lengths) == 1 and nb[0] > 512:
             # long rows cost up to seconds each: a bounded spread over the first half
-            picks = [(lengths[0], I) for I in sorted({0, nb[0] // 8, nb[0] // 4, nb[0] // 2})]
+            picks = [(0, I) for I in sorted({0, nb[0] // 8, nb[0] // 4, nb[0] // 2})]
         elif len(lengths) == 1:
-            picks = [(lengths[0], I) for I in sorted({0, nb[0] // 4, nb[0] // 2, (3 * nb[0]) // 4, nb[0] - 1})]
+            picks = [(0, I) for I in sorted({0, nb[0] // 4, nb[0] // 2, (3 * nb[0]) // 4, nb[0] - 1})]
         else:
             order = np.argsort(lengths)
             picks = []
             for s in (int(order[0]), int(order[len(order) // 2]), int(order[-1])):
-                picks += [(lengths[s], I) for I in sorted({0, nb[s] // 2, nb[s] - 1})]
-        sec, units = oracle_rows(wl, seed, picks, tau)
+                picks += [(s, I) for I in sorted({0, nb[s] // 2, nb[s] - 1})]
+        sec, units, check = oracle_sample(torch, wl, picks, cu, tau, Q, K, W, Vin, kv_map, store, O,
+                                          page=(table, wl.page_size) if wl.paged else None)
         total_units = sum(b * (b + 1) // 2 for b in nb)
         est = sec * total_units / units
         res["cpu_baseline"] = {
             "value": T / est, "unit": "tokens/s", "cores": _blas_threads(), "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, compress + retrieve of {len(picks)} block rows (sequence length, row) "
-                       f"{picks} ({units} row-block units, {sec:.1f} s), extrapolated by per-row work to all "
-                       f"{total_units} units of the layer (est. {est:.0f} s)"),
+            "sample": (f"fp64 numpy oracle on the benchmark's own inputs, compress + retrieve of {len(picks)} block "
+                       f"rows (sequence, row) {picks} ({units} row-block units, {sec:.1f} s), extrapolated by per-row "
+                       f"work to all {total_units} units of the layer (est. {est:.0f} s)"),
             "extrapolated": True}
-        log(f"{wl.name}: oracle sample {sec:.1f} s, est. {est:.0f} s per layer")
+        res["oracle_check"] = check
+        log(f"{wl.name}: oracle sample {sec:.1f} s, est. {est:.0f} s per layer; outputs against the oracle: "
+            f"{'pass' if check['pass'] else 'FAIL'} ({json.dumps(check)})")
+    del store, pv, O, Q, K, Vin, x, r
     return res
 
 
@@ -625,6 +662,15 @@ def main():
                             "TFLOPs": dense_flops / (dense_ms * 1e-3) / 1e12 if dense_ms > 0 else 0.0},
     }
 
+    if not args.no_cpu_baseline and n_map >= 1:
+        log("timing the oracle on a sample of the last mapped layer's block rows (CPU)")
+        last = mapped[-1]
+        out["cpu_baseline"], out["oracle_check"] = cpu_baseline(
+            torch, wl, args, slots[(n_map - 1) % k], send[pi[last]], recv[last],
+            recv[recompute[0]] if recompute else None, kv_map, n_map, len(recompute))
+        log(f"outputs against the oracle: {'pass' if out['oracle_check']['pass'] else 'FAIL'} "
+            f"({json.dumps(out['oracle_check'])})")
+
     if args.overlap:
         # same work, retrieves beside the compresses of later layers; outputs must not change
         ref = {l: recv[l]["o"].clone() for l in range(n_recv)}
@@ -707,9 +753,6 @@ def main():
             out["configs"][name] = bench_single(mf, torch, synth.WORKLOADS[name], args, ctx, dev, read_gbs)
             torch.cuda.synchronize()
 
-    if not args.no_cpu_baseline:
-        log("timing the oracle on a sample (CPU)")
-        out["cpu_baseline"] = cpu_baseline(wl, args, mapped, n_map, recompute)
     print(json.dumps(out), flush=True)
 
 

@@ -170,6 +170,9 @@ def _upload_oracle_store(mf, ref, x):
     dict(wl="pair_8b3b_8k", seed=11, lengths=[260, 3, 129], heads=(32, 32, 4, 128)),
     dict(wl="varlen_14b8b", seed=12, lengths=[211], heads=(40, 32, 16, 128)),
     dict(wl="pair_8b3b_8k", seed=13, lengths=[160], heads=(48, 32, 8, 64)),
+    # 33..48 sender heads: the last head chunk's hi and lo weights share one product
+    dict(wl="varlen_14b8b", seed=14, lengths=[190, 40], heads=(36, 8, 8, 128)),
+    dict(wl="varlen_14b8b", seed=15, lengths=[230], heads=(44, 16, 4, 64)),
 ])
 def test_retrieve_on_oracle_store(mf, case):
     wl = synth.WORKLOADS[case["wl"]]

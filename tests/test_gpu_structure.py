@@ -7,7 +7,10 @@ oracle comparisons of test_gpu_parity.py:
   mixed map of receiver head g at key j0 + c, so the on-chip mixed map itself is compared with
   the oracle's (not only its products with V);
 * permuting the sender heads (Q, K and the columns of W together) leaves the output unchanged up
-  to rounding: the GPU's head mix depends on the heads only through W.
+  to rounding: the GPU's head mix depends on the heads only through W;
+* weights that bf16 cannot hold (the mix multiplies the bf16 probabilities by a bf16 hi part and
+  a bf16 lo part of each weight) still enter the read-out mixed map to fp16 precision, whichever
+  path the receiver's heads take and whichever head chunk the weight falls in.
 
 [MapFlow开源, section 算得省的:融合内核执行]: the kernel mixes the sender heads linearly on chip,
 renormalises the rows and multiplies by the receiver's own V.
@@ -98,3 +101,38 @@ def test_sender_head_permutation_invariance(mf):
     assert_out_close(Op.cpu().numpy(),
                      oracle.retrieve(gpu_store_for_oracle(h, x["cu_seqlens"], wl.B, x["H_s"]), x["w"], x["v_r"],
                                      x["kv_head_map"]), "O_r (permuted) vs the oracle")
+
+
+# (H_s, H_r, H_kv, d): 8 heads of one KV group (one head per wave), 32 heads in KV groups of 4
+# (the half-block path), 16 heads in KV groups of 4 with a last chunk of two 8-head groups, and 13
+# heads of 13 KV groups (no two heads of a wave share V: the general path)
+@pytest.mark.parametrize("heads", [(40, 8, 1, 128), (40, 32, 8, 128), (44, 16, 4, 64), (44, 13, 13, 128)])
+def test_mix_keeps_the_weights_low_bits(mf, heads):
+    H_s, H_r, H_kv, d = heads
+    wl, x, tau = _case(44, [300, 90], H_s, H_r, H_kv, d)
+    say(f"case: low weight bits heads={heads}")
+    store = _compress(mf, x, tau, wl.B)
+    host = store.to_host()
+    # receiver head g mixes sender head g mod 32 with weight 1/2 + 2^-10 and sender head
+    # 32 + g mod (H_s - 32) (in the last chunk) with weight 1 + 2^-8 + 2^-12: bf16 rounds them to
+    # 1/2 and 1 + 2^-7, relative errors 2e-3 and 3.7e-3, eight times the fp16 rounding of the map
+    W = np.zeros((H_r, H_s), dtype=np.float32)
+    for g in range(H_r):
+        W[g, g % 32] = 0.5 + 2.0 ** -10
+        W[g, 32 + g % (H_s - 32)] = 1.0 + 2.0 ** -8 + 2.0 ** -12
+    T, cu, j0 = x["T"], x["cu_seqlens"], 64
+    V = np.zeros((T, H_kv, d), dtype=np.float32)
+    for s in range(len(cu) - 1):
+        for c in range(d):
+            if j0 + c < cu[s + 1] - cu[s]:
+                V[cu[s] + j0 + c, :, c] = 1.0
+    O = mf.retrieve(store, to_dev(W), to_dev(V, "bf16"), x["kv_head_map"])
+    torch.cuda.synchronize()
+    got = O.cpu().numpy().astype(np.float64)
+    want = oracle.retrieve(gpu_store_for_oracle(host, cu, wl.B, H_s), W, V, x["kv_head_map"])
+    # each read-out value is one fp16-rounded mixed-map element over an fp32 denominator: within
+    # 2^-11 relative (half an fp16 ulp) plus fp32 rounding
+    err = np.abs(got - want)
+    bound = 5.2e-4 * np.abs(want) + 1e-9
+    assert np.count_nonzero(want) > 1000
+    assert np.all(err <= bound), f"worst relative error {float((err / (np.abs(want) + 1e-30)).max()):.3e}"
