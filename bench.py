@@ -60,6 +60,8 @@ def parse():
                         "share the GPU with later compresses (reported under 'overlap')")
     p.add_argument("--read-probe-bytes", type=int, default=4 << 30,
                    help="size of the HBM read probe run after the timed steps (0 = skip)")
+    p.add_argument("--write-probe-bytes", type=int, default=20480 * 204800,
+                   help="bytes written by the HBM write probe run after the timed steps (0 = skip)")
     p.add_argument("--no-configs", action="store_true",
                    help="skip the single-layer measurements of the other workloads (8B->3B at L=8192, "
                         "the 14B->8B varlen batch with paged V, L=131072 at ~5%% density)")
@@ -729,6 +731,30 @@ def main():
         out["hbm_read_probe"] = {"bytes_read": n * 4, "GB_per_s": read_gbs}
         out["roofline"]["frac_of_read_ceiling"] = achieved / read_gbs if read_gbs > 0 else None
         del src, sink
+
+    if args.write_probe_bytes >= 20480:
+        # write ceilings: coalesced non-temporal stores alone, and with one 16-byte read per five
+        # written (the gather's mix of probability stores and key reads)
+        nb = args.write_probe_bytes // 20480 * 20480
+        dst = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+        src = torch.ones(nb // 20, dtype=torch.int32, device=dev)
+        res = {}
+        for name, s_in in (("writes_only", None), ("one_read_per_five_writes", src)):
+            mf.write_probe(dst, s_in)
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            reps = 10
+            for _ in range(reps):
+                mf.write_probe(dst, s_in)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            rd = 0 if s_in is None else nb // 5
+            res[name] = {"bytes_written": nb, "bytes_read": rd, "write_GB_per_s": nb / (ms * 1e-3) / 1e9,
+                         "total_GB_per_s": (nb + rd) / (ms * 1e-3) / 1e9}
+        out["hbm_write_probe"] = res
+        del src, dst
 
     if args.extras and n_map >= 1:
         out["prefill"] = prefill(mf, torch, wl, args, send[pi[mapped[-1]]], slots[(n_map - 1) % k], tau, ctx, dev)

@@ -15,6 +15,7 @@ from .mapflow import (  # noqa: F401
     compress_prefill_into,
     copy_probe,
     read_probe,
+    write_probe,
     dense_attention,
     layer_map_uniform,
     map_layers,

@@ -1680,4 +1680,14 @@ MF_EXPORT mf_status mf_read_probe(mf_ctx* ctx, const void* src, size_t bytes, vo
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_write_probe(mf_ctx* ctx, void* dst, size_t bytes, const void* src, void* stream) {
+  if (!dst) return fail(MF_ERR_INVALID, "dst is NULL");
+  if (bytes % 20480 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return fail(MF_ERR_INVALID, "write probe needs 16-byte aligned pointers and a multiple of 20480 bytes");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(mf::write_probe(dst, bytes, src, static_cast<hipStream_t>(stream)), "write probe launch");
+  return MF_OK;
+}
+
 }  // extern "C"

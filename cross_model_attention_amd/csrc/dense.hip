@@ -104,6 +104,35 @@ __global__ __launch_bounds__(256) void k_read(const v4u* __restrict__ src, size_
     sink[0] = acc[0] ^ acc[3];
 }
 
+// ------------------------------------------------------------------------------------------
+// HBM write probe: coalesced non-temporal 16-byte stores (each wave instruction writes 1 KiB of
+// contiguous memory).  Per iteration a workgroup writes 256 * 5 records; with a source it first
+// reads 256 records (non-temporal) and the five records it writes from each are that record plus
+// u = 0..4 in every 32-bit word, so no load can be dropped.  Without a source, record it * 1280 +
+// 256 u + t holds {it, 7, 8, 9} + u.
+// ------------------------------------------------------------------------------------------
+template <bool RD>
+__global__ __launch_bounds__(256) void k_write(v4u* __restrict__ dst, const v4u* __restrict__ src, size_t n_iter) {
+  for (size_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    v4u x = {(uint32_t)it, 7u, 8u, 9u};
+    if (RD) x = __builtin_nontemporal_load(src + it * 256 + threadIdx.x);
+    v4u* d = dst + it * 1280 + threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) __builtin_nontemporal_store(x + (uint32_t)u, d + u * 256);
+  }
+}
+
+hipError_t write_probe(void* dst, size_t bytes, const void* src, hipStream_t s) {
+  const size_t n_iter = bytes / (1280 * 16);
+  if (n_iter == 0) return hipSuccess;
+  const unsigned grid = 256 * 16;
+  if (src)
+    hipLaunchKernelGGL(k_write<true>, dim3(grid), dim3(256), 0, s, (v4u*)dst, (const v4u*)src, n_iter);
+  else
+    hipLaunchKernelGGL(k_write<false>, dim3(grid), dim3(256), 0, s, (v4u*)dst, nullptr, n_iter);
+  return hipGetLastError();
+}
+
 hipError_t read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;

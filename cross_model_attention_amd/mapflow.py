@@ -554,6 +554,17 @@ def copy_probe(dst: torch.Tensor, src: torch.Tensor, ctx=None, stream=None) -> N
     check(_L.mf_copy_probe(ctx.handle, _dev(dst, "dst"), _dev(src, "src"), nbytes, _stream(stream)))
 
 
+def write_probe(dst: torch.Tensor, src: torch.Tensor | None = None, ctx=None, stream=None) -> None:
+    """mf_write_probe: fill dst with coalesced non-temporal stores, reading one 16-byte record of
+    src per five written when src is given (the gather's read : write mix)."""
+    ctx = _ctx(ctx)
+    nbytes = dst.numel() * dst.element_size()
+    if src is not None and src.numel() * src.element_size() < nbytes // 5:
+        raise ValueError("src needs bytes / 5")
+    check(_L.mf_write_probe(ctx.handle, _dev(dst, "dst"), nbytes, None if src is None else _dev(src, "src"),
+                            _stream(stream)))
+
+
 def read_probe(src: torch.Tensor, sink: torch.Tensor, ctx=None, stream=None) -> None:
     """mf_read_probe: stream src through non-temporal loads (HBM read ceiling); sink is a device
     tensor of at least 4 bytes that the probe leaves untouched."""

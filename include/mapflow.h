@@ -556,6 +556,18 @@ mf_status mf_copy_probe(mf_ctx* ctx, void* dst, const void* src, size_t bytes, v
  */
 mf_status mf_read_probe(mf_ctx* ctx, const void* src, size_t bytes, void* sink, void* stream);
 
+/*
+ * HBM write probe: write `bytes` (a multiple of 20480; dst 16-byte aligned) to dst with coalesced
+ * non-temporal 16-byte stores, 1 KiB of contiguous memory per wavefront instruction.  With src
+ * (16-byte aligned, bytes / 5 readable) it first reads bytes / 5 from src with non-temporal
+ * loads, one 16-byte record per five written: the read : write mix of the block gather of
+ * mf_compress, whose writes of kept probabilities outweigh its key reads about five to one.
+ * Record it * 1280 + 256 u + t of dst (u = 0..4, t = 0..255) receives src record it * 256 + t, or
+ * {it, 7, 8, 9} without src, plus u in each 32-bit word.  src may be NULL.  Gives the write-heavy
+ * ceiling that the gather is compared with.
+ */
+mf_status mf_write_probe(mf_ctx* ctx, void* dst, size_t bytes, const void* src, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -385,6 +385,23 @@ def test_misaligned_inputs_are_rejected(mf):
     torch.cuda.synchronize()
 
 
+def test_write_probe_pattern(mf):
+    n_iter = 37
+    rec = torch.arange(n_iter * 256 * 4, dtype=torch.int32, device="cuda").view(n_iter * 256, 4)
+    dst = torch.zeros((n_iter * 1280, 4), dtype=torch.int32, device="cuda")
+    mf.write_probe(dst, rec)
+    torch.cuda.synchronize()
+    u = torch.arange(5, device="cuda", dtype=torch.int32).view(1, 5, 1, 1)
+    want = rec.view(n_iter, 1, 256, 4) + u
+    assert torch.equal(dst.view(n_iter, 5, 256, 4), want)
+    mf.write_probe(dst)
+    torch.cuda.synchronize()
+    it = torch.arange(n_iter, device="cuda", dtype=torch.int32).view(n_iter, 1, 1)
+    base = torch.cat([it, torch.full_like(it, 7), torch.full_like(it, 8), torch.full_like(it, 9)], dim=2)
+    want = base.view(n_iter, 1, 1, 4) + u
+    assert torch.equal(dst.view(n_iter, 5, 256, 4), want.expand(n_iter, 5, 256, 4))
+
+
 def test_read_probe_reads_without_writing(mf):
     src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
     sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")

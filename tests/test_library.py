@@ -100,6 +100,9 @@ def test_invalid_arguments_rejected_before_any_gpu_work(lib):
     assert lib.mf_copy_probe(None, ctypes.c_void_p(16), ctypes.c_void_p(32), 15, None) == _lib.MF_ERR_INVALID
     assert lib.mf_read_probe(None, ctypes.c_void_p(16), 15, ctypes.c_void_p(64), None) == _lib.MF_ERR_INVALID
     assert lib.mf_read_probe(None, ctypes.c_void_p(16), 16, None, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_write_probe(None, None, 20480, None, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_write_probe(None, ctypes.c_void_p(16), 20480 + 16, None, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_write_probe(None, ctypes.c_void_p(16), 20480, ctypes.c_void_p(8), None) == _lib.MF_ERR_INVALID
 
 
 def test_store_layout_helpers_round_trip():
