@@ -183,6 +183,7 @@ struct BsrOwner {
   int32_t* pairs = nullptr;       // device copy of geom.pairs (inside meta)
   uint8_t* active = nullptr;      // device copy of geom.active when the store is ranged (inside meta)
   int32_t* brow_seq = nullptr;    // device copy of geom.brow_seq (inside meta)
+  int32_t* gorder = nullptr;      // the gather's row order (inside meta), see gather_order
   bool cache_owned = false;       // an entry of an mf_cache: freed by the cache only
   Geometry geom;
 };
@@ -245,11 +246,38 @@ mf_status check_dtype(mf_dtype dt) {
   return MF_OK;
 }
 
+// The gather's row order: the work order, with rows of one sequence brought together per XCD.
+// The gather sends work item p to a lane of L = 8 (head groups not dividing 8: XCD p mod 8 for
+// each head group) or of L = 8 / HG (each XCD serves one head group and takes the items with p
+// mod L fixed), and the workgroups in flight on one XCD take consecutive items of its lane.  In a
+// run of 64 L entries of the work order that holds rows of several sequences, the rows are
+// grouped by sequence (work order within one), and lane x takes the x-th 64 of them: the keys
+// the workgroups in flight on one XCD read then belong to one or two sequences instead of one row
+// of each.  Runs of one sequence keep the work order.
+std::vector<int32_t> gather_order(const Geometry& g, int H_s) {
+  std::vector<int32_t> o(g.order.begin(), g.order.begin() + g.n_order);
+  const int HG = (H_s + 7) / 8;
+  const int L = (8 % HG == 0) ? 8 / HG : 8;
+  const int R = 64 * L;
+  std::vector<int32_t> run(R);
+  for (int m = 0; m + R <= g.n_order; m += R) {
+    bool mixed = false;
+    for (int j = 1; j < R; ++j) mixed |= g.brow_seq[o[m + j]] != g.brow_seq[o[m]];
+    if (!mixed) continue;
+    std::copy(o.begin() + m, o.begin() + m + R, run.begin());
+    std::stable_sort(run.begin(), run.end(), [&](int x, int y) { return g.brow_seq[x] < g.brow_seq[y]; });
+    for (int x = 0; x < L; ++x)
+      for (int k = 0; k < 64; ++k) o[m + L * k + x] = run[64 * x + k];
+  }
+  return o;
+}
+
 mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own) {
   const size_t n_info = (size_t)g.n_brow * 4 * 4;
   const size_t o_info = 0;
   const size_t o_order = align_up(o_info + n_info, 256);
-  const size_t o_coff = align_up(o_order + (size_t)g.n_brow * 4, 256);
+  const size_t o_gorder = align_up(o_order + (size_t)g.n_brow * 4, 256);
+  const size_t o_coff = align_up(o_gorder + (size_t)g.n_brow * 4, 256);
   const size_t o_seq = align_up(o_coff + (size_t)g.n_brow * 4, 256);
   const size_t o_ptr = align_up(o_seq + (size_t)g.n_brow * 4, 256);
   const size_t o_rkm = align_up(o_ptr + (size_t)(g.n_brow + 1) * 4, 256);
@@ -268,6 +296,7 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   out->row_kept_mass = reinterpret_cast<float*>(base + o_rkm);
   out->counters = reinterpret_cast<int32_t*>(base + o_cnt);
   own->brow_seq = reinterpret_cast<int32_t*>(base + o_seq);
+  own->gorder = reinterpret_cast<int32_t*>(base + o_gorder);
   own->pairs = reinterpret_cast<int32_t*>(base + o_pairs);
   own->active = g.ranged ? reinterpret_cast<uint8_t*>(base + o_active) : nullptr;
   out->n_order = g.n_order;
@@ -276,6 +305,10 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
     if (e == hipSuccess)
       e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess && g.n_order > 0) {
+      const std::vector<int32_t> go = gather_order(g, H_s);
+      e = hipMemcpy(own->gorder, go.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess)
       e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
@@ -375,7 +408,7 @@ mf_status prepare_compress_args(mf_ctx* ctx, const void* Q, const void* K, mf_dt
   a.n_brow = bsr->n_brow;
   a.nb_max = bsr->nb_max;
   a.info = bsr->brow_info;
-  a.order = bsr->brow_order;
+  a.order = static_cast<const BsrOwner*>(bsr->_owner)->gorder;
   a.coff = bsr->brow_coff;
   a.pairs = static_cast<const BsrOwner*>(bsr->_owner)->pairs;
   a.n_pair = static_cast<const BsrOwner*>(bsr->_owner)->geom.n_pair;
