@@ -272,6 +272,33 @@ std::vector<int32_t> gather_order(const Geometry& g, int H_s) {
   return o;
 }
 
+// The statistics' pair order, grouped the same way: with a multiple of 8 heads every XCD takes
+// the pairs in order (L = 1), else XCD b mod 8 takes every 8th (L = 8); in a run of 256 L pairs of
+// several sequences, the pairs are grouped by sequence and lane x takes the x-th 256.
+std::vector<int32_t> stats_pairs(const Geometry& g, int H_s) {
+  std::vector<int32_t> o(g.pairs.begin(), g.pairs.begin() + 2 * (size_t)g.n_pair);
+  const int L = (H_s % 8 == 0) ? 1 : 8;
+  const int R = 256 * L;
+  auto seq = [&](int i) { return g.brow_seq[o[2 * i]]; };
+  std::vector<std::pair<int32_t, int32_t>> run(R);
+  for (int m = 0; m + R <= g.n_pair; m += R) {
+    bool mixed = false;
+    for (int j = 1; j < R; ++j) mixed |= seq(m + j) != seq(m);
+    if (!mixed) continue;
+    for (int j = 0; j < R; ++j) run[j] = {o[2 * (m + j)], o[2 * (m + j) + 1]};
+    std::stable_sort(run.begin(), run.end(), [&](const auto& x, const auto& y) {
+      return g.brow_seq[x.first] < g.brow_seq[y.first];
+    });
+    for (int x = 0; x < L; ++x)
+      for (int k = 0; k < 256; ++k) {
+        const int i = m + L * k + x;
+        o[2 * i] = run[256 * x + k].first;
+        o[2 * i + 1] = run[256 * x + k].second;
+      }
+  }
+  return o;
+}
+
 mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own) {
   const size_t n_info = (size_t)g.n_brow * 4 * 4;
   const size_t o_info = 0;
@@ -313,8 +340,10 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
       e = hipMemcpy(out->brow_coff, g.coff.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess)
       e = hipMemcpy(own->brow_seq, g.brow_seq.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
-    if (e == hipSuccess && g.n_pair > 0)
-      e = hipMemcpy(own->pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice);
+    if (e == hipSuccess && g.n_pair > 0) {
+      const std::vector<int32_t> sp = stats_pairs(g, H_s);
+      e = hipMemcpy(own->pairs, sp.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess && own->active)
       e = hipMemcpy(own->active, g.active.data(), (size_t)g.n_brow, hipMemcpyHostToDevice);
   }
