@@ -519,9 +519,10 @@ __global__ __launch_bounds__(512) void k_gather(const T* __restrict__ Q, const T
   static_assert(PIECES >= 1 && (TILE / 16) % 512 == 0, "tile must split evenly over 512 threads");
   __shared__ __attribute__((aligned(16))) unsigned char s_out[NBUF][TILE];
 
-  // work item (chunk k of a block row's kept list, head group, block row in LPT order), chunk
-  // index slowest: the workgroups in flight sweep the same range of key blocks, whose tiles then
-  // stay in L2 for all of them.  When the head groups divide the 8 XCDs, each XCD (workgroup
+  // work item (chunk k of a block row's kept list, head group, block row in the gather's order:
+  // longest rows first, rows of one sequence grouped per XCD in a batch), chunk index slowest:
+  // the workgroups in flight sweep the same range of key blocks, whose tiles then stay in L2 for
+  // all of them.  When the head groups divide the 8 XCDs, each XCD (workgroup
   // b runs on XCD b mod 8) serves one head group, so its L2 only holds that group's key tiles.
   const int HG = (H_s + 7) >> 3;
   int p, hg, chunk;
