@@ -292,6 +292,43 @@ def test_retrieve_paged_equals_contiguous_and_varlen_equals_per_sequence(mf):
         assert torch.equal(Os, O[a:b]), f"sequence {s}"
 
 
+@pytest.mark.parametrize("H_s", [32, 36, 40])
+def test_batch_store_equals_per_sequence_stores(mf, H_s):
+    """A batch of many sequences is large enough for the gather and the statistics to regroup
+    their work orders by sequence (at least 64 L rows, 256 L pairs); every row's kept blocks,
+    probabilities and kept mass, and the retrieve output, must equal those of the sequences
+    compressed one at a time (row results do not depend on the order the rows run in)."""
+    wl = synth.WORKLOADS["varlen_14b8b"]
+    lengths = [int(n) for n in np.random.default_rng(20 + H_s).integers(900, 1500, size=40)]
+    x = synth.make_layer_inputs(wl, 20 + H_s, lengths=lengths, H_s=H_s, H_r=8, H_kv=2, d=64)
+    tau = np.float32(0.6).item()          # few kept blocks: the host copies stay small
+    cu = x["cu_seqlens"]
+    say(f"case: batch of {len(lengths)} sequences, H_s={H_s}, T={int(cu[-1])}")
+    Q, K = to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16")
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
+    store = mf.compress(Q, K, tau, wl.B, cu_seqlens=cu)
+    O = mf.retrieve(store, W, V, x["kv_head_map"])
+    torch.cuda.synchronize()
+    meta = store.meta_to_host()
+    assert int(meta["block_ptr"][-1]) == meta["nnzb"]
+    row0 = 0
+    for s_, n in enumerate(lengths):
+        a, b = int(cu[s_]), int(cu[s_ + 1])
+        st = mf.compress(Q[:, a:b].contiguous(), K[:, a:b].contiguous(), tau, wl.B)
+        Os = mf.retrieve(st, W, V[a:b].contiguous(), x["kv_head_map"])
+        torch.cuda.synchronize()
+        hs = st.to_host()
+        nb = (n + wl.B - 1) // wl.B
+        lo, hi = int(meta["block_ptr"][row0]), int(meta["block_ptr"][row0 + nb])
+        assert np.array_equal(meta["block_ptr"][row0:row0 + nb + 1] - lo, hs["block_ptr"]), f"sequence {s_}"
+        blk = store.blocks_to_host(lo, hi - lo)
+        assert np.array_equal(blk["block_idx"], hs["block_idx"]), f"sequence {s_}"
+        assert np.array_equal(blk["probs"], hs["probs"]), f"sequence {s_}"
+        assert np.array_equal(meta["row_kept_mass"][:, a:b], hs["row_kept_mass"]), f"sequence {s_}"
+        assert torch.equal(Os, O[a:b]), f"sequence {s_}"
+        row0 += nb
+
+
 def test_end_to_end_and_determinism(mf):
     wl = synth.WORKLOADS["pair_8b3b_8k"]
     x = synth.make_layer_inputs(wl, 7, lengths=[420], H_s=32, H_r=24, H_kv=8, d=128)
