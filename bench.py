@@ -487,7 +487,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus "
               f"{args.gpus}, WORLD_SIZE={world}).", flush=True)
         sys.exit(2)
 

@@ -15,7 +15,7 @@
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued on it; calls
  *     return before the GPU finishes unless stated otherwise.
  *   - Arguments are validated on the host before anything is launched; a failed check returns
- *     MF_ERR_INVALID (or MF_ERR_UNSUPPORTED for valid shapes this build has no kernel for) and
+ *     MF_ERR_INVALID (or MF_ERR_UNSUPPORTED for valid shapes the library has no kernel for) and
  *     leaves all outputs untouched.  No C++ exception crosses this boundary.
  *   - After a non-OK status, mf_last_error() returns a message for the calling thread.
  *   - A context holds scratch memory: calls on one context that use the same scratch (two
