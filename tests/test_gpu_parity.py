@@ -76,6 +76,26 @@ def _check_compress(x, host, ref, tau, B):
     return excused
 
 
+@pytest.mark.parametrize("k", range(16))
+def test_compress_random_shapes(mf, k):
+    """A seeded sweep of compress shapes (B 32 or 64, d 64 or 128, 1..64 sender heads, bf16 or
+    fp32 inputs, tau in [0.5, 1], 1..3 ragged sequences) through the oracle's compress checks:
+    kept sets (ties excused), probabilities within one bf16 ulp + 1e-6 of the exact map, kept
+    row mass."""
+    r = np.random.default_rng(np.random.SeedSequence([4343, k]))
+    B = int(r.choice([32, 64]))
+    d = int(r.choice([64, 128]))
+    H_s = int(r.integers(1, 65))
+    dtype = str(r.choice(["bf16", "f32"]))
+    tau = _f32(r.uniform(0.5, 1.0))
+    lengths = [int(n) for n in r.integers(1, 3 * B + 40, size=int(r.integers(1, 4)))]
+    wl = synth.WORKLOADS["tiny" if dtype == "f32" else "pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 500 + k, lengths=lengths, H_s=H_s, H_r=2, H_kv=1, d=d)
+    store, host = _compress_case(mf, x, tau, B, dtype)
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    _check_compress(x, host, ref, tau, B)
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_compress_tiny_fp32(mf, seed):
     wl = synth.WORKLOADS["tiny"]
@@ -195,6 +215,37 @@ def test_retrieve_on_oracle_store(mf, case):
         O2 = mf.retrieve(store, W, V, kvm)
         torch.cuda.synchronize()
         assert_out_close(O2.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], kvm), "O_r (reversed kv map)")
+
+
+def _random_shape(k):
+    """Shape k of a seeded sweep over what the retrieve accepts: B 32 or 64, d 64 or 128, 1..64
+    sender heads, 1..48 receiver heads with 1..H_r KV heads, 1..3 ragged sequences."""
+    r = np.random.default_rng(np.random.SeedSequence([4242, k]))
+    B = int(r.choice([32, 64]))
+    d = int(r.choice([64, 128]))
+    H_s = int(r.integers(1, 65))
+    H_r = int(r.integers(1, 49))
+    H_kv = int(r.choice([h for h in range(1, H_r + 1) if H_r % h == 0]))
+    lengths = [int(n) for n in r.integers(1, 3 * B + 40, size=int(r.integers(1, 4)))]
+    return B, d, H_s, H_r, H_kv, lengths
+
+
+@pytest.mark.parametrize("k", range(40))
+def test_retrieve_random_shapes(mf, k):
+    """A seeded sweep of shapes through the head-split planner and every kernel path (whole-block
+    and half-block fast paths, the general path, one or two head chunks, split receivers),
+    each against the oracle's retrieve on the oracle's own store."""
+    B, d, H_s, H_r, H_kv, lengths = _random_shape(k)
+    wl = synth.WORKLOADS["tiny" if B == 32 else "pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 300 + k, lengths=lengths, H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+    tau = _f32(wl.tau)
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    say(f"case: random shape {k}: B={B} d={d} H_s={H_s} H_r={H_r} H_kv={H_kv} lengths={lengths} "
+        f"nnzb={len(ref.block_idx)}")
+    store = _upload_oracle_store(mf, ref, x)
+    O = mf.retrieve(store, to_dev(x["w"]), to_dev(x["v_r"], wl.dtype), x["kv_head_map"])
+    torch.cuda.synchronize()
+    assert_out_close(O.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], x["kv_head_map"]), "O_r")
 
 
 @pytest.mark.parametrize("case", [
