@@ -286,6 +286,42 @@ def test_retrieve_multi(mf, case):
         mf.retrieve_multi(store, recvs[:1] * 5)          # more receivers than one launch takes
 
 
+@pytest.mark.parametrize("k", range(12))
+def test_retrieve_multi_random(mf, k):
+    """Seeded fan-outs of 1..4 receivers with random head counts and KV groupings: the planner's
+    parts, packings and launch widths must leave every receiver bit-identical to its own retrieve
+    and within tolerance of the oracle."""
+    r = np.random.default_rng(np.random.SeedSequence([4444, k]))
+    B = int(r.choice([32, 64]))
+    d = int(r.choice([64, 128]))
+    H_s = int(r.integers(1, 65))
+    recv = []
+    for _ in range(int(r.integers(1, 5))):
+        H_r = int(r.integers(1, 49))
+        recv.append((H_r, int(r.choice([h for h in range(1, H_r + 1) if H_r % h == 0]))))
+    lengths = [int(n) for n in r.integers(1, 3 * B + 40, size=int(r.integers(1, 4)))]
+    wl = synth.WORKLOADS["tiny" if B == 32 else "pair_8b3b_8k"]
+    xs = [synth.make_layer_inputs(wl, 700 + k, layer=j, lengths=lengths, H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+          for j, (H_r, H_kv) in enumerate(recv)]
+    x = xs[0]
+    tau = _f32(wl.tau)
+    ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    say(f"case: random fan-out {k}: B={B} d={d} H_s={H_s} receivers={recv} lengths={lengths}")
+    store = _upload_oracle_store(mf, ref, x)
+    recvs, singles = [], []
+    for xr in xs:
+        W = to_dev(xr["w"])
+        pv = mf.v_prepare(to_dev(xr["v_r"], wl.dtype), B, cu_seqlens=xr["cu_seqlens"])
+        recvs.append((W, pv, xr["kv_head_map"]))
+        singles.append(mf.retrieve_prepared(store, W, pv, xr["kv_head_map"]))
+    outs = mf.retrieve_multi(store, recvs)
+    torch.cuda.synchronize()
+    for j, xr in enumerate(xs):
+        assert torch.equal(outs[j], singles[j]), f"receiver {j}"
+        assert_out_close(outs[j].cpu().numpy(), oracle.retrieve(ref, xr["w"], xr["v_r"], xr["kv_head_map"]),
+                         f"O_r receiver {j}")
+
+
 @pytest.mark.parametrize("case", [
     dict(wl="tiny", seed=8, lengths=[90, 1, 75], H_s=4, d=64, dtype="f32"),
     dict(wl="pair_8b3b_8k", seed=9, lengths=[200, 70], H_s=8, d=128, dtype="bf16"),
