@@ -330,8 +330,9 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   hipError_t e = hipSuccess;
   if (g.n_brow > 0) {
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
-    if (e == hipSuccess)
-      e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice);
+    // the order lists the active rows only (n_order <= n_brow entries; none past them are read)
+    if (e == hipSuccess && g.n_order > 0)
+      e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess && g.n_order > 0) {
       const std::vector<int32_t> go = gather_order(g, H_s);
       e = hipMemcpy(own->gorder, go.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);
@@ -1200,7 +1201,7 @@ MF_EXPORT mf_status mf_dense_attention(mf_ctx* ctx, const void* Q, const void* K
     if ((st = ensure(ctx->al, ctx->dense_tables, o_pairs + (size_t)g.n_pair * 8 + 256, "dense geometry", s)) != MF_OK) return st;
     char* base = static_cast<char*>(ctx->dense_tables.p);
     MF_HIP(hipMemcpy(base, g.info.data(), (size_t)g.n_brow * 16, hipMemcpyHostToDevice), "uploading geometry");
-    MF_HIP(hipMemcpy(base + o_order, g.order.data(), (size_t)g.n_brow * 4, hipMemcpyHostToDevice),
+    MF_HIP(hipMemcpy(base + o_order, g.order.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice),
            "uploading geometry");
     MF_HIP(hipMemcpy(base + o_pairs, g.pairs.data(), (size_t)g.n_pair * 8, hipMemcpyHostToDevice),
            "uploading geometry");

@@ -479,6 +479,27 @@ def test_dense_attention(mf, lengths, Hq, Hkv, d, dtype):
     assert_out_close(O.cpu().numpy(), ref, "dense O")
 
 
+@pytest.mark.parametrize("k", range(10))
+def test_dense_attention_random_shapes(mf, k):
+    """Seeded dense recompute shapes: 1..32 query heads over a divisor number of KV heads, d 64 or
+    128, bf16 or fp32, 1..3 ragged sequences, against the oracle's causal attention."""
+    r = np.random.default_rng(np.random.SeedSequence([4545, k]))
+    Hq = int(r.integers(1, 33))
+    Hkv = int(r.choice([h for h in range(1, Hq + 1) if Hq % h == 0]))
+    d = int(r.choice([64, 128]))
+    dtype = str(r.choice(["bf16", "f32"]))
+    lengths = [int(n) for n in r.integers(1, 300, size=int(r.integers(1, 4)))]
+    wl = synth.WORKLOADS["full_8b3b_32k"]
+    x = synth.make_dense_inputs(wl, 900 + k, layer=0, lengths=lengths, H_q=Hq, H_kv=Hkv, d=d)
+    say(f"case: random dense {k}: lengths={lengths} {Hq}/{Hkv} d={d} {dtype}")
+    kv = [g // (Hq // Hkv) for g in range(Hq)]
+    O = mf.dense_attention(to_dev(x["q"], dtype), to_dev(x["k"], dtype), to_dev(x["v"], dtype), kv,
+                           cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert_out_close(O.cpu().numpy(), oracle.dense_causal_attention(x["q"], x["k"], x["v"], x["cu_seqlens"], kv),
+                     "dense O")
+
+
 def test_copy_probe(mf):
     src = torch.arange(1 << 20, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
@@ -537,6 +558,53 @@ def test_read_probe_reads_without_writing(mf):
 def _rows_of(host, r):
     a, b = int(host["block_ptr"][r]), int(host["block_ptr"][r + 1])
     return host["block_idx"][a:b], host["probs_bits"][a:b]
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_range_store_random(mf, k):
+    """Seeded row ranges (a random first row per sequence, some past the last row): the range
+    store's rows equal the full store's bit for bit, it keeps nothing elsewhere, and its retrieve
+    writes exactly its rows, equal to the full retrieve's."""
+    r = np.random.default_rng(np.random.SeedSequence([4646, k]))
+    B = int(r.choice([32, 64]))
+    H_s = int(r.integers(1, 41))
+    lengths = [int(n) for n in r.integers(1, 6 * B, size=int(r.integers(1, 5)))]
+    nbs = [(n + B - 1) // B for n in lengths]
+    row_begin = [int(r.integers(0, nb + 1)) for nb in nbs]
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 800 + k, lengths=lengths, H_s=H_s, H_r=6, H_kv=2, d=64)
+    tau = _f32(wl.tau)
+    say(f"case: random range store {k}: B={B} H_s={H_s} lengths={lengths} row_begin={row_begin}")
+    Q, K = to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16")
+    full = mf.BlockStore.create(H_s, B, x["cu_seqlens"])
+    part = mf.BlockStore.create(H_s, B, x["cu_seqlens"], row_begin=row_begin)
+    assert part.raw.n_order == sum(nb - rb for nb, rb in zip(nbs, row_begin))
+    mf.compress_into(full, Q, K, tau)
+    mf.compress_into(part, Q, K, tau)
+    full.sync()
+    part.sync()
+    hf, hp = full.to_host(), part.to_host()
+    cu = x["cu_seqlens"]
+    active_tok = np.zeros(int(cu[-1]), dtype=bool)
+    row = 0
+    for s_, n in enumerate(lengths):
+        for I in range(nbs[s_]):
+            if I >= row_begin[s_]:
+                for a_, b_ in zip(_rows_of(hf, row), _rows_of(hp, row)):
+                    assert np.array_equal(a_, b_), f"row {row}"
+                active_tok[int(cu[s_]) + I * B: int(cu[s_]) + min(n, (I + 1) * B)] = True
+            else:
+                assert len(_rows_of(hp, row)[0]) == 0, f"row {row} outside the range kept blocks"
+            row += 1
+    assert np.array_equal(hf["row_kept_mass"][:, active_tok], hp["row_kept_mass"][:, active_tok])
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
+    O_full = mf.retrieve(full, W, V, x["kv_head_map"])
+    O_part = torch.full_like(O_full, float("nan"))
+    mf.retrieve(part, W, V, x["kv_head_map"], out=O_part)
+    torch.cuda.synchronize()
+    act = torch.from_numpy(active_tok).cuda()
+    assert torch.equal(O_part[act], O_full[act])
+    assert torch.isnan(O_part[~act]).all()
 
 
 def test_chunked_prefill_rows_equal_the_full_store(mf):
