@@ -354,6 +354,57 @@ def test_compress_prefill(mf, case):
     assert_out_close(O.cpu().numpy(), ref, "sender O")
 
 
+@pytest.mark.parametrize("k", range(8))
+def test_compress_prefill_random_shapes(mf, k):
+    """Seeded shapes through the fused sender prefill: its store passes the oracle's compress
+    checks and its attention output matches the oracle's causal attention of the sender heads."""
+    r = np.random.default_rng(np.random.SeedSequence([4747, k]))
+    B = int(r.choice([32, 64]))
+    d = int(r.choice([64, 128]))
+    H_s = int(r.integers(1, 25))
+    dtype = str(r.choice(["bf16", "f32"]))
+    lengths = [int(n) for n in r.integers(1, 3 * B + 40, size=int(r.integers(1, 4)))]
+    wl = synth.WORKLOADS["tiny" if dtype == "f32" else "pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 600 + k, lengths=lengths, H_s=H_s, H_r=2, H_kv=1, d=d)
+    v = synth.make_dense_inputs(wl, 600 + k, layer=1, lengths=lengths, H_q=H_s, H_kv=H_s, d=d)["v"]
+    tau = _f32(r.uniform(0.5, 1.0))
+    say(f"case: random prefill {k}: B={B} d={d} H_s={H_s} {dtype} tau={tau} lengths={lengths}")
+    Q, K, V = to_dev(x["q_s"], dtype), to_dev(x["k_s"], dtype), to_dev(v, dtype)
+    fused = mf.BlockStore.create(H_s, B, x["cu_seqlens"])
+    O = mf.compress_prefill_into(fused, Q, K, V, tau)
+    fused.sync()
+    ref_c = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+    _check_compress(x, fused.to_host(), ref_c, tau, B)
+    ref = oracle.dense_causal_attention(x["q_s"].transpose(1, 0, 2), x["k_s"].transpose(1, 0, 2), v,
+                                        x["cu_seqlens"], list(range(H_s)))
+    assert_out_close(O.cpu().numpy(), ref, "sender O")
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_retrieve_paged_random(mf, k):
+    """Seeded page sizes and page-table shuffles: a paged V pool gives the contiguous V's output
+    bit for bit."""
+    r = np.random.default_rng(np.random.SeedSequence([4848, k]))
+    page = int(r.choice([1, 8, 16, 64, 256]))
+    lengths = [int(n) for n in r.integers(1, 400, size=int(r.integers(1, 6)))]
+    H_r = int(r.integers(1, 33))
+    H_kv = int(r.choice([h for h in range(1, H_r + 1) if H_r % h == 0]))
+    wl = synth.WORKLOADS["varlen_14b8b"]
+    x = synth.make_layer_inputs(wl, 950 + k, lengths=lengths, H_s=int(r.integers(1, 41)), H_r=H_r, H_kv=H_kv,
+                                d=int(r.choice([64, 128])))
+    tau = _f32(wl.tau)
+    say(f"case: random paged {k}: page={page} lengths={lengths} H_r={H_r} H_kv={H_kv}")
+    store = mf.compress(to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16"), tau, wl.B, cu_seqlens=x["cu_seqlens"])
+    W = to_dev(x["w"])
+    O = mf.retrieve(store, W, to_dev(x["v_r"], "bf16"), x["kv_head_map"])
+    table, n_pages = synth.make_page_table(lengths, page, seed=950 + k)
+    pool = synth.page_v(x["v_r"], lengths, table, page, n_pages)
+    Op = mf.retrieve(store, W, to_dev(pool, "bf16"), x["kv_head_map"],
+                     page_table=torch.from_numpy(table).cuda(), page_size=page)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op)
+
+
 def test_retrieve_paged_equals_contiguous_and_varlen_equals_per_sequence(mf):
     wl = synth.WORKLOADS["varlen_14b8b"]
     lengths = [300, 17, 129]
