@@ -231,3 +231,44 @@ def test_caller_allocator_provides_every_buffer_and_oom_leaks_nothing(mf):
     ref_store.free()
     ref_b.free()
     hctx.close()
+
+
+@pytest.mark.parametrize("k", range(6))
+def test_prefill_pipeline_random_depths(mf, k):
+    """Seeded depths, ring sizes and recomputed-layer counts (including no recomputed layer and a
+    ring as deep as the mapped layers): every layer of both schedules equals the one-stream serial
+    run bit for bit."""
+    r = np.random.default_rng(np.random.SeedSequence([4949, k]))
+    n_recv = int(r.integers(2, 8))
+    n_send = int(r.integers(2, 10))
+    R = 0 if k == 0 else int(r.integers(0, n_recv))       # case 0: no recomputed layer
+    n_map = n_recv - R
+    n_slots = int(r.integers(1, n_map + 1))
+    L = int(r.integers(70, 400))
+    H_s, H_r, H_kv, d = 8, 6, 2, 64
+    pi, send, recv, kv, tau, B = _pipeline_case(L, n_send, n_recv, R, H_s, H_r, H_kv, d, seed=60 + k)
+    say(f"case: random pipeline {k}: L={L} pi={pi} slots={n_slots}")
+    dsend, drecv = _to_device(send, recv)
+    cu = [0, L]
+    mf.map_layers(pi, n_send, R)
+    slots = [mf.BlockStore.create(H_s, B, cu) for _ in range(n_slots)]
+    s_main, s_pre = torch.cuda.Stream(), torch.cuda.Stream()
+    serial = {}
+    for l in range(n_recv):
+        rr = drecv[l]
+        if pi[l] < 0:
+            serial[l] = mf.dense_attention(rr["q"], rr["k"], rr["v"], kv, cu_seqlens=cu)
+        else:
+            st = mf.BlockStore.create(H_s, B, cu)
+            mf.compress_into(st, *dsend[pi[l]], tau)
+            serial[l] = mf.retrieve_prepared(st, rr["w"], mf.v_prepare(rr["v"], B, cu), kv)
+    torch.cuda.synchronize()
+    for isolate in (True, False):
+        O = _outs(recv, L, H_r, d)
+        for rr, o in zip(drecv, O):
+            rr["o"] = o
+        torch.cuda.current_stream().synchronize()
+        mf.prefill_layers(slots, dsend, drecv, kv, tau, isolate=isolate, stream_main=s_main, stream_prefetch=s_pre)
+        s_main.synchronize()
+        for l in range(n_recv):
+            assert torch.equal(O[l], serial[l]), f"isolate={isolate}: layer {l}"
