@@ -885,6 +885,35 @@ def test_compress_variants(mf, case):
     assert_out_close(O.cpu().numpy(), oracle.retrieve(ref, x["w"], x["v_r"], x["kv_head_map"]), "O_r (variant)")
 
 
+@pytest.mark.parametrize("k", range(8))
+def test_retrieve_layers_random(mf, k):
+    """Seeded cross-layer mixes: 1..4 sender layers of 1..64 heads each, random receiver shapes,
+    against the oracle's cross-layer retrieve on the same stores."""
+    r = np.random.default_rng(np.random.SeedSequence([5050, k]))
+    B = int(r.choice([32, 64]))
+    d = int(r.choice([64, 128]))
+    H_r = int(r.integers(1, 49))
+    H_kv = int(r.choice([h for h in range(1, H_r + 1) if H_r % h == 0]))
+    heads = [int(h) for h in r.integers(1, 65, size=int(r.integers(1, 5)))]
+    lengths = [int(n) for n in r.integers(1, 3 * B + 40, size=int(r.integers(1, 4)))]
+    wl = synth.WORKLOADS["tiny" if B == 32 else "pair_8b3b_8k"]
+    tau = _f32(wl.tau)
+    say(f"case: random cross-layer {k}: B={B} d={d} H_r={H_r} H_kv={H_kv} heads={heads} lengths={lengths}")
+    refs, stores, Ws, Wn = [], [], [], []
+    for l, H_s in enumerate(heads):
+        x = synth.make_layer_inputs(wl, 1000 + k, layer=l, lengths=lengths, H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+        ref = oracle.compress(x["q_s"], x["k_s"], x["cu_seqlens"], tau, B)
+        refs.append(ref)
+        stores.append(_upload_oracle_store(mf, ref, x))
+        Wn.append(x["w"])
+        Ws.append(to_dev(x["w"]))
+    v, kv = x["v_r"], x["kv_head_map"]
+    pv = mf.v_prepare(to_dev(v, wl.dtype), B, cu_seqlens=x["cu_seqlens"])
+    O = mf.retrieve_layers(stores, Ws, pv, kv)
+    torch.cuda.synchronize()
+    assert_out_close(O.cpu().numpy(), oracle.retrieve_layers(refs, Wn, v, kv), "O_r (cross-layer)")
+
+
 @pytest.mark.parametrize("case", [
     dict(wl="pair_8b3b_8k", seed=17, lengths=[230, 40], heads=[8, 16], H_r=12, H_kv=4, d=128),
     dict(wl="tiny", seed=18, lengths=[120, 1, 60], heads=[4, 4, 2], H_r=5, H_kv=5, d=64),

@@ -73,6 +73,33 @@ def test_retrieve_noalloc_equals_retrieve_and_allocates_nothing(mf):
     ctx.close()
 
 
+@pytest.mark.parametrize("k", range(6))
+def test_retrieve_noalloc_random_shapes(mf, k):
+    """Seeded shapes within the array's limit (contiguous or paged V): the allocation-free
+    retrieve equals mf_retrieve bit for bit and calls no allocator."""
+    r = np.random.default_rng(np.random.SeedSequence([5151, k]))
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    H_r = int(r.integers(1, 49))
+    c = dict(seed=40 + k, lengths=[int(n) for n in r.integers(1, 700, size=int(r.integers(1, 4)))],
+             H_s=int(r.integers(1, 65)), H_r=H_r,
+             H_kv=int(r.choice([h for h in range(1, H_r + 1) if H_r % h == 0])),
+             d=int(r.choice([64, 128])), paged=bool(r.integers(0, 2)))
+    al = _Counting()
+    ctx = mf.Context(0, allocator=(al.alloc, al.free))
+    say(f"case: random retrieve_noalloc {k}: {c}")
+    x, store, W, V, kw = _case(mf, ctx, wl, **c)
+    ref = mf.retrieve(store, W, V, x["kv_head_map"], **kw)
+    out = torch.full_like(ref, float("nan"))
+    torch.cuda.synchronize()
+    before = al.calls
+    mf.retrieve_noalloc(store, W, V, x["kv_head_map"], out=out, **kw)
+    torch.cuda.synchronize()
+    assert al.calls == before, "the no-allocation retrieve called the allocator"
+    assert torch.equal(out, ref), "differs from mf_retrieve"
+    del store
+    ctx.close()
+
+
 def test_retrieve_noalloc_refuses_sizes_past_its_array(mf):
     H_s, B, T, H_kv, d = 8, 64, 32768 + 64, 8, 128          # one block row too many
     store = mf.BlockStore.create(H_s, B, [0, T], capacity=0)
