@@ -756,6 +756,67 @@ def test_chunked_prefill_rows_equal_the_full_store(mf):
     assert torch.equal(O_pre[act], O_pre_full[act]) and torch.isnan(O_pre[~act]).all()
 
 
+@pytest.mark.parametrize("k", range(4))
+def test_prefix_cache_random_requests(mf, k):
+    """Seeded conversation trees through a cache small enough to evict: each request continues an
+    earlier one (all of it, or up to a random point) with new tokens.  Its output, assembled from
+    the looked-up prefix and a row-range store of the rest, equals compressing it whole, bit for
+    bit; requests that extend a cached one find it; the cache's bytes stay within its budget."""
+    r = np.random.default_rng(np.random.SeedSequence([5252, k]))
+    B, H_s, H_r, H_kv, d = 64, 8, 6, 2, 64
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    tau = _f32(wl.tau)
+    w = synth.make_layer_inputs(wl, 1100 + k, lengths=[B], H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+    W, kv = to_dev(w["w"]), w["kv_head_map"]
+    budget = 3 << 20
+    cache = mf.PrefixCache(budget)
+    reqs = []                                        # (tokens, q_s, k_s, v_r) of earlier requests
+    hits = 0
+    for q in range(12):
+        if reqs and r.random() < 0.8:
+            ptok, pq, pk, pv = reqs[int(r.integers(0, len(reqs)))]
+            p = len(ptok) if r.random() < 0.5 else int(r.integers(0, len(ptok) + 1))
+        else:
+            ptok, pq, pk, pv, p = np.zeros(0, np.int32), None, None, None, 0
+        n = min(p + int(r.integers(1, 4 * B)), 12 * B)
+        fresh = synth.make_layer_inputs(wl, 2000 + 100 * k + q, lengths=[n], H_s=H_s, H_r=H_r, H_kv=H_kv, d=d)
+        tail = r.integers(0, 50000, size=n - p).astype(np.int32)
+        if p < len(ptok) and n > p and tail[0] == ptok[p]:
+            tail[0] ^= 1
+        tok = np.concatenate([ptok[:p], tail])
+        qs = fresh["q_s"] if p == 0 else np.concatenate([pq[:, :p], fresh["q_s"][:, p:]], axis=1)
+        ks = fresh["k_s"] if p == 0 else np.concatenate([pk[:, :p], fresh["k_s"][:, p:]], axis=1)
+        vs = fresh["v_r"] if p == 0 else np.concatenate([pv[:p], fresh["v_r"][p:]], axis=0)
+        reqs.append((tok, qs, ks, vs))
+        Q, K, V = to_dev(qs, "bf16"), to_dev(ks, "bf16"), to_dev(vs, "bf16")
+        rows, view = cache.lookup(0, tok, B)
+        say(f"case: random cache {k} request {q}: continues {p} tokens, length {n}, cached rows {rows}")
+        assert rows <= n // B
+        hits += rows > 0
+        part = mf.BlockStore.create(H_s, B, [0, n], row_begin=[rows])
+        mf.compress_into(part, Q, K, tau)
+        part.sync()
+        O = torch.full((n, H_r, d), float("nan"), device="cuda")
+        if rows:
+            mf.retrieve(view, W, V[: rows * B].contiguous(), kv, out=O[: rows * B])
+        mf.retrieve(part, W, V, kv, out=O)
+        whole = mf.BlockStore.create(H_s, B, [0, n])
+        mf.compress_into(whole, Q, K, tau)
+        O_whole = mf.retrieve(whole, W, V, kv)
+        torch.cuda.synchronize()
+        assert torch.equal(O, O_whole), f"request {q}"
+        if n // B > 0:
+            try:
+                cache.insert(0, tok, ([view] if rows else []) + [part], n // B)
+            except mf.MapflowError as e:
+                assert "CAPACITY" in str(e), str(e)
+        assert cache.info()[1] <= budget
+        del view
+    say(f"  requests served from the cache: {hits}")
+    assert hits > 0
+    cache.close()
+
+
 def test_prefix_cache_reuses_a_previous_request(mf):
     """Request 2 extends request 1: its cached prefix plus a row-range store of the new rows give
     the same retrieve output as compressing request 2 whole; inserting the combined prefix gives
