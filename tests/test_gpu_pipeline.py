@@ -173,6 +173,76 @@ class _Budget:
         self.given += 1
 
 
+class _FailNth(_Budget):
+    """Refuses exactly the n-th allocation request (1-based) and grants every other."""
+
+    def __init__(self, n):
+        super().__init__(1 << 50)
+        self.n, self.calls = n, 0
+
+    def alloc(self, nbytes, stream):
+        self.calls += 1
+        if self.calls == self.n:
+            self.refused += 1
+            return None
+        return super().alloc(nbytes, stream)
+
+
+def _workflow(mf, ctx, x, tau, B):
+    """Create, compress, prepare V, retrieve, fan out to two receivers: every allocating call."""
+    Q, K = to_dev(x["q_s"], "bf16"), to_dev(x["k_s"], "bf16")
+    W, V = to_dev(x["w"]), to_dev(x["v_r"], "bf16")
+    store = mf.BlockStore.create(x["H_s"], B, x["cu_seqlens"], ctx=ctx)
+    objs = [store]
+    mf.compress_into(store, Q, K, tau)
+    pv = mf.v_prepare(V, B, x["cu_seqlens"], ctx=ctx)
+    objs.append(pv)
+    O = mf.retrieve_prepared(store, W, pv, x["kv_head_map"])
+    outs = mf.retrieve_multi(store, [(W, pv, x["kv_head_map"]), (W, pv, x["kv_head_map"])])
+    torch.cuda.synchronize()
+    return objs, O, outs
+
+
+@pytest.mark.parametrize("n", range(1, 16))
+def test_each_allocation_failing_leaks_nothing(mf, n):
+    """Refusing the n-th device allocation of a whole workflow (store, statistics and gather
+    scratch, prepared V, retrieve tables) turns that call into MF_ERR_OOM, leaves every buffer of
+    the context accounted for, and the same workflow succeeds afterwards with the same results as
+    an unrestricted context."""
+    wl = synth.WORKLOADS["pair_8b3b_8k"]
+    x = synth.make_layer_inputs(wl, 70, lengths=[300, 70], H_s=8, H_r=6, H_kv=2, d=64)
+    tau = float(np.float32(wl.tau))
+    say(f"case: the allocation number {n} of the workflow is refused")
+    ref_ctx = mf.Context(0, allocator="hip")
+    ref_objs, ref_O, ref_outs = _workflow(mf, ref_ctx, x, tau, wl.B)
+    al = _FailNth(n)
+    ctx = mf.Context(0, allocator=(al.alloc, al.free))
+    objs = []
+    try:
+        objs, O, outs = _workflow(mf, ctx, x, tau, wl.B)
+        failed = False
+    except mf.MapflowError as e:
+        assert "OOM" in str(e), str(e)
+        failed = True
+    assert failed == (al.refused == 1)
+    if n == 15:                    # the largest n is past the workflow's last request: all covered
+        assert not failed and al.calls < n, al.calls
+    if not failed:
+        assert torch.equal(O, ref_O) and all(torch.equal(a, b) for a, b in zip(outs, ref_outs))
+    # with nothing refused any more the workflow runs on the same context and matches
+    al.n = -1
+    objs2, O2, outs2 = _workflow(mf, ctx, x, tau, wl.B)
+    assert torch.equal(O2, ref_O) and all(torch.equal(a, b) for a, b in zip(outs2, ref_outs))
+    for o in objs + objs2:
+        o.free()
+    ctx.close()
+    assert al.live == {}, f"{len(al.live)} buffers still held"
+    assert al.taken == al.given
+    for o in ref_objs:
+        o.free()
+    ref_ctx.close()
+
+
 def test_caller_allocator_provides_every_buffer_and_oom_leaks_nothing(mf):
     wl = synth.WORKLOADS["pair_8b3b_8k"]
     x = synth.make_layer_inputs(wl, 23, lengths=[600, 130], H_s=16, H_r=12, H_kv=4, d=128)
