@@ -14,7 +14,8 @@ The whole schedule is one library call per step (mf_prefill_layers); its stage t
 the library's own HIP events, recorded on the stream each kernel runs on.
 The JSON line reports whole-step throughput (tokens through the full receiver depth per second),
 the fused-retrieve kernel's own timing, bytes and roofline fraction from HIP events recorded on its
-stream, and the fp64 oracle timed on a bounded sample of the same workload on the host cores.
+stream, and the fp64 oracle timed on a bounded sample of block rows of the benchmark's own inputs
+on the host cores, with the GPU's results for those rows compared against it (oracle_check).
 """
 from __future__ import annotations
 
