@@ -756,6 +756,23 @@ def main():
                          "total_GB_per_s": (nb + rd) / (ms * 1e-3) / 1e9}
         out["hbm_write_probe"] = res
         del src, dst
+        # the device's write ceiling: plain stores in 256 KiB runs (the gather's stores are
+        # non-temporal, which keeps its key tiles in L2 but writes more slowly)
+        nb = args.write_probe_bytes // 262144 * 262144
+        if nb > 0:
+            dst = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+            mf.fill_probe(dst, 7)
+            torch.cuda.synchronize()
+            e0, e1 = ev(), ev()
+            e0.record()
+            reps = 10
+            for _ in range(reps):
+                mf.fill_probe(dst, 7)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out["hbm_fill_probe"] = {"bytes_written": nb, "write_GB_per_s": nb / (ms * 1e-3) / 1e9}
+            del dst
 
     if args.extras and n_map >= 1:
         out["prefill"] = prefill(mf, torch, wl, args, send[pi[mapped[-1]]], slots[(n_map - 1) % k], tau, ctx, dev)

@@ -14,6 +14,7 @@ from .mapflow import (  # noqa: F401
     compress_into,
     compress_prefill_into,
     copy_probe,
+    fill_probe,
     read_probe,
     write_probe,
     dense_attention,

@@ -98,6 +98,7 @@ _SIGNATURES = {
     "mf_copy_probe": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mf_read_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
     "mf_write_probe": (c_int, [c_void_p, c_void_p, c_size_t, c_void_p, c_void_p]),
+    "mf_fill_probe": (c_int, [c_void_p, c_void_p, c_size_t, ctypes.c_uint32, c_void_p]),
     "mf_prefix_hashes": (c_int, [_P_I32, c_int64, c_int32, POINTER(c_uint64)]),
     "mf_cache_create": (c_int, [c_void_p, c_int64, POINTER(c_void_p)]),
     "mf_cache_destroy": (c_int, [c_void_p]),

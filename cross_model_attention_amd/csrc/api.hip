@@ -1753,4 +1753,14 @@ MF_EXPORT mf_status mf_write_probe(mf_ctx* ctx, void* dst, size_t bytes, const v
   return MF_OK;
 }
 
+MF_EXPORT mf_status mf_fill_probe(mf_ctx* ctx, void* dst, size_t bytes, uint32_t value, void* stream) {
+  if (!dst) return fail(MF_ERR_INVALID, "dst is NULL");
+  if (bytes % 262144 != 0 || (reinterpret_cast<uintptr_t>(dst) & 15))
+    return fail(MF_ERR_INVALID, "fill probe needs a 16-byte aligned destination and a multiple of 262144 bytes");
+  mf_status st = set_device(ctx);
+  if (st != MF_OK) return st;
+  MF_HIP(mf::fill_probe(dst, bytes, value, static_cast<hipStream_t>(stream)), "fill probe launch");
+  return MF_OK;
+}
+
 }  // extern "C"

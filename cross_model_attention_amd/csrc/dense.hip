@@ -133,6 +133,28 @@ hipError_t write_probe(void* dst, size_t bytes, const void* src, hipStream_t s) 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------
+// HBM fill probe: plain (temporal) 16-byte stores of one 32-bit value, each workgroup iteration
+// writing 256 KiB of contiguous memory (64 stores per thread; every wave instruction covers 1 KiB).
+// Long contiguous runs and ordinary stores give the chip's write ceiling, which non-temporal
+// stores in short runs do not reach.
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_fill(v4u* __restrict__ dst, size_t n_iter, uint32_t v) {
+  const v4u x = {v, v, v, v};
+  for (size_t it = blockIdx.x; it < n_iter; it += gridDim.x) {
+    v4u* d = dst + it * 16384 + threadIdx.x;
+#pragma unroll 16
+    for (int u = 0; u < 64; ++u) d[u * 256] = x;
+  }
+}
+
+hipError_t fill_probe(void* dst, size_t bytes, uint32_t v, hipStream_t s) {
+  const size_t n_iter = bytes / 262144;
+  if (n_iter == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill, dim3(2048), dim3(256), 0, s, (v4u*)dst, n_iter, v);
+  return hipGetLastError();
+}
+
 hipError_t read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s) {
   const size_t n = bytes / 16;
   if (n == 0) return hipSuccess;

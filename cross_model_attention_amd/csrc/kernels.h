@@ -143,5 +143,6 @@ bool dense_supported(int dtype, int d);
 hipError_t copy_probe(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t read_probe(const void* src, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t write_probe(void* dst, size_t bytes, const void* src, hipStream_t s);
+hipError_t fill_probe(void* dst, size_t bytes, uint32_t v, hipStream_t s);
 
 }  // namespace mf

@@ -565,6 +565,14 @@ def write_probe(dst: torch.Tensor, src: torch.Tensor | None = None, ctx=None, st
                             _stream(stream)))
 
 
+def fill_probe(dst: torch.Tensor, value: int, ctx=None, stream=None) -> None:
+    """mf_fill_probe: write the 32-bit value to every word of dst with plain stores in 256 KiB
+    runs (the device's write ceiling)."""
+    ctx = _ctx(ctx)
+    nbytes = dst.numel() * dst.element_size()
+    check(_L.mf_fill_probe(ctx.handle, _dev(dst, "dst"), nbytes, value & 0xFFFFFFFF, _stream(stream)))
+
+
 def read_probe(src: torch.Tensor, sink: torch.Tensor, ctx=None, stream=None) -> None:
     """mf_read_probe: stream src through non-temporal loads (HBM read ceiling); sink is a device
     tensor of at least 4 bytes that the probe leaves untouched."""

@@ -568,6 +568,15 @@ mf_status mf_read_probe(mf_ctx* ctx, const void* src, size_t bytes, void* sink, 
  */
 mf_status mf_write_probe(mf_ctx* ctx, void* dst, size_t bytes, const void* src, void* stream);
 
+/*
+ * HBM fill probe: write `value` to every 32-bit word of dst (`bytes` a multiple of 262144, dst
+ * 16-byte aligned) with plain (temporal) 16-byte stores, each workgroup writing 256 KiB of
+ * contiguous memory at a time.  Reads nothing.  Gives the device's write ceiling: the
+ * non-temporal stores of mf_write_probe (the gather's store kind, which keeps its key tiles in
+ * L2) reach less.
+ */
+mf_status mf_fill_probe(mf_ctx* ctx, void* dst, size_t bytes, uint32_t value, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

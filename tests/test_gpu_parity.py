@@ -581,6 +581,15 @@ def test_misaligned_inputs_are_rejected(mf):
     torch.cuda.synchronize()
 
 
+def test_fill_probe_writes_every_word(mf):
+    n = 3 * 262144 // 4
+    dst = torch.zeros(n + 64, dtype=torch.int32, device="cuda")
+    mf.fill_probe(dst[:n], 0x9E3779B9)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], torch.full((n,), 0x9E3779B9 - 2**32, dtype=torch.int32, device="cuda"))
+    assert torch.count_nonzero(dst[n:]).item() == 0            # nothing past the end
+
+
 def test_write_probe_pattern(mf):
     n_iter = 37
     rec = torch.arange(n_iter * 256 * 4, dtype=torch.int32, device="cuda").view(n_iter * 256, 4)

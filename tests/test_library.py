@@ -103,6 +103,9 @@ def test_invalid_arguments_rejected_before_any_gpu_work(lib):
     assert lib.mf_write_probe(None, None, 20480, None, None) == _lib.MF_ERR_INVALID
     assert lib.mf_write_probe(None, ctypes.c_void_p(16), 20480 + 16, None, None) == _lib.MF_ERR_INVALID
     assert lib.mf_write_probe(None, ctypes.c_void_p(16), 20480, ctypes.c_void_p(8), None) == _lib.MF_ERR_INVALID
+    assert lib.mf_fill_probe(None, None, 262144, 0, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_fill_probe(None, ctypes.c_void_p(16), 262144 + 20480, 0, None) == _lib.MF_ERR_INVALID
+    assert lib.mf_fill_probe(None, ctypes.c_void_p(8), 262144, 0, None) == _lib.MF_ERR_INVALID
 
 
 def test_store_layout_helpers_round_trip():
