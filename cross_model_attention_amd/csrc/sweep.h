@@ -52,6 +52,11 @@ __device__ __forceinline__ v4f dot_tile(const Frag<float, D>& A, const Frag<floa
 
 constexpr float kNegInf = -__builtin_inff();
 
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
+
 template <int D>
 __device__ __forceinline__ void load_lds_frag(Frag<uint16_t, D>& f, const unsigned char* row, int a) {
 #pragma unroll
@@ -278,20 +283,34 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   // the wait for the DMA at its end need not cover them.
   float2 zpend[QT];
   int Jpend = -1;                                         // block whose statistics are pending
-  auto block = [&](int J) {
-    if (J + 1 <= Jend) {
-      fetch_k(kst, J + 1);
-      dma_k(J + 1, (J + 1) & 1);                            // that buffer was last read in block J - 1
-    }
+  // block(J, Tag<true>): this wave computes block J; Tag<false>: it only issues the loads and
+  // stores.  The two kinds run in separate loops (every block a wave computes comes first), so no
+  // path into the LDS reads of a computed block passes an LDS DMA still in flight.
+  auto block = [&](int J, auto kind) {
+    constexpr bool COMPUTE = decltype(kind)::value;
+    if (J + 1 <= Jend) fetch_k(kst, J + 1);
     const bool stored = STATS && Jpend >= 0;
-    if (stored) {
-      if (a == 0) {
+    // The next key tile's DMA (into the buffer last read in block J - 1), then the previous
+    // block's statistics.  Without the attention half the DMA is issued after this block's last
+    // LDS read: the compiler cannot tell the two LDS buffers apart and makes every LDS read wait
+    // for all LDS DMA in flight, so a DMA issued before the score products would be waited for at
+    // once, with nothing to hide its latency; issued after them, it lands during the exponentials
+    // (block statistics 5.40 -> 4.97 ms on an 8B-class layer at L = 32768).  With the attention
+    // half it stays at the top of the block: the V loads after the exponentials are waited for on
+    // the same in-order counter, so a later DMA delays them instead (dense recompute 9.56 ->
+    // 10.97 ms).
+    // Every lane group stores (the four hold the same values): the stores stay unconditional, so
+    // the end-of-block wait that lets them stay in flight is known to cover the DMA on every path.
+    auto issue = [&] {
+      if (J + 1 <= Jend) dma_k(J + 1, (J + 1) & 1);
+      if (stored) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) zrow[(size_t)Jpend * B + q0 + 16 * qt + c] = zpend[qt];
+        Jpend = -1;
       }
-      Jpend = -1;
-    }
-    if (mine && J <= bi.I) {
+    };
+    if constexpr (COMPUTE) {
+      if constexpr (ATTN) issue();
       const unsigned char* kt = s_k[J & 1];
       v4f s[QT][MT];
 #pragma unroll
@@ -302,6 +321,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[qt][mt] = dot_tile<D>(kf, qf[qt], zero4());
       }
+      if constexpr (!ATTN) issue();
       // only the diagonal block and blocks of a partial row need the causal / length mask
       const bool masked = J == bi.I || partial;
       v8h pop[ATTN ? QT : 1][NCH];
@@ -376,6 +396,8 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
             for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma_f16(vop, pop[qt][ch], acc[qt][dt]);
           }
       }
+    } else {
+      issue();
     }
     if (J + 1 <= Jend) stage_k(kst, (J + 1) & 1);
     if (DMA) {
@@ -389,7 +411,10 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   dma_k(0, 0);
   if (DMA) dma_wait();
   __syncthreads();
-  for (int J = 0; J <= Jend; ++J) block(J);
+  const int Jc = mine ? bi.I : -1;                         // last block this wave computes
+  int J = 0;
+  for (; J <= Jc; ++J) block(J, BoolTag<true>{});
+  for (; J <= Jend; ++J) block(J, BoolTag<false>{});
   if (STATS && Jpend >= 0 && a == 0) {                     // the last block's statistics
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) zrow[(size_t)Jpend * B + q0 + 16 * qt + c] = zpend[qt];
