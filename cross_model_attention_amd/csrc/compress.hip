@@ -397,6 +397,27 @@ __device__ __forceinline__ void stream_tile(const unsigned char* tile, unsigned 
                                             int w, int lane) {
   constexpr int PIECES = B * B / 512;              // pieces per thread per tile
   const int per = PIECES / NQ;
+  if constexpr (B == 64) {
+    // Piece u0 of wave w is row r = 16 (w / 2) + 2 (u0 mod 4) + 8 (u0 / 4) + (w mod 2), record
+    // k = lane.  The 8 waves x 8 pieces cover the 64 rows once, each wave instruction still
+    // stores one whole row (1 KiB), and the row's head-slot rotation rec_rot(r mod 16) = u0 mod 4
+    // is known at compile time: no branch per piece, and the reads of a part can be issued
+    // together before their wait.
+#pragma unroll
+    for (int u0 = 0; u0 < PIECES; ++u0) {
+      if (u0 / per != q) continue;
+      const int rr = 2 * (u0 & 3) + 8 * (u0 >> 2) + (w & 1);    // r mod 16
+      const int r = 16 * (w >> 1) + rr;
+      const v4u x = *reinterpret_cast<const v4u*>(tile + (r * B + (lane ^ rec_xor(rr))) * 16);
+      v4u y;
+      if ((u0 & 3) == 0) y = x;
+      else if ((u0 & 3) == 1) y = v4u{x[1], x[2], x[3], x[0]};
+      else if ((u0 & 3) == 2) y = v4u{x[2], x[3], x[0], x[1]};
+      else y = v4u{x[3], x[0], x[1], x[2]};
+      __builtin_nontemporal_store(y, reinterpret_cast<v4u*>(dst + ((size_t)r * B + lane) * 16));
+    }
+    return;
+  }
 #pragma unroll
   for (int u0 = 0; u0 < PIECES; ++u0) {
     if (u0 / per != q) continue;
