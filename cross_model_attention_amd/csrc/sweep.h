@@ -208,29 +208,29 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   // masked wherever they are read)
   // Each lane's source offset within a block of keys is the same for every block; only the
   // block base (uniform) changes, except in a block that runs past the sequence's end.
-  int dma_row[DMA ? NDMA : 1];
-  uint32_t dma_off[DMA ? NDMA : 1];
+  // The sequence's last key block is the only one that can run past its end; its clamped offsets
+  // (rows past the end read the last key) are computed here once, so a block's DMA only selects
+  // between two offsets instead of clamping every load of every block.
+  const int Jlast = (b0.n - 1) / B;
+  uint32_t dma_off[DMA ? NDMA : 1], dma_off_last[DMA ? NDMA : 1];
   if constexpr (DMA) {
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) {
       const int byte = (w * NDMA + u) * 1024 + lane * 16;
       const int r = byte / (D * 2), p = (byte % (D * 2)) / 16;
-      dma_row[u] = r;
       dma_off[u] = (uint32_t)(r * hd.k_stride * 2 + (p ^ kswz<D>(r)) * 16);
+      const int over = Jlast * B + r - (b0.n - 1);
+      dma_off_last[u] = over > 0 ? dma_off[u] - (uint32_t)over * (uint32_t)(hd.k_stride * 2) : dma_off[u];
     }
   }
   auto dma_k = [&](int J, int buf) {
     if constexpr (DMA) {
       const MF_GLOBAL unsigned char* kb = (const MF_GLOBAL unsigned char*)Kh + (size_t)J * B * hd.k_stride * 2;
-      const bool full = J * B + B <= b0.n;
+      const bool last = J == Jlast;
 #pragma unroll
       for (int u = 0; u < NDMA; ++u) {
         const int kib = w * NDMA + u;
-        uint32_t off = dma_off[u];
-        if (!full) {
-          const int r = dma_row[u], over = J * B + r - (b0.n - 1);
-          if (over > 0) off -= (uint32_t)over * (uint32_t)(hd.k_stride * 2);   // clamp onto the sequence's last key
-        }
+        const uint32_t off = last ? dma_off_last[u] : dma_off[u];
         __builtin_amdgcn_global_load_lds(kb + off, (__attribute__((address_space(3))) void*)&s_k[buf][kib * 1024], 16, 0, 0);
       }
     }
