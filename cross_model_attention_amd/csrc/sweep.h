@@ -207,10 +207,9 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   // fetches chunk p ^ kswz(r) of key J B + r (clamped into the sequence: keys past its end are
   // masked wherever they are read)
   // Each lane's source offset within a block of keys is the same for every block; only the
-  // block base (uniform) changes, except in a block that runs past the sequence's end.
-  // The sequence's last key block is the only one that can run past its end; its clamped offsets
-  // (rows past the end read the last key) are computed here once, so a block's DMA only selects
-  // between two offsets instead of clamping every load of every block.
+  // block base (uniform) changes.  The sequence's last key block is the only one that can run
+  // past its end; its clamped offsets (rows past the end read the last key) are computed here
+  // once, so a block's DMA only selects between two offsets instead of clamping every load.
   const int Jlast = (b0.n - 1) / B;
   uint32_t dma_off[DMA ? NDMA : 1], dma_off_last[DMA ? NDMA : 1];
   if constexpr (DMA) {
@@ -294,11 +293,10 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
     // block's statistics.  Without the attention half the DMA is issued after this block's last
     // LDS read: the compiler cannot tell the two LDS buffers apart and makes every LDS read wait
     // for all LDS DMA in flight, so a DMA issued before the score products would be waited for at
-    // once, with nothing to hide its latency; issued after them, it lands during the exponentials
-    // (block statistics 5.40 -> 4.97 ms on an 8B-class layer at L = 32768).  With the attention
-    // half it stays at the top of the block: the V loads after the exponentials are waited for on
-    // the same in-order counter, so a later DMA delays them instead (dense recompute 9.56 ->
-    // 10.97 ms).
+    // once, with nothing to hide its latency; issued after them, it lands during the
+    // exponentials.  With the attention half it stays at the top of the block: the V loads after
+    // the exponentials are waited for on the same in-order counter, so a later DMA would delay
+    // them instead (measured slower).
     // Every lane group stores (the four hold the same values): the stores stay unconditional, so
     // the end-of-block wait that lets them stay in flight is known to cover the DMA on every path.
     auto issue = [&] {
