@@ -342,6 +342,7 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
     int e = 0;
     if (head_of(threadIdx.x) >= 0) {
       float sa = 0.f;
+#pragma unroll 8
       for (int h = 0; h < H_s; ++h) sa += fabsf(s_x[threadIdx.x][h]);
       if (sa > 0.f && sa < __builtin_inff()) {
         int ex;
@@ -362,7 +363,9 @@ __global__ __launch_bounds__(RT_WAVES * 64) void k_retrieve(const RetrieveArgs a
   for (int t = threadIdx.x; t < HR_MAX * RT_ROWS; t += blockDim.x) {
     const int j = t / RT_ROWS, i = t % RT_ROWS;
     float den = 0.f;
+    // unrolled so that the LDS reads of several terms are in flight at once; the sum keeps its order
     if (head_of(j) >= 0 && i < rows)
+#pragma unroll 8
       for (int h = 0; h < H_s; ++h) {
         const float x = s_x[j][h];
         const float hi = bf16_to_f32(f32_to_bf16(x));
