@@ -277,6 +277,24 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
       for (int dt = 0; dt < NDT; ++dt) acc[qt][dt] = zero4();
   }
   const int kbrow0 = pairs[2 * pr] - b0.I;                // block row holding key block 0
+  // bf16 attention: each block's prepared V tile (one KV head, fp16 operand records) is staged in
+  // LDS by DMA once per workgroup beside the keys, instead of every wave loading it
+  constexpr bool VLDS = ATTN && DMA;
+  constexpr int VT = (D / 16) * (B / 32) * 1024;          // bytes of one block's V tile
+  constexpr int NVDMA = VLDS ? VT / 1024 / (NTHR / 64) : 1;
+  __shared__ __attribute__((aligned(16))) unsigned char s_v[VLDS ? 2 : 1][VLDS ? VT : 16];
+  auto dma_v = [&](int J, int buf) {
+    if constexpr (VLDS) {
+      const MF_GLOBAL unsigned char* vsrc = (const MF_GLOBAL unsigned char*)(
+          ao.vfrag + (((size_t)hd.vhead * n_brow + kbrow0 + J) * (B / 32)) * (D / 16) * 512);
+#pragma unroll
+      for (int u = 0; u < NVDMA; ++u) {
+        const int kib = w * NVDMA + u;
+        __builtin_amdgcn_global_load_lds(vsrc + kib * 1024 + lane * 16,
+                                         (__attribute__((address_space(3))) void*)&s_v[buf][kib * 1024], 16, 0, 0);
+      }
+    }
+  };
   v4u kst[CPT];
   // A block's statistics are stored during the next block, right after that block's key DMA, so
   // the wait for the DMA at its end need not cover them.
@@ -300,7 +318,10 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
     // Every lane group stores (the four hold the same values): the stores stay unconditional, so
     // the end-of-block wait that lets them stay in flight is known to cover the DMA on every path.
     auto issue = [&] {
-      if (J + 1 <= Jend) dma_k(J + 1, (J + 1) & 1);
+      if (J + 1 <= Jend) {
+        dma_k(J + 1, (J + 1) & 1);
+        dma_v(J + 1, (J + 1) & 1);
+      }
       if (stored) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) zrow[(size_t)Jpend * B + q0 + 16 * qt + c] = zpend[qt];
@@ -389,7 +410,8 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
         for (int ch = 0; ch < NCH; ++ch)
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt) {
-            const v8h vop = as_v8h(ld16(vb + (ch * NDT + dt) * 512));
+            const v8h vop = VLDS ? as_v8h(*reinterpret_cast<const v4u*>(&s_v[J & 1][((ch * NDT + dt) * 64 + lane) * 16]))
+                                 : as_v8h(ld16(vb + (ch * NDT + dt) * 512));
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) acc[qt][dt] = mfma_f16(vop, pop[qt][ch], acc[qt][dt]);
           }
@@ -407,6 +429,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
   fetch_k(kst, 0);
   stage_k(kst, 0);
   dma_k(0, 0);
+  dma_v(0, 0);
   if (DMA) dma_wait();
   __syncthreads();
   const int Jc = mine ? bi.I : -1;                         // last block this wave computes
