@@ -307,14 +307,12 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
     constexpr bool COMPUTE = decltype(kind)::value;
     if (J + 1 <= Jend) fetch_k(kst, J + 1);
     const bool stored = STATS && Jpend >= 0;
-    // The next key tile's DMA (into the buffer last read in block J - 1), then the previous
-    // block's statistics.  Without the attention half the DMA is issued after this block's last
-    // LDS read: the compiler cannot tell the two LDS buffers apart and makes every LDS read wait
-    // for all LDS DMA in flight, so a DMA issued before the score products would be waited for at
-    // once, with nothing to hide its latency; issued after them, it lands during the
-    // exponentials.  With the attention half it stays at the top of the block: the V loads after
-    // the exponentials are waited for on the same in-order counter, so a later DMA would delay
-    // them instead (measured slower).
+    // The next block's key (and V) tile DMA, into the buffers last read in block J - 1, then the
+    // previous block's statistics.  The DMA is issued after this block's score reads of the keys:
+    // the compiler cannot tell the two LDS buffers apart and makes every LDS read wait for all LDS
+    // DMA in flight, so a DMA issued before the score products would be waited for at once, with
+    // nothing to hide its latency; issued after them, it lands during the exponentials (the
+    // attention half's V reads, which follow, wait for what is left of it).
     // Every lane group stores (the four hold the same values): the stores stay unconditional, so
     // the end-of-block wait that lets them stay in flight is known to cover the DMA on every path.
     auto issue = [&] {
@@ -329,7 +327,6 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
       }
     };
     if constexpr (COMPUTE) {
-      if constexpr (ATTN) issue();
       const unsigned char* kt = s_k[J & 1];
       v4f s[QT][MT];
 #pragma unroll
@@ -340,7 +337,7 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) s[qt][mt] = dot_tile<D>(kf, qf[qt], zero4());
       }
-      if constexpr (!ATTN) issue();
+      issue();
       // only the diagonal block and blocks of a partial row need the causal / length mask
       const bool masked = J == bi.I || partial;
       v8h pop[ATTN ? QT : 1][NCH];
