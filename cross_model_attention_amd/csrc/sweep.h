@@ -383,10 +383,14 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
           // exponentials 2^(s c - r) times 2^(r - m)
           const float alpha = mprev == m_run[qt] ? 1.f : fast_exp2(mprev - m_run[qt]);
           const float f = zr.x > 0.f ? fast_exp2(zr.y - m_run[qt]) * 32768.f : 0.f;
+          // past the first blocks of a row its running maximum rarely moves: the wave skips the
+          // rescale when every alpha is exactly 1
+          if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[qt][dt][i] *= alpha;
+              for (int i = 0; i < 4; ++i) acc[qt][dt][i] *= alpha;
+          }
 #pragma unroll
           for (int ch = 0; ch < NCH; ++ch) {
             uint32_t pk[4];
