@@ -135,6 +135,40 @@ __device__ __forceinline__ float2 block_stats(v4f (&s)[MT], int kq, bool qvalid,
   return make_float2(z, none ? kNegInf : r);
 }
 
+// The same for a sweep with the attention half: the reference is the row's new running maximum
+// max(m_run, block maximum), so every value stays at most 2^15 in fp16, and s[] receives the
+// block's probabilities already scaled for the fp16 products, 2^(s c - ref + 15).  Returns z
+// (without the 2^15) and the reference; (0, -inf) when no key of the block is visible.
+template <int MT, bool MASKED>
+__device__ __forceinline__ float2 block_stats_run(v4f (&s)[MT], int kq, bool qvalid, float scale2, float m_run) {
+  if (MASKED) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!(qvalid && kq + 16 * mt + i <= 0)) s[mt][i] = kNegInf;
+  }
+  float bm = kNegInf;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    bm = __builtin_fmaxf(bm, __builtin_fmaxf(__builtin_fmaxf(s[mt][0], s[mt][1]), __builtin_fmaxf(s[mt][2], s[mt][3])));
+  bm = xrow_max(bm);
+  const bool none = MASKED && bm == kNegInf;            // nothing visible: z = 0
+  const float ref = none ? 0.f : __builtin_fmaxf(m_run, bm * scale2);
+  const float off = 15.f - ref;
+  float z = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(fmaf(s[mt][i], scale2, off));
+      z += e;
+      s[mt][i] = e;                                     // 0 for invisible keys
+    }
+  z = xrow_sum(z);
+  return make_float2(z * 0x1p-15f, none ? kNegInf : ref);
+}
+
 // Output half of a sweep that also computes attention (the fused sender prefill, and the dense
 // recompute): prepared V operand tiles and their per-head exponents.
 struct AttnOut {
@@ -367,22 +401,18 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
             }
           }
         }
-        if (!done) {
-          zr = masked ? block_stats<MT, true, ATTN>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
-                      : block_stats<MT, false, ATTN>(s[qt], 0, true, scale2);
-        }
-        if (STATS) zpend[qt] = zr;
-        const float mprev = m_run[qt];
-        if (!done && zr.x > 0.f) {
-          const float mn = __builtin_fmaxf(m_run[qt], zr.y);
-          l_run[qt] = l_run[qt] * (double)fast_exp2(m_run[qt] - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
-          m_run[qt] = mn;
-        }
         if constexpr (ATTN) {
-          // rescale the output to the new maximum; this block's probabilities are its
-          // exponentials 2^(s c - r) times 2^(r - m)
-          const float alpha = mprev == m_run[qt] ? 1.f : fast_exp2(mprev - m_run[qt]);
-          const float f = zr.x > 0.f ? fast_exp2(zr.y - m_run[qt]) * 32768.f : 0.f;
+          // statistics against the new running maximum; s holds the block's fp16-scaled
+          // probabilities, and the output is rescaled to the new maximum
+          zr = masked ? block_stats_run<MT, true>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2, m_run[qt])
+                      : block_stats_run<MT, false>(s[qt], 0, true, scale2, m_run[qt]);
+          if (STATS) zpend[qt] = zr;
+          float alpha = 1.f;
+          if (zr.x > 0.f) {
+            if (zr.y != m_run[qt]) alpha = fast_exp2(m_run[qt] - zr.y);   // 0 on a row's first block
+            l_run[qt] = l_run[qt] * (double)alpha + (double)zr.x;
+            m_run[qt] = zr.y;
+          }
           // past the first blocks of a row its running maximum rarely moves: the wave skips the
           // rescale when every alpha is exactly 1
           if (__builtin_amdgcn_ballot_w64(alpha != 1.f) != 0) {
@@ -396,10 +426,21 @@ __device__ __forceinline__ void sweep_body(const SweepHead<T>& hd, int h, int pr
             uint32_t pk[4];
 #pragma unroll
             for (int e = 0; e < 8; e += 2) {
-              const f2 v2 = {s[qt][2 * ch + (e >> 2)][e & 3] * f, s[qt][2 * ch + ((e + 1) >> 2)][(e + 1) & 3] * f};
+              const f2 v2 = {s[qt][2 * ch + (e >> 2)][e & 3], s[qt][2 * ch + ((e + 1) >> 2)][(e + 1) & 3]};
               pk[e / 2] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v2, h2));
             }
             pop[qt][ch] = as_v8h(v4u{pk[0], pk[1], pk[2], pk[3]});
+          }
+        } else {
+          if (!done) {
+            zr = masked ? block_stats<MT, true>(s[qt], J * B + 4 * a - qloc, qr < rows, scale2)
+                        : block_stats<MT, false>(s[qt], 0, true, scale2);
+          }
+          if (STATS) zpend[qt] = zr;
+          if (!done && zr.x > 0.f) {
+            const float mn = __builtin_fmaxf(m_run[qt], zr.y);
+            l_run[qt] = l_run[qt] * (double)fast_exp2(m_run[qt] - mn) + (double)zr.x * (double)fast_exp2(zr.y - mn);
+            m_run[qt] = mn;
           }
         }
       }
