@@ -33,7 +33,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-RETRIEVE_SRC = os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip")
+# the retrieve kernel and its host side (work order, head splits): counter traffic taken on other
+# versions of either is not reported
+RETRIEVE_SRC = (os.path.join(ROOT, "cross_model_attention_amd", "csrc", "retrieve.hip"),
+                os.path.join(ROOT, "cross_model_attention_amd", "csrc", "api.hip"))
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -84,17 +87,25 @@ def retrieve_flops(nnzb, H_s, H_r, B, d):
     return nnzb * (2 * H_r * H_s * B * B + 2 * H_r * B * B * d)
 
 
+def sources_sha256(paths):
+    """sha256 over the concatenated bytes of ``paths`` (one path or a sequence of them)."""
+    h = hashlib.sha256()
+    for p in ([paths] if isinstance(paths, str) else paths):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_from_profile(kernel_src, workload):
     """Measured HBM bytes per retrieve launch of ``workload`` from the committed counter summary,
-    if it was taken on the current kernel source (else None)."""
+    if it was taken on the current sources ``kernel_src`` (one path or several; else None)."""
     path = os.path.join(ROOT, "profiles", "retrieve_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(workload)
     if rec is None:
         return None
-    src = open(kernel_src, "rb").read()
-    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("source_sha256") != sources_sha256(kernel_src):
         return None
     return rec.get("bytes_per_launch")
 

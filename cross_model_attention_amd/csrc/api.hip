@@ -272,6 +272,22 @@ std::vector<int32_t> gather_order(const Geometry& g, int H_s) {
   return o;
 }
 
+// The retrieve's row order: block row gidx runs on XCD gidx mod 8 with all its row tiles and
+// head splits, and about 8 block rows are in flight per XCD.  In each run of 8 K entries of the
+// work order XCD x takes K consecutive entries (x-th from the front in even runs, from the back
+// in odd runs, so that no XCD always gets the longest rows of a run): the rows in flight on an
+// XCD are then neighbours, whose kept blocks and V tiles overlap most.
+std::vector<int32_t> retrieve_order(const Geometry& g) {
+  std::vector<int32_t> o(g.order.begin(), g.order.begin() + g.n_order);
+  constexpr int K = 8, R = 8 * K;   // 8 rows per XCD: the rows in flight on it
+  for (int m = 0, run = 0; m + R <= g.n_order; m += R, ++run)
+    for (int x = 0; x < 8; ++x) {
+      const int src = (run & 1) ? 7 - x : x;
+      for (int k = 0; k < K; ++k) o[m + 8 * k + x] = g.order[m + K * src + k];
+    }
+  return o;
+}
+
 // The statistics' pair order, grouped the same way: with a multiple of 8 heads every XCD takes
 // the pairs in order (L = 1), else XCD b mod 8 takes every 8th (L = 8); in a run of 256 L pairs of
 // several sequences, the pairs are grouped by sequence and lane x takes the x-th 256.
@@ -331,8 +347,10 @@ mf_status alloc_bsr_meta(const Geometry& g, int H_s, mf_bsr* out, BsrOwner* own)
   if (g.n_brow > 0) {
     e = hipMemcpy(out->brow_info, g.info.data(), n_info, hipMemcpyHostToDevice);
     // the order lists the active rows only (n_order <= n_brow entries; none past them are read)
-    if (e == hipSuccess && g.n_order > 0)
-      e = hipMemcpy(out->brow_order, g.order.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess && g.n_order > 0) {
+      const std::vector<int32_t> ro = retrieve_order(g);
+      e = hipMemcpy(out->brow_order, ro.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);
+    }
     if (e == hipSuccess && g.n_order > 0) {
       const std::vector<int32_t> go = gather_order(g, H_s);
       e = hipMemcpy(own->gorder, go.data(), (size_t)g.n_order * 4, hipMemcpyHostToDevice);

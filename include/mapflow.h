@@ -62,7 +62,10 @@ typedef struct mf_cache mf_cache;
  *
  *   brow_info   int32 [n_brow][4]   {first token of the block row, first token of its sequence,
  *                                     sequence length, block row index within the sequence}
- *   brow_order  int32 [n_brow]       block rows by descending in-sequence index (work order)
+ *   brow_order  int32 [n_order]      the retrieve's work order over the active block rows:
+ *                                    descending in-sequence index, dealt in runs of 64 entries
+ *                                    so that entry p (run on XCD p mod 8) and its neighbours on
+ *                                    that XCD are 8 consecutive rows of the order
  *   brow_coff   int32 [n_brow]       causal blocks of all earlier block rows (exclusive prefix
  *                                    of I + 1): the row's offset in per-causal-block scratch
  *   block_ptr   int32 [n_brow + 1]   CSR row pointer over kept blocks
