@@ -12,6 +12,9 @@ oracle comparisons of test_gpu_parity.py:
   a bf16 lo part of each weight) still enter the read-out mixed map to fp16 precision, whichever
   path the receiver's heads take and whichever head chunk the weight falls in.
 
+Also the retrieve's work order that a store carries: a permutation of its block rows, dealt to
+the XCDs as the header describes it.
+
 [MapFlow开源, section 算得省的:融合内核执行]: the kernel mixes the sender heads linearly on chip,
 renormalises the rows and multiplies by the receiver's own V.
 """
@@ -136,3 +139,45 @@ def test_mix_keeps_the_weights_low_bits(mf, heads):
     bound = 5.2e-4 * np.abs(want) + 1e-9
     assert np.count_nonzero(want) > 1000
     assert np.all(err <= bound), f"worst relative error {float((err / (np.abs(want) + 1e-30)).max()):.3e}"
+
+
+def _documented_work_order(lengths, B):
+    """The retrieve's work order as the header states it: block rows by descending in-sequence
+    index (ties in row order), then in each whole run of 64 entries XCD x (entry p runs on XCD
+    p mod 8) takes 8 consecutive entries of that order, the x-th group of 8 in even runs and the
+    (7 - x)-th in odd runs; a last partial run keeps the sorted order."""
+    I = [i for n in lengths for i in range(-(-n // B))]
+    srt = sorted(range(len(I)), key=lambda b: -I[b])
+    o = list(srt)
+    for run, m in enumerate(range(0, len(srt) - 63, 64)):
+        for x in range(8):
+            src = 7 - x if run & 1 else x
+            for k in range(8):
+                o[m + 8 * k + x] = srt[m + 8 * src + k]
+    return np.array(o, np.int32)
+
+
+@pytest.mark.parametrize("lengths", [[64 * 200 + 17], [3000, 64 * 150, 900, 5000], [50]])
+def test_retrieve_work_order_is_the_documented_deal(mf, lengths):
+    import ctypes
+    from cross_model_attention_amd import mapflow as mfm
+
+    B, H_s, d = 64, 8, 64
+    T = sum(lengths)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    Q = torch.randn(H_s, T, d, device="cuda", generator=g).to(torch.bfloat16)
+    K = torch.randn(H_s, T, d, device="cuda", generator=g).to(torch.bfloat16)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    store = mf.compress(Q, K, 0.9, B, cu_seqlens=cu)
+    r = store.raw
+    want = _documented_work_order(lengths, B)
+    assert r.n_order == r.n_brow == len(want)
+    # the store's order array, copied out by the library's own 16-byte copy kernel
+    nbytes = -(-r.n_order * 4 // 16) * 16
+    dst = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    mfm.check(mfm._L.mf_copy_probe(store.ctx.handle, ctypes.c_void_p(dst.data_ptr()),
+                                   ctypes.c_void_p(r.brow_order), nbytes, mfm._stream(None)))
+    got = dst.cpu().numpy()[: r.n_order]
+    say(f"work order of {lengths}: {r.n_order} rows, first 16 {got[:16].tolist()}")
+    assert sorted(got.tolist()) == list(range(r.n_brow)), "not a permutation of the block rows"
+    np.testing.assert_array_equal(got, want)
